@@ -1,0 +1,340 @@
+"""Benchmark of the grouped NF4 MoE expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload olmoe]
+                    [--no-cpu-baseline] [--no-decode]
+
+A step is one full routed-expert layer forward (route + permute, gate_up with
+SwiGLU, down, combine) over the whole batch, inputs resident in HBM.  The
+headline workload is the OLMoE-1B-7B-shaped prefill layer (E=64, H=2048,
+I=1024, top-8, T=4096 tokens); the value is its algorithmic TFLOP/s
+(6*T*k*H*I per forward).  The same JSON line carries:
+
+  roofline      the dominant kernel (the gate_up grouped GEMM) timed alone
+                with HIP events on the stream it runs on, against the fp16
+                dense MFMA peak;
+  decode        the batch-1 decode layer (Qwen3-30B-A3B shape, 8 routed
+                experts) as packed-weight GB/s over 48 distinct layer stacks
+                replayed from a HIP graph;
+  cpu_baseline  the CPU oracle timed on this host on the same layer shape.
+
+Prints exactly one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "grouped NF4 MoE layer TFLOP/s (prefill) + packed-weight GB/s (decode M=1)"
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+DECODE_LAYERS = 48
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gpu_stacks(cfg, dev, seed=0, group=16):
+    """Quantise the layer's fp32 weights on the GPU, a few experts at a time."""
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    out = {}
+    for which, (n, kk) in (("gu", (2 * cfg.I, cfg.H)), ("dn", (cfg.H, cfg.I))):
+        p = torch.empty((cfg.E, n, kk // 2), dtype=torch.uint8, device=dev)
+        a = torch.empty((cfg.E, n, kk // 64), dtype=torch.float32, device=dev)
+        for e0 in range(0, cfg.E, group):
+            ex = range(e0, min(e0 + group, cfg.E))
+            w = torch.from_numpy(synth.stack_weights(cfg, which, seed, ex)).to(dev)
+            pp, aa = binding.quantize(w)
+            p[e0:e0 + len(ex)] = pp
+            a[e0:e0 + len(ex)] = aa
+            del w
+        out[which] = (p, a)
+    return out
+
+
+def time_events(fn, iters: int, stream) -> float:
+    """Average milliseconds per call of fn(), HIP events on `stream`."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def traffic_from_profiles(kernel_src: str):
+    """HBM bytes per launch of the gate_up GEMM from committed counter runs.
+
+    Returns None when no counter summary exists or when the kernel source
+    changed since the counters were taken.
+    """
+    path = os.path.join(ROOT, "profiles", "gate_up_gemm_olmoe_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds_target: float = 10.0):
+    """Time the CPU oracle on the layer shape (random NF4 stacks; values do
+    not change its cost).  Runs whole forwards until about `seconds_target`."""
+    import numpy as np
+
+    import oracle
+    from grouped_nf4_gemm_quantize_amd import synth
+
+    rng = np.random.default_rng(1)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    gp = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+    ga = rng.uniform(0.01, 0.05, size=(E, 2 * I, H // 64)).astype(np.float32)
+    dp = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
+    da = rng.uniform(0.01, 0.05, size=(E, H, I // 64)).astype(np.float32)
+    x = synth.activations(cfg)
+    lg = synth.router_logits(cfg)
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    runs, elapsed = 0, 0.0
+    while elapsed < seconds_target and runs < 5:
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, lg, cfg.k, gp, ga, dp, da)
+        elapsed += time.perf_counter() - t0
+        runs += 1
+    per = elapsed / runs
+    return {
+        "value": round(cfg.flops() / per / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{runs} full {cfg.name} layer forward(s) (T={cfg.T}, E={E}, H={H}, "
+                   f"I={I}, top-{cfg.k}) of the NumPy fp64 oracle, random NF4 stacks, "
+                   f"{per:.2f} s each"),
+    }
+
+
+def bench_decode(dev, steps: int):
+    """48 distinct decode layers (8 routed experts each) replayed from a graph."""
+    import numpy as np
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    cfg = synth.config("decode")
+    st = gpu_stacks(cfg, dev)
+    gp, ga = st["gu"]
+    dp, da = st["dn"]
+    layers = []
+    for l in range(DECODE_LAYERS):
+        lg = np.random.default_rng(1000 + l).standard_normal((1, cfg.E), dtype=np.float32)
+        layers.append(dict(
+            gp=gp.clone(), ga=ga.clone(), dp=dp.clone(), da=da.clone(),
+            lg=torch.from_numpy(lg).to(dev),
+            y=torch.empty((1, cfg.H), dtype=torch.bfloat16, device=dev),
+            ws=torch.empty(binding.forward_workspace_bytes(1, cfg.H, cfg.I, cfg.E, cfg.k),
+                           dtype=torch.uint8, device=dev)))
+    del gp, ga, dp, da, st
+    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
+
+    def run_all():
+        for L in layers:
+            binding.moe_forward(x, L["lg"], cfg.k, L["gp"], L["ga"], L["dp"], L["da"],
+                                y=L["y"], workspace=L["ws"])
+
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            run_all()
+        eager_ms = time_events(run_all, max(steps, 3), stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run_all()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            g.replay()
+        graph_ms = time_events(g.replay, max(steps, 10), stream)
+    per_layer_bytes = cfg.k * (2 * cfg.I * cfg.H + cfg.H * cfg.I) * 9 // 16
+    gbs = DECODE_LAYERS * per_layer_bytes / (graph_ms * 1e-3) / 1e9
+    out = {
+        "metric": "packed-weight GB/s (decode M=1)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "workload": (f"Qwen3-30B-A3B-shaped decode layer x{DECODE_LAYERS} distinct stacks "
+                     f"(E={cfg.E}, H={cfg.H}, I={cfg.I}, top-{cfg.k}, T=1), HIP graph replay"),
+        "bytes_per_layer": per_layer_bytes,
+        "us_per_layer": round(graph_ms * 1e3 / DECODE_LAYERS, 3),
+        "us_per_layer_eager": round(eager_ms * 1e3 / DECODE_LAYERS, 3),
+        "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+    }
+    del layers, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe",
+                    choices=["olmoe", "qwen3_zipf", "qlora"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.workload)
+    log(f"[bench] workload {cfg}")
+    st = gpu_stacks(cfg, dev)
+    gp, ga = st["gu"]
+    dp, da = st["dn"]
+    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
+    lg = torch.from_numpy(synth.router_logits(cfg)).to(dev)
+    glo = dlo = None
+    lw = synth.lora_weights(cfg)
+    if lw is not None:
+        t = {k_: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k_, v in lw.items()}
+        glo = (t["a_gu"], t["b_gu"], cfg.lora_scale)
+        dlo = (t["a_dn"], t["b_dn"], cfg.lora_scale)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
+                            y=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` forwards, bracketed by device syncs
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = cfg.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] layer forward {ms * 1e3:.1f} us  {tflops:.1f} TFLOP/s")
+
+    # dominant kernel alone: the gate_up grouped GEMM on this forward's routing
+    ptr = binding.forward_routing(ws, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    base = ws.data_ptr()
+    P = cfg.P
+    sp = ws[ptr["sorted_pair"] - base: ptr["sorted_pair"] - base + 4 * P].view(torch.int32)
+    off = ws[ptr["offsets"] - base: ptr["offsets"] - base + 4 * (cfg.E + 1)].view(torch.int32)
+    x16 = x.to(torch.float16)
+    h = torch.empty((P, cfg.I), dtype=torch.float16, device=dev)
+    o = torch.empty((P, cfg.H), dtype=torch.float16, device=dev)
+
+    def gate_up():
+        binding.grouped_gemm(x16, gp, ga, off, P, gather=sp, gather_div=cfg.k, lora=glo,
+                             swiglu=True, out=h)
+
+    def down():
+        binding.grouped_gemm(h, dp, da, off, P, lora=dlo, scatter=sp, out=o)
+
+    for _ in range(2):
+        gate_up()
+        down()
+    gu_ms = time_events(gate_up, max(args.steps, 10), stream)
+    dn_ms = time_events(down, max(args.steps, 10), stream)
+    gu_flops = 4.0 * P * cfg.H * cfg.I
+    dn_flops = 2.0 * P * cfg.H * cfg.I
+    if glo is not None:
+        gu_flops += 2.0 * P * cfg.lora_r * (cfg.H + 2 * cfg.I)
+        dn_flops += 2.0 * P * cfg.lora_r * (cfg.I + cfg.H)
+    gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    dn_tf = dn_flops / (dn_ms * 1e-3) / 1e12
+    log(f"[bench] gate_up GEMM {gu_ms * 1e3:.1f} us {gu_tf:.1f} TFLOP/s; "
+        f"down GEMM {dn_ms * 1e3:.1f} us {dn_tf:.1f} TFLOP/s")
+    traffic = traffic_from_profiles(os.path.join(
+        ROOT, "grouped_nf4_gemm_quantize_amd", "csrc", "gemm.hip"))
+    del h, o, x16
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name} layer prefill: E={cfg.E} H={cfg.H} I={cfg.I} "
+                         f"top-{cfg.k} T={cfg.T}" + (f" LoRA r={cfg.lora_r}" if cfg.lora_r else "")),
+            "E": cfg.E, "H": cfg.H, "I": cfg.I, "k": cfg.k, "T": cfg.T,
+            "routing": cfg.logits, "lora_r": cfg.lora_r,
+            "flops_per_step": flops,
+        },
+        "roofline": {
+            "kernel": "grouped_gemm_kernel (gate_up + SwiGLU)",
+            "bound": "mfma",
+            "achieved": round(gu_tf, 3),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gu_tf / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "flops_per_launch": gu_flops,
+        },
+        "kernels": {
+            "gate_up_us": round(gu_ms * 1e3, 3), "gate_up_tflops": round(gu_tf, 3),
+            "down_us": round(dn_ms * 1e3, 3), "down_tflops": round(dn_tf, 3),
+        },
+    }
+    del gp, ga, dp, da, st, y, ws
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        result["decode"] = bench_decode(dev, args.steps)
+        log(f"[bench] decode {result['decode']}")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg)
+        log(f"[bench] cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

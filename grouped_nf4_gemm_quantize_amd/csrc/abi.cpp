@@ -1,0 +1,492 @@
+// Host side of the C ABI declared in include/nf4moe.h: argument validation,
+// workspace layout, and kernel launches on the caller's stream.
+//
+// Every check runs before anything is enqueued, and every failure returns a
+// distinct status with a thread-local message (the pages' stance: refuse in
+// the pre-flight rather than fail later, experts4bit-qlora 0.22.0 README
+// "Which door?"; fail fast with a clear error, "Scope").
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/nf4moe.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace nf4moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return NF4MOE_OK;
+}
+
+int hip_fail(hipError_t err, const char* what) {
+  return fail(NF4MOE_EHIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+const float kLevels[16] = NF4MOE_LEVELS_INIT;
+
+// t[j] = the largest fp32 value <= the exact midpoint of levels j and j+1.
+// The midpoint of two fp32 numbers is exact in double precision.
+QuantThresholds make_thresholds() {
+  QuantThresholds th;
+  for (int j = 0; j < 15; ++j) {
+    const double mid = ((double)kLevels[j] + (double)kLevels[j + 1]) * 0.5;
+    float t = (float)mid;
+    if ((double)t > mid) t = std::nextafter(t, -INFINITY);
+    th.t[j] = t;
+  }
+  return th;
+}
+
+const QuantThresholds& thresholds() {
+  static const QuantThresholds th = make_thresholds();
+  return th;
+}
+
+std::atomic<int> g_cu_cache[64];
+
+int cu_count(int* out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev >= 0 && dev < 64) {
+    const int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return NF4MOE_OK;
+    }
+  }
+  int n = 0;
+  err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return hip_fail(err, "hipDeviceGetAttribute");
+  if (n <= 0) n = 256;
+  if (dev >= 0 && dev < 64) g_cu_cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return NF4MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_lora(const nf4moe_lora* l, const char* name) {
+  if (l == nullptr) return NF4MOE_OK;
+  if (l->A == nullptr || l->B == nullptr)
+    return fail(NF4MOE_EINVAL, "%s: LoRA A and B must be non-null", name);
+  if (l->r < 1 || l->r > NF4MOE_MAX_LORA_R)
+    return fail(NF4MOE_EINVAL, "%s: LoRA rank r=%d outside [1, %d]", name, l->r,
+                NF4MOE_MAX_LORA_R);
+  if (l->dtype != NF4MOE_BF16 && l->dtype != NF4MOE_F16)
+    return fail(NF4MOE_EDTYPE, "%s: LoRA dtype must be BF16 or F16", name);
+  if (!std::isfinite(l->scale))
+    return fail(NF4MOE_EINVAL, "%s: LoRA scale is not finite", name);
+  if (!aligned(l->A, 16) || !aligned(l->B, 2))
+    return fail(NF4MOE_EINVAL, "%s: LoRA A must be 16-byte aligned", name);
+  return NF4MOE_OK;
+}
+
+int check_route_shape(int64_t T, int E, int k) {
+  if (T < 1) return fail(NF4MOE_EINVAL, "T=%lld must be >= 1", (long long)T);
+  if (E < 1) return fail(NF4MOE_EINVAL, "E=%d must be >= 1", E);
+  if (E > NF4MOE_MAX_EXPERTS)
+    return fail(NF4MOE_ESHAPE, "E=%d exceeds %d experts", E, NF4MOE_MAX_EXPERTS);
+  if (k < 1 || k > E || k > NF4MOE_MAX_TOPK)
+    return fail(NF4MOE_ETOPK, "k=%d must satisfy 1 <= k <= min(E=%d, %d)", k, E,
+                NF4MOE_MAX_TOPK);
+  if (T > (int64_t)INT32_MAX / k)
+    return fail(NF4MOE_EOVERFLOW, "T*k = %lld pairs overflow int32 indexing",
+                (long long)T * k);
+  return NF4MOE_OK;
+}
+
+// ---- routing workspace layout
+struct RouteLayout {
+  size_t masks, base, total;
+};
+
+RouteLayout route_layout(int64_t T, int E) {
+  const int64_t nchunks = (T + kRouteChunk - 1) / kRouteChunk;
+  RouteLayout L;
+  size_t o = 0;
+  L.masks = o;
+  o = align_up(o + (size_t)nchunks * E * 4, 256);
+  L.base = o;
+  o = align_up(o + (size_t)nchunks * E * 4, 256);
+  L.total = o;
+  return L;
+}
+
+// ---- forward workspace layout (the same regions for every path)
+struct FwdLayout {
+  size_t ids, w, sorted, pos, offsets, route, x16, h, o, hbuf, total;
+  RouteLayout r;
+};
+
+FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k) {
+  FwdLayout L;
+  const size_t P = (size_t)T * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.ids = take(P * 4);
+  L.w = take(P * 4);
+  L.sorted = take(P * 4);
+  L.pos = take(P * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.r = route_layout(T, E);
+  L.route = take(L.r.total);
+  L.x16 = take((size_t)T * H * 2);
+  L.h = take(P * (size_t)I * 2);
+  L.o = take(P * (size_t)H * 2);
+  L.hbuf = take((size_t)k * I * 4);
+  L.total = o;
+  return L;
+}
+
+bool use_decode_path(int64_t T, int H, int I, int k, const nf4moe_lora* a,
+                     const nf4moe_lora* b) {
+  return T == 1 && a == nullptr && b == nullptr && H <= 32768 &&
+         (int64_t)k * I <= 32768;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nf4moe_strerror(int status) {
+  switch (status) {
+    case NF4MOE_OK: return "ok";
+    case NF4MOE_EINVAL: return "invalid argument";
+    case NF4MOE_ESHAPE: return "unsupported shape";
+    case NF4MOE_EBLOCK: return "unsupported quantisation blocksize (must be 64)";
+    case NF4MOE_ETOPK: return "invalid top-k";
+    case NF4MOE_EDTYPE: return "unsupported dtype";
+    case NF4MOE_EWORKSPACE: return "workspace too small";
+    case NF4MOE_EOVERFLOW: return "size overflows 32-bit indexing";
+    case NF4MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* nf4moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* nf4moe_version(void) { return "0.1.0"; }
+
+int nf4moe_codebook(float* out16) {
+  if (out16 == nullptr) return fail(NF4MOE_EINVAL, "out16 is NULL");
+  std::memcpy(out16, kLevels, sizeof(kLevels));
+  return ok();
+}
+
+int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K) {
+  if (E < 1 || N < 1 || K < 1) return fail(NF4MOE_EINVAL, "sizes must be positive");
+  if (K % NF4MOE_BLOCKSIZE) return fail(NF4MOE_ESHAPE, "K=%lld is not a multiple of 64", (long long)K);
+  const int64_t n = E * N * K;
+  if (n / E / N != K) return fail(NF4MOE_EOVERFLOW, "E*N*K overflows");
+  ok();
+  return n / 2 + (n / NF4MOE_BLOCKSIZE) * 4;
+}
+
+int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
+                         int64_t K, int blocksize, uint8_t* packed,
+                         float* absmax, int32_t* nonfinite_flag, void* stream) {
+  if (w == nullptr || packed == nullptr || absmax == nullptr)
+    return fail(NF4MOE_EINVAL, "w, packed and absmax must be non-null");
+  if (E < 1 || N < 1 || K < 1)
+    return fail(NF4MOE_EINVAL, "E, N, K must be positive (got %lld, %lld, %lld)",
+                (long long)E, (long long)N, (long long)K);
+  if (blocksize != NF4MOE_BLOCKSIZE)
+    return fail(NF4MOE_EBLOCK, "blocksize=%d: only nf4/64 storage is supported", blocksize);
+  if (K % NF4MOE_BLOCKSIZE)
+    return fail(NF4MOE_ESHAPE, "K=%lld is not a multiple of 64", (long long)K);
+  if (w_dtype != NF4MOE_F32 && w_dtype != NF4MOE_BF16)
+    return fail(NF4MOE_EDTYPE, "w_dtype=%d: the quantiser takes F32 or BF16", w_dtype);
+  const int64_t n = E * N * K;
+  if (n / E / N != K || n > ((int64_t)1 << 50))
+    return fail(NF4MOE_EOVERFLOW, "E*N*K is too large");
+  if (!aligned(w, w_dtype == NF4MOE_F32 ? 16 : 8) || !aligned(packed, 2) ||
+      !aligned(absmax, 4))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (w needs 16 bytes for F32, 8 for BF16)");
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != NF4MOE_OK) return st;
+  hipError_t err = launch_quantize(w, w_dtype, n, packed, absmax, nonfinite_flag,
+                                   thresholds(), cus, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "quantize launch");
+  return ok();
+}
+
+size_t moe_route_permute_workspace(int64_t T, int E, int k) {
+  (void)k;
+  if (T < 1 || E < 1 || E > NF4MOE_MAX_EXPERTS) return 0;
+  return route_layout(T, E).total;
+}
+
+int moe_route_permute(const float* logits, int64_t T, int E, int k,
+                      int renormalize, int32_t* topk_ids, float* topk_w,
+                      int32_t* sorted_pair, int32_t* pair_pos,
+                      int32_t* expert_offsets, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr ||
+      sorted_pair == nullptr || expert_offsets == nullptr)
+    return fail(NF4MOE_EINVAL, "logits, topk_ids, topk_w, sorted_pair and expert_offsets must be non-null");
+  int st = check_route_shape(T, E, k);
+  if (st != NF4MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1)
+    return fail(NF4MOE_EINVAL, "renormalize must be 0 or 1");
+  const RouteLayout L = route_layout(T, E);
+  if (workspace == nullptr || ws_bytes < L.total)
+    return fail(NF4MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? ws_bytes : (size_t)0);
+  char* ws = (char*)workspace;
+  RouteArgs a{};
+  a.logits = logits;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.renormalize = renormalize;
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.sorted_pair = sorted_pair;
+  a.pair_pos = pair_pos;
+  a.expert_offsets = expert_offsets;
+  a.chunk_masks = (uint32_t*)(ws + L.masks);
+  a.chunk_base = (int32_t*)(ws + L.base);
+  a.x_in = nullptr;
+  a.x16 = nullptr;
+  hipError_t err = launch_route(a, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "route launch");
+  return ok();
+}
+
+static int gemm_common(const void* a, int a_dtype, const int32_t* gather,
+                       int gather_div, const uint8_t* packed, const float* absmax,
+                       const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
+                       const nf4moe_lora* lora, int epilogue,
+                       const float* row_scale, const int32_t* scatter, void* out,
+                       int out_dtype, hipStream_t stream) {
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != NF4MOE_OK) return st;
+  GemmArgs g{};
+  g.a = a;
+  g.a_bf16 = a_dtype == NF4MOE_BF16;
+  g.gather = gather;
+  g.gather_div = gather ? gather_div : 1;
+  g.packed = packed;
+  g.absmax = absmax;
+  g.offsets = expert_offsets;
+  g.E = E;
+  g.P = P;
+  g.N = (int)N;
+  g.K = (int)K;
+  if (lora) {
+    g.lora_a = lora->A;
+    g.lora_b = lora->B;
+    g.lora_r = lora->r;
+    g.lora_scale = lora->scale;
+    g.lora_bf16 = lora->dtype == NF4MOE_BF16;
+  }
+  g.swiglu = epilogue == NF4MOE_EPI_SWIGLU;
+  g.row_scale = row_scale;
+  g.scatter = scatter;
+  g.out = out;
+  g.out_dtype = out_dtype;
+  hipError_t err = launch_grouped_gemm(g, cus, stream);
+  if (err != hipSuccess) return hip_fail(err, "grouped GEMM launch");
+  return NF4MOE_OK;
+}
+
+int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
+                     const int32_t* gather, int gather_div,
+                     const uint8_t* packed, const float* absmax,
+                     const int32_t* expert_offsets, int E, int64_t P,
+                     int64_t N, int64_t K, const nf4moe_lora* lora,
+                     int epilogue, const float* row_scale,
+                     const int32_t* scatter, void* out, int out_dtype,
+                     void* stream) {
+  if (a == nullptr || packed == nullptr || absmax == nullptr ||
+      expert_offsets == nullptr || out == nullptr)
+    return fail(NF4MOE_EINVAL, "a, packed, absmax, expert_offsets and out must be non-null");
+  if (E < 1 || E > NF4MOE_MAX_EXPERTS)
+    return fail(E < 1 ? NF4MOE_EINVAL : NF4MOE_ESHAPE, "E=%d outside [1, %d]", E,
+                NF4MOE_MAX_EXPERTS);
+  if (P < 0 || a_rows < 0) return fail(NF4MOE_EINVAL, "P and a_rows must be >= 0");
+  if (N < 16 || K < 64) return fail(NF4MOE_EINVAL, "N >= 16 and K >= 64 required");
+  if (K % NF4MOE_BLOCKSIZE) return fail(NF4MOE_ESHAPE, "K=%lld is not a multiple of 64", (long long)K);
+  if (N % 16) return fail(NF4MOE_ESHAPE, "N=%lld is not a multiple of 16", (long long)N);
+  if (epilogue != NF4MOE_EPI_NONE && epilogue != NF4MOE_EPI_SWIGLU)
+    return fail(NF4MOE_EINVAL, "unknown epilogue %d", epilogue);
+  if (epilogue == NF4MOE_EPI_SWIGLU && N % 32)
+    return fail(NF4MOE_ESHAPE, "SwiGLU needs N=2I with I a multiple of 16 (N=%lld)", (long long)N);
+  if (a_dtype != NF4MOE_F16 && a_dtype != NF4MOE_BF16)
+    return fail(NF4MOE_EDTYPE, "a_dtype=%d: activations must be F16 or BF16", a_dtype);
+  if (out_dtype != NF4MOE_F16 && out_dtype != NF4MOE_BF16 && out_dtype != NF4MOE_F32)
+    return fail(NF4MOE_EDTYPE, "out_dtype=%d unsupported", out_dtype);
+  if (gather != nullptr && gather_div < 1)
+    return fail(NF4MOE_EINVAL, "gather_div must be >= 1");
+  if (P >= INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX / 2)
+    return fail(NF4MOE_EOVERFLOW, "P, N or K too large for 32-bit row indexing");
+  int st = check_lora(lora, "lora");
+  if (st != NF4MOE_OK) return st;
+  if (!aligned(a, 16) || !aligned(packed, 8) || !aligned(absmax, 4) ||
+      !aligned(out, out_dtype == NF4MOE_F32 ? 4 : 2))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (a needs 16 bytes, packed 8)");
+  if (P == 0) return ok();
+  st = gemm_common(a, a_dtype, gather, gather_div, packed, absmax, expert_offsets,
+                   E, P, N, K, lora, epilogue, row_scale, scatter, out, out_dtype,
+                   (hipStream_t)stream);
+  if (st != NF4MOE_OK) return st;
+  return ok();
+}
+
+size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k) {
+  if (T < 1 || H < 1 || I < 1 || E < 1 || E > NF4MOE_MAX_EXPERTS || k < 1) return 0;
+  return fwd_layout(T, H, I, E, k).total;
+}
+
+int moe_expert_forward_routing(void* workspace, int64_t T, int H, int I, int E,
+                               int k, int32_t** topk_ids, float** topk_w,
+                               int32_t** sorted_pair, int32_t** expert_offsets) {
+  if (workspace == nullptr) return fail(NF4MOE_EINVAL, "workspace is NULL");
+  int st = check_route_shape(T, E, k);
+  if (st != NF4MOE_OK) return st;
+  if (H < 1 || I < 1) return fail(NF4MOE_EINVAL, "H and I must be positive");
+  const FwdLayout L = fwd_layout(T, H, I, E, k);
+  char* ws = (char*)workspace;
+  if (topk_ids) *topk_ids = (int32_t*)(ws + L.ids);
+  if (topk_w) *topk_w = (float*)(ws + L.w);
+  if (sorted_pair) *sorted_pair = (int32_t*)(ws + L.sorted);
+  if (expert_offsets) *expert_offsets = (int32_t*)(ws + L.offsets);
+  return ok();
+}
+
+int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
+                       int64_t T, int H, int I, int E, int k, int renormalize,
+                       const uint8_t* gu_packed, const float* gu_absmax,
+                       const uint8_t* dn_packed, const float* dn_absmax,
+                       const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora,
+                       void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  if (x == nullptr || router_logits == nullptr || gu_packed == nullptr ||
+      gu_absmax == nullptr || dn_packed == nullptr || dn_absmax == nullptr ||
+      y == nullptr)
+    return fail(NF4MOE_EINVAL, "x, router_logits, the four stack buffers and y must be non-null");
+  int st = check_route_shape(T, E, k);
+  if (st != NF4MOE_OK) return st;
+  if (H < 64 || I < 64) return fail(NF4MOE_EINVAL, "H and I must be >= 64");
+  if (H % 64 || I % 64)
+    return fail(NF4MOE_ESHAPE, "H=%d and I=%d must be multiples of 64", H, I);
+  if (renormalize != 0 && renormalize != 1)
+    return fail(NF4MOE_EINVAL, "renormalize must be 0 or 1");
+  if (x_dtype != NF4MOE_BF16 && x_dtype != NF4MOE_F16)
+    return fail(NF4MOE_EDTYPE, "x_dtype=%d: activations must be BF16 or F16", x_dtype);
+  if (y_dtype != NF4MOE_BF16 && y_dtype != NF4MOE_F16 && y_dtype != NF4MOE_F32)
+    return fail(NF4MOE_EDTYPE, "y_dtype=%d unsupported", y_dtype);
+  st = check_lora(gu_lora, "gu_lora");
+  if (st != NF4MOE_OK) return st;
+  st = check_lora(dn_lora, "dn_lora");
+  if (st != NF4MOE_OK) return st;
+  const int64_t P = T * k;
+  if (!aligned(x, 16) || !aligned(gu_packed, 16) || !aligned(dn_packed, 16) ||
+      !aligned(gu_absmax, 4) || !aligned(dn_absmax, 4) || !aligned(y, 16))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (x, y and packed stacks need 16 bytes)");
+  const FwdLayout L = fwd_layout(T, H, I, E, k);
+  if (workspace == nullptr || ws_bytes < L.total)
+    return fail(NF4MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(NF4MOE_EINVAL, "workspace must be 256-byte aligned");
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != NF4MOE_OK) return st;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ids = (int32_t*)(ws + L.ids);
+  float* wts = (float*)(ws + L.w);
+
+  if (use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
+    GemvArgs g{};
+    g.x = x;
+    g.x_bf16 = x_dtype == NF4MOE_BF16;
+    g.logits = router_logits;
+    g.E = E;
+    g.k = k;
+    g.renormalize = renormalize;
+    g.H = H;
+    g.I = I;
+    g.gu_packed = gu_packed;
+    g.gu_absmax = gu_absmax;
+    g.dn_packed = dn_packed;
+    g.dn_absmax = dn_absmax;
+    g.topk_ids = ids;
+    g.topk_w = wts;
+    g.hbuf = (float*)(ws + L.hbuf);
+    g.y = y;
+    g.y_dtype = y_dtype;
+    hipError_t err = launch_decode(g, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "decode launch");
+    return ok();
+  }
+
+  RouteArgs r{};
+  r.logits = router_logits;
+  r.T = T;
+  r.E = E;
+  r.k = k;
+  r.renormalize = renormalize;
+  r.topk_ids = ids;
+  r.topk_w = wts;
+  r.sorted_pair = (int32_t*)(ws + L.sorted);
+  r.pair_pos = (int32_t*)(ws + L.pos);
+  r.expert_offsets = (int32_t*)(ws + L.offsets);
+  r.chunk_masks = (uint32_t*)(ws + L.route + L.r.masks);
+  r.chunk_base = (int32_t*)(ws + L.route + L.r.base);
+  const bool conv = x_dtype == NF4MOE_BF16;
+  r.x_in = x;
+  r.x_bf16 = conv ? 1 : 0;
+  r.x16 = conv ? (_Float16*)(ws + L.x16) : nullptr;
+  r.H = H;
+  hipError_t err = launch_route(r, s);
+  if (err != hipSuccess) return hip_fail(err, "route launch");
+
+  const void* xa = conv ? (const void*)(ws + L.x16) : x;
+  _Float16* h = (_Float16*)(ws + L.h);
+  _Float16* o = (_Float16*)(ws + L.o);
+  st = gemm_common(xa, NF4MOE_F16, r.sorted_pair, k, gu_packed, gu_absmax,
+                   r.expert_offsets, E, P, 2 * (int64_t)I, H, gu_lora,
+                   NF4MOE_EPI_SWIGLU, nullptr, nullptr, h, NF4MOE_F16, s);
+  if (st != NF4MOE_OK) return st;
+  st = gemm_common(h, NF4MOE_F16, nullptr, 1, dn_packed, dn_absmax, r.expert_offsets,
+                   E, P, H, I, dn_lora, NF4MOE_EPI_NONE, nullptr,
+                   r.sorted_pair, o, NF4MOE_F16, s);
+  if (st != NF4MOE_OK) return st;
+  err = launch_combine(o, wts, T, k, H, y, y_dtype, cus, s);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return ok();
+}
+
+}  // extern "C"

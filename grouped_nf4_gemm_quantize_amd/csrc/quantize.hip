@@ -1,0 +1,105 @@
+// NF4 blockwise quantiser for fused expert stacks.
+//
+// Experts4bit.from_float quantises the fused gate_up / down stacks to NF4
+// with one absmax per 64 elements (experts4bit-qlora 0.22.0 README,
+// "Quickstart" and "Which door?"); the blocks never cross an expert boundary
+// (load_in_4bit solutions page, "Which project solves it").  A block here is
+// 64 consecutive elements of one row of one expert, so it can cross neither.
+//
+// Layout: 16 lanes own one block, 4 consecutive elements each, so a wave64
+// covers 4 blocks = 256 consecutive elements and every load is a coalesced
+// 16-byte (fp32) or 8-byte (bf16) access.  HBM bound: 4 (or 2) bytes read and
+// 0.5625 bytes written per element.
+
+#include "common.h"
+#include "launch.h"
+
+namespace nf4moe {
+
+template <bool kBF16>
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const void* __restrict__ w, int64_t nblocks, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, int32_t* __restrict__ nonfinite_flag,
+    QuantThresholds thr) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 15;   // position of this lane inside its block
+  const int blk_in_wave = lane >> 4;
+  const int64_t wave_global = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+
+  float t[15];
+#pragma unroll
+  for (int j = 0; j < 15; ++j) t[j] = thr.t[j];
+
+  bool bad = false;
+  for (int64_t b0 = wave_global * 4; b0 < nblocks; b0 += nwaves * 4) {
+    const int64_t blk = b0 + blk_in_wave;
+    const bool live = blk < nblocks;
+    const int64_t e0 = blk * kBlock + sub * 4;  // first element of this lane
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      if constexpr (kBF16) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(
+            reinterpret_cast<const uint16_t*>(w) + e0);
+        x[0] = bf16_bits_to_f32(v.x & 0xffffu);
+        x[1] = bf16_bits_to_f32(v.x >> 16);
+        x[2] = bf16_bits_to_f32(v.y & 0xffffu);
+        x[3] = bf16_bits_to_f32(v.y >> 16);
+      } else {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(
+            reinterpret_cast<const float*>(w) + e0);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+      }
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bad |= !__builtin_isfinite(x[i]);
+      a = fmaxf(a, fabsf(x[i]));
+    }
+    // max over the 16 lanes of the block (lanes differ only in bits 0..3)
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+
+    uint32_t codes[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t c = 7u;
+      if (a != 0.f) {
+        const float xn = x[i] / a;  // IEEE fp32 division (no fast-math)
+        c = 0u;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) c += (xn > t[j]) ? 1u : 0u;
+      }
+      codes[i] = c;
+    }
+    if (live) {
+      const uint32_t b01 = (codes[0] << 4) | codes[1];
+      const uint32_t b23 = (codes[2] << 4) | codes[3];
+      *reinterpret_cast<uint16_t*>(packed + e0 / 2) = (uint16_t)(b01 | (b23 << 8));
+      if (sub == 0) absmax[blk] = a;
+    }
+  }
+  if (bad && nonfinite_flag != nullptr) atomicOr(nonfinite_flag, 1);
+}
+
+hipError_t launch_quantize(const void* w, int w_dtype, int64_t nelem,
+                           uint8_t* packed, float* absmax, int32_t* flag,
+                           const QuantThresholds& thr, int num_cus,
+                           hipStream_t stream) {
+  const int64_t nblocks = nelem / kBlock;
+  const int64_t waves_needed = (nblocks + 3) / 4;
+  int64_t grid = (waves_needed + 3) / 4;
+  const int64_t cap = (int64_t)num_cus * 16;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (w_dtype == kBF16)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, w, nblocks, packed, absmax, flag, thr);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, w, nblocks, packed, absmax, flag, thr);
+  return hipGetLastError();
+}
+
+}  // namespace nf4moe

@@ -1,0 +1,249 @@
+// Router top-k, token/expert pair permutation, and the per-token combine.
+//
+// The routed layer sorts token/expert pairs by expert and runs the groups
+// (experts4bit-qlora 0.22.0 README, "Which training path?"), then sums each
+// token's expert outputs back in group-sorted order.  Everything here runs on
+// the device with no host synchronisation (the zero-host-sync contract of the
+// README's "CUDA-graph decode capture" section).
+//
+// Pair id p = t*k + j.  Because a token's k experts are distinct, the rank of
+// pair (t, j) inside its expert's group is the number of EARLIER TOKENS that
+// picked the same expert.  Tokens are processed in chunks of 32: each chunk
+// keeps, per expert, a 32-bit mask of the chunk tokens that picked it.  The
+// rank is then  chunk_base[chunk][e] + popcount(mask & bits below t), a
+// stable counting sort with no sequential pass over the pairs.
+//
+// Kernels (in launch order):
+//   route_chunk_kernel  top-k + softmax weights per token (one wave per
+//                       token), per-chunk expert masks; optionally converts
+//                       the chunk's activation rows to fp16 for the GEMMs;
+//   route_scan_kernel   per-expert totals -> offsets and per-chunk bases;
+//   route_scatter_kernel  sorted_pair / pair_pos from the masks.
+
+#include "common.h"
+#include "launch.h"
+#include "route_device.h"
+
+namespace nf4moe {
+
+template <int kRegs>
+__global__ __launch_bounds__(256) void route_chunk_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int renormalize,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    uint32_t* __restrict__ chunk_masks, const void* __restrict__ x_in,
+    int x_bf16, _Float16* __restrict__ x16, int H) {
+  __shared__ uint32_t mask[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t chunk = blockIdx.x;
+  const int64_t t0 = chunk * kRouteChunk;
+  for (int e = tid; e < E; e += blockDim.x) mask[e] = 0u;
+  __syncthreads();
+
+  for (int i = wave; i < kRouteChunk; i += 4) {
+    const int64_t t = t0 + i;
+    if (t >= T) break;
+    int id;
+    float w;
+    route_one_token<kRegs>(logits + t * E, E, k, renormalize, lane, &id, &w);
+    if (lane < k) {
+      topk_ids[t * k + lane] = id;
+      topk_w[t * k + lane] = w;
+      atomicOr(&mask[id], 1u << i);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) chunk_masks[chunk * E + e] = mask[e];
+
+  // Activation rows of this chunk to fp16 (8 elements per thread and step).
+  if (x16 != nullptr && x_bf16) {
+    const int64_t rows = (T - t0) < kRouteChunk ? (T - t0) : kRouteChunk;
+    const int64_t n8 = rows * H / 8;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(x_in) + t0 * H;
+    _Float16* dst = x16 + t0 * H;
+    for (int64_t i = tid; i < n8; i += blockDim.x) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + i * 8);
+      u32x4 o;
+      o.x = pack_half2((_Float16)bf16_bits_to_f32(v.x & 0xffffu), (_Float16)bf16_bits_to_f32(v.x >> 16));
+      o.y = pack_half2((_Float16)bf16_bits_to_f32(v.y & 0xffffu), (_Float16)bf16_bits_to_f32(v.y >> 16));
+      o.z = pack_half2((_Float16)bf16_bits_to_f32(v.z & 0xffffu), (_Float16)bf16_bits_to_f32(v.z >> 16));
+      o.w = pack_half2((_Float16)bf16_bits_to_f32(v.w & 0xffffu), (_Float16)bf16_bits_to_f32(v.w >> 16));
+      *reinterpret_cast<u32x4*>(dst + i * 8) = o;
+    }
+  }
+}
+
+// Single workgroup of 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void route_scan_kernel(
+    const uint32_t* __restrict__ chunk_masks, int64_t nchunks, int E,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ chunk_base) {
+  __shared__ int32_t s_cnt[kMaxExperts];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < E) {
+    int64_t c = 0;
+    int32_t acc[4] = {0, 0, 0, 0};
+    for (; c + 4 <= nchunks; c += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += __popc(chunk_masks[(c + u) * E + e]);
+    }
+    for (; c < nchunks; ++c) acc[0] += __popc(chunk_masks[c * E + e]);
+    total = acc[0] + acc[1] + acc[2] + acc[3];
+  }
+  s_cnt[e] = (e < E) ? total : 0;
+  __syncthreads();
+  // Inclusive Hillis-Steele scan over 1024 entries.
+  for (int off = 1; off < kMaxExperts; off <<= 1) {
+    const int32_t a = (e >= off) ? s_cnt[e - off] : 0;
+    __syncthreads();
+    s_cnt[e] += a;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int32_t excl = s_cnt[e] - total;
+    expert_offsets[e] = excl;
+    if (e == E - 1) expert_offsets[E] = s_cnt[e];
+    if (chunk_base != nullptr) {
+      int32_t run = excl;
+      for (int64_t c = 0; c < nchunks; ++c) {
+        chunk_base[c * E + e] = run;
+        run += __popc(chunk_masks[c * E + e]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, const uint32_t* __restrict__ chunk_masks,
+    const int32_t* __restrict__ chunk_base, int64_t T, int E, int k,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+  const int64_t chunk = blockIdx.x;
+  const int64_t t0 = chunk * kRouteChunk;
+  int64_t t1 = t0 + kRouteChunk;
+  if (t1 > T) t1 = T;
+  for (int64_t p = t0 * k + threadIdx.x; p < t1 * k; p += blockDim.x) {
+    const int64_t t = p / k;
+    const int e = topk_ids[p];
+    const uint32_t m = chunk_masks[chunk * E + e];
+    const uint32_t below = (1u << (uint32_t)(t - t0)) - 1u;
+    const int32_t rank = chunk_base[chunk * E + e] + __popc(m & below);
+    sorted_pair[rank] = (int32_t)p;
+    if (pair_pos != nullptr) pair_pos[p] = rank;
+  }
+}
+
+// y[t] = sum_j w[t, j] * o[t*k + j]  (fp32, ascending j), per-slot rows o in
+// pair order.  8 columns per thread and step.
+template <int kOut>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const _Float16* __restrict__ o, const float* __restrict__ w, int64_t T,
+    int k, int H, void* __restrict__ y) {
+  const int64_t n8 = (int64_t)T * H / 8;
+  const int h8 = H / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / h8;
+    const int64_t c = (i - t * h8) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const float wj = w[t * k + j];
+      const u32x4 v = *reinterpret_cast<const u32x4*>(o + (t * k + j) * H + c);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x2 hv = u32_as_half2(u[q]);
+        acc[2 * q] = fmaf(wj, (float)hv.x, acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wj, (float)hv.y, acc[2 * q + 1]);
+      }
+    }
+    if constexpr (kOut == kF32) {
+      float* dst = reinterpret_cast<float*>(y) + t * H + c;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    } else if constexpr (kOut == kBF16) {
+      u32x4 r;
+      r.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+      r.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+      r.z = (uint32_t)f32_to_bf16_bits(acc[4]) | ((uint32_t)f32_to_bf16_bits(acc[5]) << 16);
+      r.w = (uint32_t)f32_to_bf16_bits(acc[6]) | ((uint32_t)f32_to_bf16_bits(acc[7]) << 16);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + t * H + c) = r;
+    } else {
+      u32x4 r;
+      r.x = pack_half2((_Float16)acc[0], (_Float16)acc[1]);
+      r.y = pack_half2((_Float16)acc[2], (_Float16)acc[3]);
+      r.z = pack_half2((_Float16)acc[4], (_Float16)acc[5]);
+      r.w = pack_half2((_Float16)acc[6], (_Float16)acc[7]);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<_Float16*>(y) + t * H + c) = r;
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  const int64_t nchunks = (a.T + kRouteChunk - 1) / kRouteChunk;
+  const int regs = (a.E + 63) / 64;
+  const dim3 grid((unsigned)nchunks), block(256);
+#define NF4MOE_ROUTE_CASE(R)                                                  \
+  case R:                                                                     \
+    hipLaunchKernelGGL(route_chunk_kernel<R>, grid, block, 0, stream,         \
+                       a.logits, a.T, a.E, a.k, a.renormalize, a.topk_ids,    \
+                       a.topk_w, a.chunk_masks, a.x_in, a.x_bf16, a.x16, a.H); \
+    break;
+  switch (regs) {
+    NF4MOE_ROUTE_CASE(1)
+    NF4MOE_ROUTE_CASE(2)
+    NF4MOE_ROUTE_CASE(4)
+    NF4MOE_ROUTE_CASE(8)
+    NF4MOE_ROUTE_CASE(16)
+    case 3:
+      hipLaunchKernelGGL(route_chunk_kernel<4>, grid, block, 0, stream, a.logits,
+                         a.T, a.E, a.k, a.renormalize, a.topk_ids, a.topk_w,
+                         a.chunk_masks, a.x_in, a.x_bf16, a.x16, a.H);
+      break;
+    case 5: case 6: case 7:
+      hipLaunchKernelGGL(route_chunk_kernel<8>, grid, block, 0, stream, a.logits,
+                         a.T, a.E, a.k, a.renormalize, a.topk_ids, a.topk_w,
+                         a.chunk_masks, a.x_in, a.x_bf16, a.x16, a.H);
+      break;
+    default:
+      hipLaunchKernelGGL(route_chunk_kernel<16>, grid, block, 0, stream, a.logits,
+                         a.T, a.E, a.k, a.renormalize, a.topk_ids, a.topk_w,
+                         a.chunk_masks, a.x_in, a.x_bf16, a.x16, a.H);
+      break;
+  }
+#undef NF4MOE_ROUTE_CASE
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream,
+                     a.chunk_masks, nchunks, a.E, a.expert_offsets, a.chunk_base);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, grid, block, 0, stream, a.topk_ids,
+                     a.chunk_masks, a.chunk_base, a.T, a.E, a.k, a.sorted_pair,
+                     a.pair_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const _Float16* o, const float* w, int64_t T, int k,
+                          int H, void* y, int y_dtype, int num_cus,
+                          hipStream_t stream) {
+  const int64_t n8 = T * H / 8;
+  int64_t grid = (n8 + 255) / 256;
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (y_dtype == kF32)
+    hipLaunchKernelGGL(combine_kernel<kF32>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, o, w, T, k, H, y);
+  else if (y_dtype == kBF16)
+    hipLaunchKernelGGL(combine_kernel<kBF16>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, o, w, T, k, H, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<kF16>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, o, w, T, k, H, y);
+  return hipGetLastError();
+}
+
+}  // namespace nf4moe

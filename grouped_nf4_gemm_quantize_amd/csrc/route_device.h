@@ -1,0 +1,79 @@
+// Device-side top-k routing of one token by one wave (shared by the routing
+// kernels and the fused decode kernel).
+#pragma once
+
+#include "common.h"
+
+namespace nf4moe {
+
+namespace route_detail {
+
+// true if b ranks before a: larger logit, or equal logit and lower id.
+__device__ __forceinline__ bool better(float bv, int bid, float av, int aid) {
+  return bv > av || (bv == av && bid < aid);
+}
+
+}  // namespace route_detail
+
+// One wave routes one token at a time.  Logit e of the token lives in lane
+// e % 64, register e / 64.
+template <int kRegs>
+__device__ __forceinline__ void route_one_token(
+    const float* __restrict__ lg_row, int E, int k, int renormalize,
+    int lane, int* out_id, float* out_w) {
+  float v[kRegs];
+  uint32_t taken = 0u;
+#pragma unroll
+  for (int r = 0; r < kRegs; ++r) {
+    const int e = lane + 64 * r;
+    v[r] = (e < E) ? lg_row[e] : -__builtin_inff();
+  }
+  float my_v = 0.f;
+  int my_id = 0;
+  float top = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) {
+      const int e = lane + 64 * r;
+      if (e < E && !((taken >> r) & 1u) && route_detail::better(v[r], e, bv, bid)) {
+        bv = v[r];
+        bid = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oid = __shfl_xor(bid, off, 64);
+      if (route_detail::better(ov, oid, bv, bid)) {
+        bv = ov;
+        bid = oid;
+      }
+    }
+    // every lane now holds the winner of round j
+    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+    if (lane == j) {
+      my_v = bv;
+      my_id = bid;
+    }
+    if (j == 0) top = bv;
+  }
+  float s;
+  float ej = (lane < k) ? expf(my_v - top) : 0.f;
+  if (renormalize) {
+    s = wave_sum(ej);
+  } else {
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) {
+      const int e = lane + 64 * r;
+      if (e < E) part += expf(v[r] - top);
+    }
+    s = wave_sum(part);
+  }
+  *out_id = my_id;
+  *out_w = ej / s;
+}
+
+}  // namespace nf4moe

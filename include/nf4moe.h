@@ -1,0 +1,233 @@
+/*
+ * nf4moe.h -- C ABI of the MI355X (gfx950) grouped NF4 MoE expert library.
+ *
+ * The library runs the routed Mixture-of-Experts expert projections directly
+ * on a frozen, fused, NF4-packed expert stack:
+ *
+ *   gate_up_proj [E, 2I, H] and down_proj [E, H, I]  (rows are [out, in]),
+ *
+ * as described on the experts4bit-qlora pages ("The problem", "Quickstart"
+ * of the 0.22.0 README) and the grouped-nf4-gemm solutions entry ("How do I
+ * run a grouped GEMM directly on NF4 packed MoE expert weights, without
+ * dequantizing to bf16 first?").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns all
+ *    memory; the library never allocates device memory.  Entry points that
+ *    need scratch take a caller-provided workspace and expose a size query.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *    default stream).  No call synchronises the host with the device, so the
+ *    calls can be captured in a HIP graph.
+ *  - Every call returns an int status: NF4MOE_OK (0) or a negative error.
+ *    Argument errors are found on the host BEFORE anything is enqueued;
+ *    nf4moe_last_error() then returns a thread-local description.  A failed
+ *    kernel launch returns NF4MOE_EHIP.  There is no fallback path.
+ *  - Storage format (pinned by the byte totals the pages print: 16.31 GB for
+ *    the 48-layer Qwen3-30B-A3B stack, "Training + expert offload" of the
+ *    0.22.0 README, and 12,846,366,720 bytes per cell in the 2026 narrative's
+ *    "What these numbers do not say"): for a stack [E, N, K],
+ *      packed [E, N, K/2] uint8, two 4-bit codes per byte, the even element
+ *             in the HIGH nibble: byte = (code[2i] << 4) | code[2i+1];
+ *      absmax [E, N, K/64] fp32, one scale per 64 consecutive elements of a
+ *             row (blocks never cross a row or an expert: "Which project
+ *             solves it" on the load_in_4bit solutions page);
+ *      weight = fp32(level[code] * absmax), level = the 16-entry NF4
+ *             codebook returned by nf4moe_codebook().
+ *  - Compute precision: fp32 accumulation ("NF4 decoded in-register inside
+ *    the GEMM, fp32 accumulation", 0.22.0 README "Which door?").  Weights
+ *    are decoded to fp16 MFMA operands (level and absmax rounded to fp16,
+ *    product rounded to fp16); activations enter the MFMA as fp16.  Values
+ *    must therefore lie in fp16 range (|v| < 65504); values below 2^-14 lose
+ *    precision gradually (fp16 subnormals).
+ */
+#ifndef NF4MOE_H
+#define NF4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define NF4MOE_OK          0
+#define NF4MOE_EINVAL     -1  /* null required pointer, non-positive size     */
+#define NF4MOE_ESHAPE     -2  /* a dimension is not a multiple it must be     */
+#define NF4MOE_EBLOCK     -3  /* blocksize other than 64                      */
+#define NF4MOE_ETOPK      -4  /* k < 1, k > E or k > NF4MOE_MAX_TOPK          */
+#define NF4MOE_EDTYPE     -5  /* unsupported dtype for this argument          */
+#define NF4MOE_EWORKSPACE -6  /* workspace smaller than the size query        */
+#define NF4MOE_EOVERFLOW  -7  /* a size overflows the 32-bit row indexing     */
+#define NF4MOE_EHIP       -8  /* a HIP runtime call or kernel launch failed   */
+
+#define NF4MOE_BLOCKSIZE   64
+#define NF4MOE_MAX_TOPK    32
+#define NF4MOE_MAX_EXPERTS 1024
+#define NF4MOE_MAX_LORA_R  16
+
+typedef enum {
+  NF4MOE_F32 = 0,
+  NF4MOE_BF16 = 1,
+  NF4MOE_F16 = 2
+} nf4moe_dtype;
+
+/* Epilogues of grouped_nf4_gemm. */
+#define NF4MOE_EPI_NONE   0
+#define NF4MOE_EPI_SWIGLU 1 /* N = 2I outputs -> I outputs: silu(first I) * next I */
+
+/* Static description of the status code (never NULL). */
+const char* nf4moe_strerror(int status);
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* nf4moe_last_error(void);
+/* Library version string, e.g. "0.1.0". */
+const char* nf4moe_version(void);
+
+/* [host] Writes the 16 fp32 NF4 levels, ascending, to out16.
+ * The levels are the 4-bit NormalFloat construction (normal quantiles with an
+ * exact zero, 8 positive and 7 negative levels, normalised to [-1, 1]); the
+ * pages fix only that training and serving share one codebook (0.22.0
+ * README, "Inference").  Returns NF4MOE_EINVAL if out16 is NULL. */
+int nf4moe_codebook(float* out16);
+
+/* Bytes of one packed stack [E, N, K]: E*N*K/2 + (E*N*K/64)*4.
+ * Returns a negative status if a size is non-positive or K % 64 != 0. */
+int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K);
+
+/* ---- NF4 blockwise quantiser ---------------------------------------------
+ * Quantises an expert stack w [E, N, K] (row-major, fp32 or bf16) with
+ * blocks of 64 consecutive elements along K, as Experts4bit.from_float does
+ * for the fused stacks (0.22.0 README "Quickstart"; blocks never cross an
+ * expert: load_in_4bit solutions page, "Which project solves it").
+ *   absmax = max |x| over the block (exact);
+ *   xn     = x / absmax (IEEE fp32 division);
+ *   code   = index of the nearest level to xn (exact comparison; a tie goes
+ *            to the lower index); an all-zero block stores absmax 0, code 7.
+ * Output bytes are identical on every run and device.
+ *   w_dtype        NF4MOE_F32 or NF4MOE_BF16 (else EDTYPE)
+ *   blocksize      must be 64 (else EBLOCK)
+ *   K              must be a positive multiple of 64 (else ESHAPE)
+ *   packed, absmax outputs as described in the conventions above
+ *   nonfinite_flag nullable device int32; set to 1 (never cleared) if any
+ *                  input element is NaN or +-Inf.  Codes of such blocks are
+ *                  unspecified.
+ */
+int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
+                         int64_t K, int blocksize, uint8_t* packed,
+                         float* absmax, int32_t* nonfinite_flag, void* stream);
+
+/* ---- router top-k and pair permutation -----------------------------------
+ * For T tokens with fp32 router logits [T, E] (E <= NF4MOE_MAX_EXPERTS):
+ *   topk_ids [T, k] int32  the k largest logits per token, descending; equal
+ *                          logits go to the lower expert id;
+ *   topk_w   [T, k] fp32   renormalize=1: softmax over the k selected logits
+ *                          (sums to 1); renormalize=0: the full-softmax
+ *                          probabilities of the selected experts;
+ *   sorted_pair [T*k]      pair ids p = t*k + j grouped by expert, ascending
+ *                          expert and ascending p inside an expert ("sort
+ *                          token/expert pairs, run the groups", 0.22.0 README
+ *                          "Which training path?");
+ *   pair_pos [T*k]         nullable; inverse permutation (pair_pos[p] = i
+ *                          iff sorted_pair[i] = p);
+ *   expert_offsets [E+1]   exclusive prefix sum of the per-expert pair counts;
+ *                          expert_offsets[E] = T*k.
+ * Logits must be finite (non-finite logits give unspecified ids).
+ * workspace: moe_route_permute_workspace(T, E, k) bytes (may be NULL if 0).
+ */
+size_t moe_route_permute_workspace(int64_t T, int E, int k);
+int moe_route_permute(const float* logits, int64_t T, int E, int k,
+                      int renormalize, int32_t* topk_ids, float* topk_w,
+                      int32_t* sorted_pair, int32_t* pair_pos,
+                      int32_t* expert_offsets, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* ---- per-expert LoRA adapter ---------------------------------------------
+ * delta = scale * (a A_e^T) B_e^T with A [E, r, K] and B [E, N, r] (the
+ * trainable per-expert low-rank delta of ExpertsLoRA, solutions index "How do
+ * I QLoRA-train the fused experts"; r=8, alpha=16 in the 0.22.0 Quickstart,
+ * so scale = alpha / r).  1 <= r <= NF4MOE_MAX_LORA_R; dtype BF16 or F16.
+ * Pass a NULL pointer to the struct for "no adapter".
+ */
+typedef struct {
+  const void* A;
+  const void* B;
+  int r;
+  float scale;
+  int dtype;
+} nf4moe_lora;
+
+/* ---- grouped NF4 GEMM ----------------------------------------------------
+ * out_row(i) = a[src(i)] . W_e^T  (+ LoRA delta)  for rows
+ * expert_offsets[e] <= i < expert_offsets[e+1], with W_e = dequant(packed[e],
+ * absmax[e]) [N, K], decoded in registers (never written to memory) and fp32
+ * accumulation: the single-launch grouped kernel of grouped-nf4-gemm ("How do
+ * I run a grouped GEMM directly on NF4 packed MoE expert weights").
+ *   a [a_rows, K]   activations, F16 or BF16 (else EDTYPE);
+ *   gather          nullable int32 [P]; src(i) = gather[i] / gather_div,
+ *                   else src(i) = i.  Indices are not checked on the device:
+ *                   src(i) must be < a_rows;
+ *   packed, absmax  the stack [E, N, K] (K % 64 == 0, N % 16 == 0);
+ *   expert_offsets  device int32 [E+1], non-decreasing, offsets[0] = 0 and
+ *                   offsets[E] <= P (rows at and beyond offsets[E] are not
+ *                   written);
+ *   P               host-side upper bound of the row count (sizes the grid);
+ *   lora            [host] nullable adapter on this projection (added before
+ *                   the epilogue);
+ *   epilogue        NF4MOE_EPI_NONE, or NF4MOE_EPI_SWIGLU (N = 2I must be a
+ *                   multiple of 32; the output has N/2 columns);
+ *   row_scale       nullable fp32 [P], multiplies output row i;
+ *   scatter         nullable int32 [P]; output row i is written to row
+ *                   scatter[i] of out, else to row i;
+ *   out             F32, F16 or BF16 rows of N (or N/2) elements.
+ * One kernel launch; no workspace (the per-expert tile table is rebuilt from
+ * expert_offsets inside the kernel).
+ */
+int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
+                     const int32_t* gather, int gather_div,
+                     const uint8_t* packed, const float* absmax,
+                     const int32_t* expert_offsets, int E, int64_t P,
+                     int64_t N, int64_t K, const nf4moe_lora* lora,
+                     int epilogue, const float* row_scale,
+                     const int32_t* scatter, void* out, int out_dtype,
+                     void* stream);
+
+/* ---- full routed-expert layer --------------------------------------------
+ * y [T, H] = sum_j w_tj * down_e(silu(gate_e(x_t)) * up_e(x_t)) over the k
+ * experts the router picks for token t: route + permute, gate_up (+LoRA),
+ * SwiGLU, down (+LoRA), combine over the slots in ascending slot order
+ * (experts summed per token in group-sorted pair order, 0.22.0 README
+ * "Which training path?").  T == 1 runs the split-K decode GEMV kernels (the
+ * single-token fast path, 0.22.0 README "Inference"); otherwise the grouped
+ * MFMA kernels.  Same contract either way.
+ *   x [T, H]        BF16 or F16 activations;
+ *   router_logits   fp32 [T, E];
+ *   H, I            multiples of 64; E <= NF4MOE_MAX_EXPERTS; k <= min(E, 32);
+ *   gu_*            gate_up stack [E, 2I, H]; dn_* down stack [E, H, I];
+ *   gu_lora/dn_lora [host] nullable adapters (r must match the size query);
+ *   y               [T, H] in y_dtype (BF16, F16 or F32);
+ *   workspace       moe_expert_forward_workspace(T, H, I, E, k) bytes.
+ */
+size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k);
+int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
+                       int64_t T, int H, int I, int E, int k, int renormalize,
+                       const uint8_t* gu_packed, const float* gu_absmax,
+                       const uint8_t* dn_packed, const float* dn_absmax,
+                       const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora,
+                       void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/* Device-pointer views into a moe_expert_forward workspace (for inspection of
+ * the routing a forward used; valid after the forward completes on its
+ * stream).  Any out-pointer may be NULL.  Returns a negative status on bad
+ * sizes. */
+int moe_expert_forward_routing(void* workspace, int64_t T, int H, int I,
+                               int E, int k, int32_t** topk_ids,
+                               float** topk_w, int32_t** sorted_pair,
+                               int32_t** expert_offsets);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4MOE_H */
