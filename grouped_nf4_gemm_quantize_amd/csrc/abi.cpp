@@ -169,7 +169,7 @@ FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k) {
 
 bool use_decode_path(int64_t T, int H, int I, int k, const nf4moe_lora* a,
                      const nf4moe_lora* b) {
-  return T == 1 && a == nullptr && b == nullptr && H <= 32768 &&
+  return T == 1 && a == nullptr && b == nullptr && H <= 8192 &&
          (int64_t)k * I <= 32768;
 }
 
@@ -283,7 +283,7 @@ int moe_route_permute(const float* logits, int64_t T, int E, int k,
   return ok();
 }
 
-static int gemm_common(const void* a, int a_dtype, const int32_t* gather,
+static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t* gather,
                        int gather_div, const uint8_t* packed, const float* absmax,
                        const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
                        const nf4moe_lora* lora, int epilogue,
@@ -294,6 +294,7 @@ static int gemm_common(const void* a, int a_dtype, const int32_t* gather,
   if (st != NF4MOE_OK) return st;
   GemmArgs g{};
   g.a = a;
+  g.a_rows = a_rows;
   g.a_bf16 = a_dtype == NF4MOE_BF16;
   g.gather = gather;
   g.gather_div = gather ? gather_div : 1;
@@ -351,13 +352,17 @@ int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
     return fail(NF4MOE_EINVAL, "gather_div must be >= 1");
   if (P >= INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX / 2)
     return fail(NF4MOE_EOVERFLOW, "P, N or K too large for 32-bit row indexing");
+  // the kernel addresses activations and one expert's weights with 32-bit
+  // byte offsets
+  if (a_rows * K * 2 > (int64_t)UINT32_MAX || N * K / 2 > (int64_t)UINT32_MAX)
+    return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
   int st = check_lora(lora, "lora");
   if (st != NF4MOE_OK) return st;
-  if (!aligned(a, 16) || !aligned(packed, 8) || !aligned(absmax, 4) ||
+  if (!aligned(a, 16) || !aligned(packed, 16) || !aligned(absmax, 4) ||
       !aligned(out, out_dtype == NF4MOE_F32 ? 4 : 2))
-    return fail(NF4MOE_EINVAL, "misaligned buffer (a needs 16 bytes, packed 8)");
+    return fail(NF4MOE_EINVAL, "misaligned buffer (a and packed need 16 bytes)");
   if (P == 0) return ok();
-  st = gemm_common(a, a_dtype, gather, gather_div, packed, absmax, expert_offsets,
+  st = gemm_common(a, a_dtype, a_rows, gather, gather_div, packed, absmax, expert_offsets,
                    E, P, N, K, lora, epilogue, row_scale, scatter, out, out_dtype,
                    (hipStream_t)stream);
   if (st != NF4MOE_OK) return st;
@@ -412,6 +417,11 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
   st = check_lora(dn_lora, "dn_lora");
   if (st != NF4MOE_OK) return st;
   const int64_t P = T * k;
+  // the GEMMs address activations and one expert's weights with 32-bit byte
+  // offsets
+  if (T * H * 2 > (int64_t)UINT32_MAX || P * I * 2 > (int64_t)UINT32_MAX ||
+      2 * (int64_t)I * H / 2 > (int64_t)UINT32_MAX)
+    return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
   if (!aligned(x, 16) || !aligned(gu_packed, 16) || !aligned(dn_packed, 16) ||
       !aligned(gu_absmax, 4) || !aligned(dn_absmax, 4) || !aligned(y, 16))
     return fail(NF4MOE_EINVAL, "misaligned buffer (x, y and packed stacks need 16 bytes)");
@@ -476,11 +486,11 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
   const void* xa = conv ? (const void*)(ws + L.x16) : x;
   _Float16* h = (_Float16*)(ws + L.h);
   _Float16* o = (_Float16*)(ws + L.o);
-  st = gemm_common(xa, NF4MOE_F16, r.sorted_pair, k, gu_packed, gu_absmax,
+  st = gemm_common(xa, NF4MOE_F16, T, r.sorted_pair, k, gu_packed, gu_absmax,
                    r.expert_offsets, E, P, 2 * (int64_t)I, H, gu_lora,
                    NF4MOE_EPI_SWIGLU, nullptr, nullptr, h, NF4MOE_F16, s);
   if (st != NF4MOE_OK) return st;
-  st = gemm_common(h, NF4MOE_F16, nullptr, 1, dn_packed, dn_absmax, r.expert_offsets,
+  st = gemm_common(h, NF4MOE_F16, P, nullptr, 1, dn_packed, dn_absmax, r.expert_offsets,
                    E, P, H, I, dn_lora, NF4MOE_EPI_NONE, nullptr,
                    r.sorted_pair, o, NF4MOE_F16, s);
   if (st != NF4MOE_OK) return st;

@@ -78,16 +78,19 @@ struct Lut {
 };
 
 // Fill the LDS table from the fp32 levels (each half rounded to nearest-even
-// fp16).  Must be followed by a barrier before the first lookup.
+// fp16).  `stage` is a 16-entry LDS scratch array.  The fill ends with a
+// barrier, so the table is ready to use on return.
 template <int kLutCopies>
-__device__ __forceinline__ void lut_fill(uint32_t* lut, const float* levels,
-                                         int tid, int nthreads) {
+__device__ __forceinline__ void lut_fill(uint32_t* lut, uint16_t* stage,
+                                         const float* levels, int tid,
+                                         int nthreads) {
+  if (tid < 16) stage[tid] = __builtin_bit_cast(uint16_t, (_Float16)levels[tid]);
+  __syncthreads();
   for (int i = tid; i < 256 * kLutCopies; i += nthreads) {
-    int b = i / kLutCopies;
-    _Float16 lo = (_Float16)levels[b >> 4];
-    _Float16 hi = (_Float16)levels[b & 15];
-    lut[i] = pack_half2(lo, hi);
+    const int b = i / kLutCopies;
+    lut[i] = (uint32_t)stage[b >> 4] | ((uint32_t)stage[b & 15] << 16);
   }
+  __syncthreads();
 }
 
 // Per-lane constant of the lookup address: 4 * (lane % copies).

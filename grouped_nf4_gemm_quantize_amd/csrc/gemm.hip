@@ -5,39 +5,47 @@
 // accumulation that replaces the dequantise-then-GEMM round trip
 // (experts4bit-qlora 0.22.0 README, "The package family"; grouped-nf4-gemm
 // solutions entry "How do I run a grouped GEMM directly on NF4 packed MoE
-// expert weights").  The weights never exist in memory in decoded form.
+// expert weights").  Decoded weights never exist in memory.
 //
-// Tiling (gfx950, wave64, v_mfma_f32_16x16x32_f16):
-//   workgroup = 4 waves = one M-tile of 128 rows of ONE expert x 512 weight
-//   rows (N).  The waves split N only: wave w owns 128 weight rows (8 n-tiles
-//   of 16) and all 128 rows (8 m-tiles), i.e. 256 fp32 accumulators per lane.
-//   Every weight is therefore decoded exactly once per workgroup.
-//   K advances 64 at a time (one absmax block): two MFMA k-substeps of 32.
+// Work decomposition (gfx950, wave64, v_mfma_f32_32x32x16_f16):
+//   A tile = 128 rows of ONE expert (an M-tile) x 512 weight rows (N).
+//   Workgroup = 4 waves; the waves split N only, so wave w owns 128 weight
+//   rows (4 n-tiles of 32) against all 128 rows (4 m-tiles of 32): 256 fp32
+//   accumulators per lane (the accumulation registers), and every weight is
+//   decoded exactly once per tile.
+//   K advances 64 per step (one absmax block) in four MFMA substeps of 16.
+//   Workgroups are persistent (one per CU): the decode table and the
+//   per-expert tile table are built once, then tiles are taken in an order
+//   that gives the 32 workgroups of one XCD consecutive tiles (tiles sharing
+//   activation rows or weight rows meet in that XCD's L2).
 //
-// Operand paths:
-//   A (activations, fp16) -- gathered rows staged through a double-buffered
-//     LDS tile (128 rows x 64 k, 144-byte padded rows so the 16-byte
-//     fragment reads are conflict-free) and shared by the 4 waves.
-//   B (weights) -- each lane loads its 8 packed bytes (16 codes) of a weight
-//     row straight from HBM into registers and decodes them through the LDS
-//     byte->half2 table (common.h): one v_perm + one ds_read_b32 per two
-//     weights, then one v_pk_mul_f16 by the block's absmax.
-//   The MFMA k order inside an instruction only has to agree between A and B:
-//   lane group g (= lane/16) supplies k in [16g, 16g+16) of the 64-block,
-//   substep s takes [16g + 8s, 16g + 8s + 8).
+// Operand staging: activations (fp16), packed weights, absmax (and the LoRA
+// A rows) of a step are copied global -> LDS by buffer loads that write LDS
+// directly (no VGPR staging) into a 3-stage ring, two steps ahead of use.
+// The copies are issued from inline assembly, so the compiler does not track
+// them: the kernel itself waits with a counted s_waitcnt on the vector-memory
+// counter (the stage in use is complete once at most the newer stage's
+// copies are pending) followed by s_barrier, which keeps the newer stage in
+// flight across the barrier.  Every wave issues the same number of copies
+// per step, so one immediate count holds for all of them.
+//   A stage: 128 rows x 128 B; the 16-byte chunk c of row r sits at chunk
+//            c ^ (r & 7) (XOR swizzle: fragment reads are conflict-free).
+//   B stage: 512 rows x 32 B (64 codes of a block); the 16-byte half h of
+//            row l sits at half h ^ ((l >> 2) & 1).
+//   S stage: 512 fp32 absmax.   L stage: 16 LoRA A rows x 128 B.
+// Buffer resources bound every copy: a source offset outside the tensor
+// reads zeros instead of faulting.
+// Decode: the lane's 8 codes for one MFMA operand (one u32) go through the
+// LDS byte -> half2 table (common.h): per byte one address computation and
+// one ds_read_b32, then one v_pk_mul_f16 by the block's absmax.
+// MFMA k order: within a 64-block, lane group g = lane/32 takes k in
+// [32g, 32g+32); substep s uses [32g + 8s, 32g + 8s + 8) for both operands.
 //
-// Epilogues: optional per-expert LoRA (u = X A_e^T accumulated as an extra
-// 16-column MFMA tile, split over the waves by k-step and reduced in LDS,
-// then G += scale * u B_e^T as one more MFMA step), SwiGLU (gate and up rows
-// of the same output column sit in the same lane), row scale, scatter.
-//
-// Tile scheduling: every workgroup rebuilds the per-expert M-tile table from
-// expert_offsets in LDS (one load and a scan, overlapped with filling the
-// decode table), so no host synchronisation and no extra launch is needed;
-// the grid is sized from the upper bound ceil(P/128) + E and surplus
-// workgroups exit.  blockIdx is remapped
-// so that the workgroups one XCD runs back to back share an M-tile (its A
-// rows stay in that XCD's L2).
+// Epilogues: optional per-expert LoRA (u = X A_e^T on 16x16x32 MFMAs, each
+// wave for its own 32 rows, exchanged through LDS in fp16 with the LoRA scale
+// applied, then G += u B_e^T as one more 32x32x16 MFMA per accumulator tile),
+// SwiGLU (gate and up columns of one output column share a lane), row scale,
+// scatter, conversion to the output dtype.
 
 #include "common.h"
 #include "launch.h"
@@ -48,14 +56,75 @@ __constant__ float c_levels_gemm[16] = NF4MOE_LEVELS_INIT;
 
 namespace {
 
-constexpr int BM = kGemmBM;            // 128 rows per M-tile
-constexpr int BK = 64;                 // k per step (one absmax block)
-constexpr int MT = BM / 16;            // 8 m-tiles of 16 rows
-constexpr int NT = 8;                  // 8 n-tiles of 16 weight rows per wave
+constexpr int BM = kGemmBM;       // 128 rows per M-tile
+constexpr int BK = 64;            // k per step (one absmax block)
 constexpr int NWAVES = 4;
-constexpr int kLutCopies = 64;
-constexpr int A_STRIDE = BK * 2 + 16;  // bytes per LDS A row (padded)
-constexpr int A_BUF = BM * A_STRIDE;   // bytes per A buffer
+constexpr int MT = BM / 32;       // 4 m-tiles of 32 rows
+constexpr int NT = 4;             // 4 n-tiles of 32 weight rows per wave
+constexpr int BNW = NT * 32;      // 128 weight rows per wave
+constexpr int BN = NWAVES * BNW;  // 512 weight rows per workgroup
+constexpr int kCopies = 32;
+constexpr int OFF_B = BM * BK * 2;             // A: 16384 B
+constexpr int OFF_S = OFF_B + BN * BK / 2;     // B: 16384 B
+constexpr int OFF_L = OFF_S + BN * 4;          // S: 2048 B
+constexpr int STAGE = OFF_L + kMaxLoraR * BK * 2;  // L: 2048 B -> 36864 B
+constexpr int kStages = 3;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+}  // namespace
+
+__shared__ __attribute__((aligned(16))) char g_ring[kStages * STAGE];
+__shared__ uint32_t g_lut[256 * kCopies];
+__shared__ __attribute__((aligned(16))) _Float16 g_u[BM * kMaxLoraR];
+__shared__ int32_t g_tiles[kMaxExperts + 1];
+__shared__ uint16_t g_lstage[16];
+__shared__ int32_t g_wsum[NWAVES];
+
+namespace {
+
+// ---- buffer resources and the direct-to-LDS copies -------------------------
+
+// Raw buffer resource over [base, base + bytes): stride 0, offset-addressed.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)p);
+}
+
+// Lane i copies 16 (resp. 4) bytes from rsrc + voff + soff to LDS address
+// lds + 16 i (resp. 4 i).  M0 carries the LDS base; one wait state separates
+// its write from the load.  The kernel uses M0 for nothing else.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending
+// and its LDS operations are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- small helpers ---------------------------------------------------------
 
 template <int kOut>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
@@ -68,7 +137,6 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   }
 }
 
-// 8 bf16 (two u32x4 halves packed as u32x4) -> 8 fp16 packed as u32x4.
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   u32x4 o;
   o.x = pack_half2((_Float16)bf16_bits_to_f32(v.x & 0xffffu), (_Float16)bf16_bits_to_f32(v.x >> 16));
@@ -78,334 +146,374 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return o;
 }
 
-__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) {
-  return __builtin_bit_cast(f16x8, v);
-}
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+__device__ __forceinline__ uint32_t lut_read(uint32_t addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(g_lut) + addr);
+}
+
+// 8 codes -> 8 fp16 weights (x absmax), as an MFMA operand.
+__device__ __forceinline__ f16x8 decode_scaled(uint32_t q, uint32_t lane_off, f16x2 sc) {
+  const uint32_t d0 = lut_read(lut_addr<kCopies, 0>(q, lane_off));
+  const uint32_t d1 = lut_read(lut_addr<kCopies, 1>(q, lane_off));
+  const uint32_t d2 = lut_read(lut_addr<kCopies, 2>(q, lane_off));
+  const uint32_t d3 = lut_read(lut_addr<kCopies, 3>(q, lane_off));
+  const u32x4 v = {half2_as_u32(u32_as_half2(d0) * sc), half2_as_u32(u32_as_half2(d1) * sc),
+                   half2_as_u32(u32_as_half2(d2) * sc), half2_as_u32(u32_as_half2(d3) * sc)};
+  return as_f16x8(v);
+}
+
+// Copy sources of one tile: buffer resources (scalar) and per-lane byte
+// offsets (fixed for the tile; the step adds a scalar offset).
+struct Src {
+  i32x4 a_rsrc, b_rsrc, s_rsrc, l_rsrc;
+  uint32_t a_off[4];  // A: 4 x 16 B per lane (1 KB per wave instruction)
+  uint32_t b_off[4];  // B: 4 x 16 B
+  uint32_t s_off[2];  // absmax: 2 x 4 B
+  uint32_t l_off[2];  // LoRA A: 2 x 4 B
+};
+
+template <bool kLora>
+constexpr int dma_per_step() { return kLora ? 12 : 10; }
+
+template <bool kLora>
+__device__ __forceinline__ void issue_step(const Src& s, int kb, uint32_t st, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(s.a_rsrc, s.a_off[i], (uint32_t)kb * (BK * 2), st + (wave * 4 + i) * 1024);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(s.b_rsrc, s.b_off[i], (uint32_t)kb * (BK / 2), st + OFF_B + (wave * 4 + i) * 1024);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    dma4(s.s_rsrc, s.s_off[i], (uint32_t)kb * 4, st + OFF_S + (wave * 2 + i) * 256);
+  if constexpr (kLora) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma4(s.l_rsrc, s.l_off[i], (uint32_t)kb * (BK * 2), st + OFF_L + (wave * 2 + i) * 256);
+  }
+}
+
+// Per-lane LDS read offsets, fixed for the kernel.
+struct Rd {
+  uint32_t a[4];   // A fragment of substep s (m-tile 0; + 4096 per m-tile)
+  uint32_t b;      // packed row of n-tile 0 (+ 1024 per n-tile)
+  uint32_t s;      // absmax of n-tile 0 (+ 128 per n-tile)
+  uint32_t ua[4];  // LoRA: A fragment (16x16x32) of this wave's rows, [m16 * 2 + k half]
+  uint32_t ul;     // LoRA: A_e fragment of this lane (k half 0; + 64 B for half 1)
+  uint32_t lane_off;
+};
+
+// One k-step on the stage at LDS byte offset `st`.  MTV = m-tiles (of 32
+// rows) holding valid rows.
+template <int MTV, bool kLora, bool kABf16>
+__device__ __forceinline__ void compute_step(const char* st, const Rd& rd, int lora_r,
+                                             int lora_bf16, int lane,
+                                             f32x16 (&acc)[MT][NT], f32x4 (&acc_u)[2]) {
+  // this wave's packed weights and absmax for the step
+  u32x4 bq[NT];
+  f16x2 sc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    bq[nt] = *reinterpret_cast<const u32x4*>(st + OFF_B + rd.b + nt * 1024);
+    const _Float16 sh = (_Float16)*reinterpret_cast<const float*>(st + OFF_S + rd.s + nt * 128);
+    sc[nt] = f16x2{sh, sh};
+  }
+
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f16x8 af[MT];
+#pragma unroll
+    for (int mt = 0; mt < MTV; ++mt) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.a[s] + mt * 4096);
+      if constexpr (kABf16) v = bf16x8_to_f16x8(v);
+      af[mt] = as_f16x8(v);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t q = s == 0 ? bq[nt].x : (s == 1 ? bq[nt].y : (s == 2 ? bq[nt].z : bq[nt].w));
+      const f16x8 bf = decode_scaled(q, rd.lane_off, sc[nt]);
+#pragma unroll
+      for (int mt = 0; mt < MTV; ++mt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf, acc[mt][nt], 0, 0, 0);
+    }
+  }
+
+  if constexpr (kLora) {
+    // u[32 rows of this wave][16 ranks] += X . A_e^T over this step's 64 k
+    const bool live = (lane & 15) < lora_r;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 l = *reinterpret_cast<const u32x4*>(st + OFF_L + rd.ul + s2 * 64);
+      if (lora_bf16) l = bf16x8_to_f16x8(l);
+      if (!live) l = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int m16 = 0; m16 < 2; ++m16) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.ua[m16 * 2 + s2]);
+        if constexpr (kABf16) v = bf16x8_to_f16x8(v);
+        acc_u[m16] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l),
+                                                            acc_u[m16], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The k-loop of one tile: copies run two steps ahead through the ring.
+template <int MTV, bool kLora, bool kABf16>
+__device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
+                                      int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
+                                      f32x4 (&acc_u)[2]) {
+  constexpr int ND = dma_per_step<kLora>();
+  const uint32_t ring = lds_addr(g_ring);
+  issue_step<kLora>(src, 0, ring, wave);
+  if (nk > 1) issue_step<kLora>(src, 1, ring + STAGE, wave);
+  int cur = 0;  // stage of step kb
+  for (int kb = 0; kb < nk; ++kb) {
+    // stage kb is complete once only step kb+1's copies may still be pending
+    if (kb + 1 < nk) wait_vm_barrier<ND>(); else wait_vm_barrier<0>();
+    if (kb + 2 < nk) {
+      const int nxt = cur == 0 ? 2 : cur - 1;  // (cur + 2) mod 3
+      issue_step<kLora>(src, kb + 2, ring + nxt * STAGE, wave);
+    }
+    compute_step<MTV, kLora, kABf16>(g_ring + cur * STAGE, rd, lora_r, lora_bf16, lane, acc,
+                                     acc_u);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+}
+
 }  // namespace
 
 template <bool kSwiglu, bool kLora, bool kABf16, int kOut>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g,
-                                                              int n_tiles) {
-  __shared__ uint32_t s_lut[256 * kLutCopies];
-  __shared__ __attribute__((aligned(16))) char s_a[2 * A_BUF];
-  __shared__ int32_t s_tiles[kMaxExperts + 1];
-
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g4 = lane >> 4;   // lane group: k sub-range
-  const int c16 = lane & 15;  // row of an A fragment / column of a B fragment
+  const int n32 = lane & 31;  // column of a B operand / row of an A operand
+  const int g2 = lane >> 5;   // k half of the operands
+  const int c16 = lane & 15, g4 = lane >> 4;  // 16x16x32 operand coordinates
 
-  lut_fill<kLutCopies>(s_lut, c_levels_gemm, tid, 256);
-  // M-tile table from the offsets: thread t owns experts 4t..4t+3; an
-  // exclusive scan over the 256 thread sums gives each expert's first tile.
+  lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm, tid, 256);
+
+  // M-tile table from the offsets: thread t owns experts 4t..4t+3
   {
-    __shared__ int32_t s_wave_sum[NWAVES];
     int32_t cnt[4];
     int32_t local = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int ex = tid * 4 + u;
       cnt[u] = 0;
-      if (ex < g.E) {
-        const int32_t rows = g.offsets[ex + 1] - g.offsets[ex];
-        cnt[u] = (rows + BM - 1) / BM;
-      }
+      if (ex < g.E) cnt[u] = (g.offsets[ex + 1] - g.offsets[ex] + BM - 1) / BM;
       local += cnt[u];
     }
-    int32_t incl = local;  // inclusive scan inside the wave
+    int32_t incl = local;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int32_t v = __shfl_up(incl, off, 64);
       if (lane >= off) incl += v;
     }
-    if (lane == 63) s_wave_sum[wave] = incl;
+    if (lane == 63) g_wsum[wave] = incl;
     __syncthreads();
-    int32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wave_sum[w];
-    int32_t run = base + incl - local;
+    int32_t run = incl - local;
+    for (int w = 0; w < wave; ++w) run += g_wsum[w];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int ex = tid * 4 + u;
-      if (ex < g.E) s_tiles[ex] = run;
+      if (ex < g.E) g_tiles[ex] = run;
       run += cnt[u];
     }
-    if (tid == 255) s_tiles[g.E] = run;
+    if (tid == 255) g_tiles[g.E] = run;
   }
   __syncthreads();
-
-  // ---- which (expert, M-tile, N-tile) this workgroup computes
-  const int per_xcd = gridDim.x >> 3;  // grid is a multiple of 8
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  const int mt_global = logical / n_tiles;
-  const int n_idx = logical - mt_global * n_tiles;
-  if (mt_global >= s_tiles[g.E]) return;  // surplus workgroup (uniform exit)
-  int lo = 0, hi = g.E;  // s_tiles[lo] <= mt_global < s_tiles[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_tiles[mid] <= mt_global) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int m_local = mt_global - s_tiles[e];
-  const int off_e = g.offsets[e];
-  const int cnt_e = g.offsets[e + 1] - off_e;
-  const int row0 = off_e + m_local * BM;
-  const int rows_valid = min(BM, cnt_e - m_local * BM);
-  const int mt_valid = (rows_valid + 15) >> 4;
 
   const int N = g.N;
   const int K = g.K;
+  const int I = N >> 1;  // SwiGLU: output columns
   const int nk = K / BK;
-  const int I = N >> 1;  // SwiGLU only
 
-  // ---- A staging assignment: thread -> 4 (row, 16-byte chunk) slots
-  const int a_chunk = tid & 7;
-  int64_t a_off[4];
-  bool a_ok[4];
+  Rd rd;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    a_ok[i] = r < rows_valid;
-    int64_t src = 0;
-    if (a_ok[i]) {
-      const int idx = row0 + r;
-      src = g.gather ? (int64_t)(g.gather[idx] / g.gather_div) : (int64_t)idx;
+  for (int s = 0; s < 4; ++s) rd.a[s] = n32 * 128 + (((g2 * 4 + s) ^ (n32 & 7)) << 4);
+  rd.b = (wave * BNW + n32) * 32 + ((g2 ^ ((n32 >> 2) & 1)) << 4);
+  rd.s = (wave * BNW + n32) * 4;
+  // LoRA operands of 16x16x32: A row m16*16 + c16 of this wave's 32 rows and
+  // k chunk 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
+#pragma unroll
+  for (int m16 = 0; m16 < 2; ++m16)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int row = wave * 32 + m16 * 16 + c16;
+      rd.ua[m16 * 2 + s2] = row * 128 + (((4 * s2 + g4) ^ (row & 7)) << 4);
     }
-    a_off[i] = src * K + a_chunk * 8;  // element offset at k = 0
-  }
+  rd.ul = c16 * 128 + g4 * 16;
+  rd.lane_off = (uint32_t)(lane & 31) * 4u;
 
-  // ---- B assignment: n-tile nt of this wave -> weight row of lane column
-  const uint8_t* b_ptr[NT];
-  const float* s_ptr[NT];
-  bool n_ok[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int nrow, base;
+  // weight row of LDS B row l (0..511) of N-tile n_idx, clamped to a valid row
+  auto weight_row = [&](int l, int n_idx) -> int {
+    const int w = l >> 7, nt = (l >> 5) & 3, n = l & 31;
+    int row;
     if constexpr (kSwiglu) {
-      base = n_idx * 256 + wave * 64 + (nt & 3) * 16;
-      n_ok[nt] = base < I;
-      nrow = (nt < 4 ? 0 : I) + base + c16;
+      const int col = n_idx * 256 + w * 64 + (nt & 1) * 32 + n;
+      row = (col < I ? col : I - 1) + (nt >= 2 ? I : 0);
     } else {
-      base = n_idx * 512 + wave * 128 + nt * 16;
-      n_ok[nt] = base < N;
-      nrow = base + c16;
+      const int col = n_idx * 512 + w * 128 + nt * 32 + n;
+      row = col < N ? col : N - 1;
     }
-    if (!n_ok[nt]) nrow = 0;
-    const int64_t wrow = (int64_t)e * N + nrow;
-    b_ptr[nt] = g.packed + wrow * (K / 2) + g4 * 8;
-    s_ptr[nt] = g.absmax + wrow * (K / BK);
-  }
-  bool any_n = false;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) any_n |= n_ok[nt];
+    return row;
+  };
 
-  const uint32_t lane_off = lut_lane_offset<kLutCopies>(lane);
+  const i32x4 a_rsrc = make_rsrc(g.a, (uint32_t)(g.a_rows * (int64_t)K * 2));
+  const int total = __builtin_amdgcn_readfirstlane(g_tiles[g.E]) * n_tiles;
+  const int G = gridDim.x;  // a multiple of 8
+  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  for (int r = 0;; ++r) {
+    const int tix = r * G + xcd * (G >> 3) + pos;
+    if (tix >= total) break;
+    const int mt_global = tix / n_tiles;
+    const int n_idx = tix - mt_global * n_tiles;
+    int lo = 0, hi = g.E;  // g_tiles[lo] <= mt_global < g_tiles[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g_tiles[mid] <= mt_global) lo = mid; else hi = mid;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int m_local = mt_global - __builtin_amdgcn_readfirstlane(g_tiles[e]);
+    const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + m_local * BM;
+    const int rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
+    const int mtv = (rows_valid + 31) >> 5;
 
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  f32x4 acc_u[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc_u[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- prologue: A(0) -> LDS buffer 0, B(0) -> registers
-  u32x4 a_reg[4];
-  auto load_a = [&](int kb) {
+    Src src;
+    src.a_rsrc = a_rsrc;
+    const uint32_t b_bytes = (uint32_t)N * (uint32_t)(K / 2);
+    const uint32_t s_bytes = (uint32_t)N * (uint32_t)nk * 4u;
+    src.b_rsrc = make_rsrc(reinterpret_cast<const char*>(g.packed) + (int64_t)e * b_bytes, b_bytes);
+    src.s_rsrc = make_rsrc(reinterpret_cast<const char*>(g.absmax) + (int64_t)e * s_bytes, s_bytes);
+    // A: wave instruction i covers LDS chunks [64 i, 64 i + 64) = rows 8i..8i+7
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (a_ok[i]) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const uint16_t*>(g.a) + a_off[i] + (int64_t)kb * BK);
-        a_reg[i] = kABf16 ? bf16x8_to_f16x8(v) : v;
-      } else {
-        a_reg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int c = (wave * 4 + i) * 64 + lane;
+      const int row = c >> 3;
+      const int gchunk = (c & 7) ^ (row & 7);
+      const int rr = row < rows_valid ? row : 0;
+      const int idx = row0 + rr;
+      const uint32_t a_src = g.gather ? (uint32_t)(g.gather[idx] / g.gather_div) : (uint32_t)idx;
+      src.a_off[i] = (a_src * (uint32_t)K + gchunk * 8) * 2;
     }
-  };
-  auto store_a = [&](int buf) {
+    // B: wave instruction i covers LDS rows [32 i, 32 i + 32), two 16-B halves each
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<u32x4*>(s_a + buf * A_BUF + r * A_STRIDE + a_chunk * 16) = a_reg[i];
+      const int c = (wave * 4 + i) * 64 + lane;
+      const int l = c >> 1;
+      const int half = (c & 1) ^ ((l >> 2) & 1);
+      src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + half * 16;
     }
-  };
-  u32x2 b_reg[NT];
-  float s_reg[NT];
-  auto load_b = [&](int kb) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (n_ok[nt]) {
-        b_reg[nt] = *reinterpret_cast<const u32x2*>(b_ptr[nt] + (int64_t)kb * 32);
-        s_reg[nt] = s_ptr[nt][kb];
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int l = (wave * 2 + i) * 64 + lane;
+      src.s_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)nk * 4u;
     }
-  };
+    if constexpr (kLora) {
+      const uint32_t l_bytes = (uint32_t)g.lora_r * (uint32_t)K * 2u;
+      src.l_rsrc = make_rsrc(reinterpret_cast<const char*>(g.lora_a) + (int64_t)e * l_bytes, l_bytes);
+      // LoRA A: 16 rows x 128 B per step; dword d of the block is row d / 32
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int d = (wave * 2 + i) * 64 + lane;
+        const int rho = d >> 5;
+        const int rc = rho < g.lora_r ? rho : 0;
+        src.l_off[i] = (uint32_t)rc * (uint32_t)K * 2u + (uint32_t)(d & 31) * 4u;
+      }
+    } else {
+      src.l_rsrc = i32x4{0, 0, 0, 0};
+      src.l_off[0] = src.l_off[1] = 0;
+    }
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nk; ++kb) {
-    const int buf = kb & 1;
-    // decode this step's weights (registers loaded during the previous step)
-    u32x4 bf[NT][2];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (n_ok[nt]) {
-        const _Float16 sh = (_Float16)s_reg[nt];
-        const f16x2 sc = {sh, sh};
-        uint32_t d0[4], d1[4];
-        decode8<kLutCopies>(s_lut, lane_off, b_reg[nt].x, d0);
-        decode8<kLutCopies>(s_lut, lane_off, b_reg[nt].y, d1);
-        bf[nt][0] = u32x4{half2_as_u32(u32_as_half2(d0[0]) * sc), half2_as_u32(u32_as_half2(d0[1]) * sc),
-                          half2_as_u32(u32_as_half2(d0[2]) * sc), half2_as_u32(u32_as_half2(d0[3]) * sc)};
-        bf[nt][1] = u32x4{half2_as_u32(u32_as_half2(d1[0]) * sc), half2_as_u32(u32_as_half2(d1[1]) * sc),
-                          half2_as_u32(u32_as_half2(d1[2]) * sc), half2_as_u32(u32_as_half2(d1[3]) * sc)};
-      }
-    }
-    // LoRA A operand of this step (one wave per step, rotating)
-    const bool lora_turn = kLora && ((kb & 3) == wave);
-    u32x4 bl[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
-    if (lora_turn && c16 < g.lora_r) {
-      const uint16_t* la = reinterpret_cast<const uint16_t*>(g.lora_a) +
-                           ((int64_t)e * g.lora_r + c16) * K + (int64_t)kb * BK + g4 * 16;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(la + 8 * s);
-        bl[s] = g.lora_bf16 ? bf16x8_to_f16x8(v) : v;
-      }
-    }
-    // prefetch the next step
-    if (kb + 1 < nk) {
-      load_a(kb + 1);
-      load_b(kb + 1);
-    }
-    // MFMAs
-    const char* abuf = s_a + buf * A_BUF;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt < mt_valid && (any_n || lora_turn)) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(
-              abuf + (mt * 16 + c16) * A_STRIDE + g4 * 32 + s * 16);
-          const f16x8 af = as_f16x8(av);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            if (n_ok[nt])
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  af, as_f16x8(bf[nt][s]), acc[mt][nt], 0, 0, 0);
-          }
-          if (lora_turn)
-            acc_u[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                af, as_f16x8(bl[s]), acc_u[mt], 0, 0, 0);
-        }
-      }
-    }
-    if (kb + 1 < nk) store_a(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- LoRA: reduce u over the waves, then G += (scale * u) B_e^T
-  if constexpr (kLora) {
-    float* s_u = reinterpret_cast<float*>(s_a);  // [NWAVES][BM][16]
+    f32x16 acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_u[(wave * BM + mt * 16 + g4 * 4 + i) * 16 + c16] = acc_u[mt][i];
-    __syncthreads();
-    u32x4 bl2[NT];
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      uint16_t v[8];
+        for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
+    f32x4 acc_u[2];
+    acc_u[0] = acc_u[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // every wave is done with the previous tile's stages (and LoRA exchange)
+    lds_barrier();
+    switch (mtv) {
+      case 1: kloop<1, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 2: kloop<2, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 3: kloop<3, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      default: kloop<4, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+    }
+
+    // ---- LoRA: G += (scale * u) B_e^T, u exchanged between the waves in fp16
+    if constexpr (kLora) {
+      // 16x16 accumulator layout: lane holds rank c16 of rows 4*g4 + i
 #pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = 0;
-      const int rho0 = g4 * 8;
-      if (n_ok[nt] && g4 < 2) {
-        int nrow;
-        if constexpr (kSwiglu) {
-          nrow = (nt < 4 ? 0 : I) + n_idx * 256 + wave * 64 + (nt & 3) * 16 + c16;
-        } else {
-          nrow = n_idx * 512 + wave * 128 + nt * 16 + c16;
-        }
+      for (int m16 = 0; m16 < 2; ++m16)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          g_u[(wave * 32 + m16 * 16 + g4 * 4 + i) * kMaxLoraR + c16] =
+              (_Float16)(acc_u[m16][i] * g.lora_scale);
+      lds_barrier();
+      f16x8 bl2[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int l = wave * BNW + nt * 32 + n32;
         const uint16_t* lb = reinterpret_cast<const uint16_t*>(g.lora_b) +
-                             ((int64_t)e * N + nrow) * g.lora_r;
+                             ((int64_t)e * N + weight_row(l, n_idx)) * g.lora_r;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          if (rho0 + t < g.lora_r) {
-            const uint16_t raw = lb[rho0 + t];
-            if (g.lora_bf16) {
-              const _Float16 h = (_Float16)bf16_bits_to_f32(raw);
-              v[t] = __builtin_bit_cast(uint16_t, h);
-            } else {
-              v[t] = raw;
-            }
+        for (int tt = 0; tt < 8; ++tt) {
+          const int rho = g2 * 8 + tt;
+          _Float16 hv = (_Float16)0.f;
+          if (rho < g.lora_r) {
+            const uint16_t raw = lb[rho];
+            hv = g.lora_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
           }
+          bl2[nt][tt] = hv;
         }
       }
-      bl2[nt] = u32x4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-                      (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
-    }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt < mt_valid && any_n) {
-        const int row = mt * 16 + c16;
-        _Float16 u[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int rho = g4 * 8 + t;
-          float sum = 0.f;
-          if (g4 < 2 && rho < g.lora_r) {
-#pragma unroll
-            for (int w = 0; w < NWAVES; ++w) sum += s_u[(w * BM + row) * 16 + rho];
-          }
-          u[t] = (_Float16)(sum * g.lora_scale);
-        }
-        const f16x8 af = {u[0], u[1], u[2], u[3], u[4], u[5], u[6], u[7]};
+      for (int mt = 0; mt < MT; ++mt) {
+        const f16x8 au = *reinterpret_cast<const f16x8*>(&g_u[(mt * 32 + n32) * kMaxLoraR + g2 * 8]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          if (n_ok[nt])
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                af, as_f16x8(bl2[nt]), acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(au, bl2[nt], acc[mt][nt], 0, 0, 0);
       }
     }
-  }
 
-  // ---- epilogue: SwiGLU / row scale / scatter, convert and store
+    // ---- epilogue: SwiGLU / row scale / scatter, convert and store.
+    // 32x32 accumulator layout: lane holds column (lane & 31) and, for
+    // j = 0..15, row 8*(j/4) + 4*(lane/32) + (j%4) of the 32x32 tile.
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt >= mt_valid) continue;
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt >= mtv) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = mt * 16 + g4 * 4 + i;
-      if (row >= rows_valid) continue;
-      const int grow = row0 + row;
-      const int64_t orow = g.scatter ? (int64_t)g.scatter[grow] : (int64_t)grow;
-      const float rs = g.row_scale ? g.row_scale[grow] : 1.0f;
-      if constexpr (kSwiglu) {
+      for (int j = 0; j < 16; ++j) {
+        const int row = mt * 32 + 8 * (j >> 2) + 4 * g2 + (j & 3);
+        if (row >= rows_valid) continue;
+        const int grow = row0 + row;
+        const int64_t orow = g.scatter ? (int64_t)g.scatter[grow] : (int64_t)grow;
+        const float rs = g.row_scale ? g.row_scale[grow] : 1.0f;
+        if constexpr (kSwiglu) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          if (!n_ok[nt]) continue;
-          const int col = n_idx * 256 + wave * 64 + nt * 16 + c16;
-          const float h = silu_f(acc[mt][nt][i]) * acc[mt][nt + 4][i];
-          store_out<kOut>(g.out, orow * I + col, h * rs);
-        }
-      } else {
+          for (int nt = 0; nt < 2; ++nt) {
+            const int col = n_idx * 256 + wave * 64 + nt * 32 + n32;
+            if (col < I) {
+              const float h = silu_f(acc[mt][nt][j]) * acc[mt][nt + 2][j];
+              store_out<kOut>(g.out, orow * I + col, h * rs);
+            }
+          }
+        } else {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (!n_ok[nt]) continue;
-          const int col = n_idx * 512 + wave * 128 + nt * 16 + c16;
-          store_out<kOut>(g.out, orow * N + col, acc[mt][nt][i] * rs);
+          for (int nt = 0; nt < NT; ++nt) {
+            const int col = n_idx * 512 + wave * 128 + nt * 32 + n32;
+            if (col < N) store_out<kOut>(g.out, orow * N + col, acc[mt][nt][j] * rs);
+          }
         }
       }
     }
@@ -437,11 +545,12 @@ static void launch_a(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t stream) {
-  (void)num_cus;
   const int n_tiles = g.swiglu ? (g.N / 2 + 255) / 256 : (g.N + 511) / 512;
-  const int64_t max_mtiles = (g.P + BM - 1) / BM + g.E;
-  int64_t grid = max_mtiles * n_tiles;
-  grid = (grid + 7) / 8 * 8;
+  // persistent: one workgroup per CU (a multiple of 8 for the XCD ordering)
+  int grid = (num_cus + 7) / 8 * 8;
+  const int64_t max_tiles = ((g.P + BM - 1) / BM + g.E) * n_tiles;
+  if ((int64_t)grid > max_tiles) grid = (int)((max_tiles + 7) / 8 * 8);
+  if (grid < 8) grid = 8;
   const dim3 dg((unsigned)grid);
   const bool lora = g.lora_a != nullptr;
   if (g.swiglu) {

@@ -3,7 +3,9 @@
 // At batch 1 the expert projection is a matrix-vector product per routed
 // expert that streams the packed bytes once (experts4bit-qlora 0.22.0 README,
 // "Inference": the single-token decode fast path uses a fused 4-bit GEMV).  HBM
-// bandwidth on the NF4 codes + absmax is the roofline.
+// bandwidth on the NF4 codes + absmax is the roofline, and with only ~21 MB
+// per layer the time is dominated by how early the loads are issued, so both
+// kernels issue every weight load of a wave before doing any arithmetic.
 //
 //   gemv_gate_up_kernel  routes the token (every workgroup recomputes the
 //     top-k of its E logits -- a few hundred cycles -- so no extra launch),
@@ -30,7 +32,8 @@ __constant__ float c_levels_gemv[16] = NF4MOE_LEVELS_INIT;
 
 namespace {
 constexpr int kCopies = 32;
-constexpr int kMaxChunksPerLane = 16;
+constexpr int kMaxItems = 4;          // gate/up items preloaded per wave and round
+constexpr int kMaxChunksPerLane = 16;  // down: chunks of the concatenated K
 
 __device__ __forceinline__ float dot_chunk(const uint32_t* lut, uint32_t lane_off,
                                            u32x4 q, const _Float16* act) {
@@ -68,9 +71,11 @@ __device__ __forceinline__ void store1(void* out, int64_t idx, float v) {
 
 }  // namespace
 
-template <int kRegs>
+// kCpl = ceil(H / 2048) <= 4: 32-weight chunks of one row per lane.
+template <int kRegs, int kCpl>
 __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvArgs g) {
   __shared__ uint32_t s_lut[256 * kCopies];
+  __shared__ uint16_t s_stage[16];
   __shared__ int s_ids[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
   extern __shared__ __attribute__((aligned(16))) _Float16 s_x[];  // [H]
@@ -80,11 +85,6 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = g.H, I = g.I, k = g.k;
 
-  lut_fill<kCopies>(s_lut, c_levels_gemv, tid, 256);
-  for (int i = tid; i < H; i += 256) {
-    const uint16_t raw = reinterpret_cast<const uint16_t*>(g.x)[i];
-    s_x[i] = g.x_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
-  }
   if (wave == 0) {
     int id;
     float w;
@@ -98,42 +98,68 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvArgs g) {
       }
     }
   }
-  __syncthreads();
+  for (int i = tid; i < H; i += 256) {
+    const uint16_t raw = reinterpret_cast<const uint16_t*>(g.x)[i];
+    s_x[i] = g.x_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
+  }
+  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, 256);  // ends with a barrier
 
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
   const int chunks = H / 32;
   const int64_t row_bytes = H / 2;
   const int64_t row_blocks = H / 64;
   const int nw = gridDim.x * 4;
-  for (int q = blockIdx.x * 4 + wave; q < k * I; q += nw) {
-    const int j = q / I;
-    const int i = q - j * I;
-    const int e = s_ids[j];
-    const int64_t rg = (int64_t)e * 2 * I + i;
-    const int64_t ru = rg + I;
-    const uint8_t* pg = g.gu_packed + rg * row_bytes;
-    const uint8_t* pu = g.gu_packed + ru * row_bytes;
-    const float* ag = g.gu_absmax + rg * row_blocks;
-    const float* au = g.gu_absmax + ru * row_blocks;
-    float accg = 0.f, accu = 0.f;
-    for (int c = lane; c < chunks; c += 64) {
-      const u32x4 qg = *reinterpret_cast<const u32x4*>(pg + c * 16);
-      const u32x4 qu = *reinterpret_cast<const u32x4*>(pu + c * 16);
-      const float sg = ag[c >> 1];
-      const float su = au[c >> 1];
-      const _Float16* xs = s_x + c * 32;
-      accg = fmaf(dot_chunk(s_lut, lane_off, qg, xs), sg, accg);
-      accu = fmaf(dot_chunk(s_lut, lane_off, qu, xs), su, accu);
+  const int items = k * I;
+  for (int q0 = blockIdx.x * 4 + wave; q0 < items; q0 += nw * kMaxItems) {
+    // issue every load of this round first
+    u32x4 qg[kMaxItems][kCpl], qu[kMaxItems][kCpl];
+    float sg[kMaxItems][kCpl], su[kMaxItems][kCpl];
+#pragma unroll
+    for (int it = 0; it < kMaxItems; ++it) {
+      const int q = q0 + it * nw;
+      const int qq = q < items ? q : q0;  // clamp: re-read a valid item
+      const int j = qq / I;
+      const int i = qq - j * I;
+      const int e = s_ids[j];
+      const int64_t rg = (int64_t)e * 2 * I + i;
+      const int64_t ru = rg + I;
+#pragma unroll
+      for (int m = 0; m < kCpl; ++m) {
+        int c = lane + 64 * m;
+        if (c >= chunks) c = chunks - 1;
+        qg[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + rg * row_bytes + c * 16);
+        qu[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + ru * row_bytes + c * 16);
+        sg[it][m] = g.gu_absmax[rg * row_blocks + (c >> 1)];
+        su[it][m] = g.gu_absmax[ru * row_blocks + (c >> 1)];
+      }
     }
-    accg = wave_sum(accg);
-    accu = wave_sum(accu);
-    if (lane == 0) g.hbuf[q] = silu_g(accg) * accu * s_w[j];
+#pragma unroll
+    for (int it = 0; it < kMaxItems; ++it) {
+      const int q = q0 + it * nw;
+      float accg = 0.f, accu = 0.f;
+#pragma unroll
+      for (int m = 0; m < kCpl; ++m) {
+        const int c = lane + 64 * m;
+        if (c < chunks) {
+          const _Float16* xs = s_x + c * 32;
+          accg = fmaf(dot_chunk(s_lut, lane_off, qg[it][m], xs), sg[it][m], accg);
+          accu = fmaf(dot_chunk(s_lut, lane_off, qu[it][m], xs), su[it][m], accu);
+        }
+      }
+      accg = wave_sum(accg);
+      accu = wave_sum(accu);
+      if (lane == 0 && q < items) {
+        const int j = q / I;
+        g.hbuf[q] = silu_g(accg) * accu * s_w[j];
+      }
+    }
   }
 }
 
 template <int kOut>
 __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
   __shared__ uint32_t s_lut[256 * kCopies];
+  __shared__ uint16_t s_stage[16];
   extern __shared__ __attribute__((aligned(16))) _Float16 s_h[];  // [k, I]
 
   const int tid = threadIdx.x;
@@ -141,10 +167,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = g.H, I = g.I, k = g.k;
 
-  lut_fill<kCopies>(s_lut, c_levels_gemv, tid, 256);
-  for (int i = tid; i < k * I; i += 256) s_h[i] = (_Float16)g.hbuf[i];
-
-  // this lane's chunks of the concatenated K (fixed for every output row)
+  // this lane's chunks of the concatenated K (the same for every output row)
   const int cps = I / 32;  // chunks per slot
   const int total = k * cps;
   int64_t pk_off[kMaxChunksPerLane];
@@ -167,48 +190,76 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
       nc = m + 1;
     }
   }
-  __syncthreads();
-
-  const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
+  // one output row per wave and round; issue the row's loads before the
+  // table fill so they are in flight meanwhile
   const int nw = gridDim.x * 4;
-  for (int n = blockIdx.x * 4 + wave; n < H; n += nw) {
-    const int64_t prow = (int64_t)n * (I / 2);
-    const int64_t arow = (int64_t)n * (I / 64);
-    float acc = 0.f;
+  int n = blockIdx.x * 4 + wave;
+  u32x4 q[kMaxChunksPerLane];
+  float s[kMaxChunksPerLane];
+  auto load_row = [&](int row) {
+    const int64_t prow = (int64_t)row * (I / 2);
+    const int64_t arow = (int64_t)row * (I / 64);
 #pragma unroll
     for (int m = 0; m < kMaxChunksPerLane; ++m) {
       if (m < nc) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(g.dn_packed + pk_off[m] + prow);
-        const float s = g.dn_absmax[am_off[m] + arow];
-        acc = fmaf(dot_chunk(s_lut, lane_off, q, s_h + h_off[m]), s, acc);
+        q[m] = *reinterpret_cast<const u32x4*>(g.dn_packed + pk_off[m] + prow);
+        s[m] = g.dn_absmax[am_off[m] + arow];
       }
     }
+  };
+  if (n < H) load_row(n);
+
+  for (int i = tid; i < k * I; i += 256) s_h[i] = (_Float16)g.hbuf[i];
+  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, 256);  // ends with a barrier
+
+  const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
+  for (; n < H; n += nw) {
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < kMaxChunksPerLane; ++m) {
+      if (m < nc) acc = fmaf(dot_chunk(s_lut, lane_off, q[m], s_h + h_off[m]), s[m], acc);
+    }
+    if (n + nw < H) load_row(n + nw);
     acc = wave_sum(acc);
     if (lane == 0) store1<kOut>(g.y, n, acc);
   }
 }
 
+template <int kRegs>
+static void launch_gate_up(const GemvArgs& g, int grid, size_t xs, hipStream_t stream) {
+  const int cpl = (g.H + 2047) / 2048;
+  if (cpl <= 1)
+    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 1>), dim3(grid), dim3(256), xs, stream, g);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 2>), dim3(grid), dim3(256), xs, stream, g);
+  else
+    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 4>), dim3(grid), dim3(256), xs, stream, g);
+}
+
 hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream) {
   const int regs = (g.E + 63) / 64;
-  const int grid = num_cus * 2;
   const size_t xs = (size_t)g.H * sizeof(_Float16);
-#define NF4MOE_GU(R)                                                          \
-  hipLaunchKernelGGL(gemv_gate_up_kernel<R>, dim3(grid), dim3(256), xs, stream, g)
-  if (regs <= 1) NF4MOE_GU(1);
-  else if (regs <= 2) NF4MOE_GU(2);
-  else if (regs <= 4) NF4MOE_GU(4);
-  else if (regs <= 8) NF4MOE_GU(8);
-  else NF4MOE_GU(16);
-#undef NF4MOE_GU
+  // gate/up: enough waves that every item is preloaded in one round
+  const int items = g.k * g.I;
+  int grid_gu = (items + 4 * kMaxItems - 1) / (4 * kMaxItems);
+  if (grid_gu > num_cus * 2) grid_gu = num_cus * 2;
+  if (grid_gu < 1) grid_gu = 1;
+  if (regs <= 1) launch_gate_up<1>(g, grid_gu, xs, stream);
+  else if (regs <= 2) launch_gate_up<2>(g, grid_gu, xs, stream);
+  else if (regs <= 4) launch_gate_up<4>(g, grid_gu, xs, stream);
+  else if (regs <= 8) launch_gate_up<8>(g, grid_gu, xs, stream);
+  else launch_gate_up<16>(g, grid_gu, xs, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  int grid_dn = (g.H + 3) / 4;
+  if (grid_dn > num_cus * 2) grid_dn = num_cus * 2;
   const size_t hs = (size_t)g.k * g.I * sizeof(_Float16);
   if (g.y_dtype == kF32)
-    hipLaunchKernelGGL(gemv_down_kernel<kF32>, dim3(grid), dim3(256), hs, stream, g);
+    hipLaunchKernelGGL(gemv_down_kernel<kF32>, dim3(grid_dn), dim3(256), hs, stream, g);
   else if (g.y_dtype == kBF16)
-    hipLaunchKernelGGL(gemv_down_kernel<kBF16>, dim3(grid), dim3(256), hs, stream, g);
+    hipLaunchKernelGGL(gemv_down_kernel<kBF16>, dim3(grid_dn), dim3(256), hs, stream, g);
   else
-    hipLaunchKernelGGL(gemv_down_kernel<kF16>, dim3(grid), dim3(256), hs, stream, g);
+    hipLaunchKernelGGL(gemv_down_kernel<kF16>, dim3(grid_dn), dim3(256), hs, stream, g);
   return hipGetLastError();
 }
 

@@ -46,6 +46,7 @@ hipError_t launch_combine(const _Float16* o, const float* w, int64_t T, int k,
 
 struct GemmArgs {
   const void* a;
+  int64_t a_rows;  // rows of `a` (bounds the activation copies)
   int a_bf16;
   const int32_t* gather;  // nullable
   int gather_div;

@@ -26,8 +26,13 @@
 
 namespace nf4moe {
 
+// One workgroup of 8 waves per chunk of 32 tokens; wave w routes tokens
+// w, w+8, w+16, w+24 of the chunk with all four logit rows loaded up front.
+constexpr int kRouteWaves = 8;
+constexpr int kTokPerWave = kRouteChunk / kRouteWaves;
+
 template <int kRegs>
-__global__ __launch_bounds__(256) void route_chunk_kernel(
+__global__ __launch_bounds__(512) void route_chunk_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int renormalize,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     uint32_t* __restrict__ chunk_masks, const void* __restrict__ x_in,
@@ -39,14 +44,23 @@ __global__ __launch_bounds__(256) void route_chunk_kernel(
   const int64_t chunk = blockIdx.x;
   const int64_t t0 = chunk * kRouteChunk;
   for (int e = tid; e < E; e += blockDim.x) mask[e] = 0u;
-  __syncthreads();
 
-  for (int i = wave; i < kRouteChunk; i += 4) {
+  float v[kTokPerWave][kRegs];
+#pragma unroll
+  for (int u = 0; u < kTokPerWave; ++u) {
+    int64_t t = t0 + wave + kRouteWaves * u;
+    if (t >= T) t = T - 1;  // clamp: routed again, never written
+    route_load<kRegs>(logits + t * E, E, lane, v[u]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kTokPerWave; ++u) {
+    const int i = wave + kRouteWaves * u;
     const int64_t t = t0 + i;
     if (t >= T) break;
     int id;
     float w;
-    route_one_token<kRegs>(logits + t * E, E, k, renormalize, lane, &id, &w);
+    route_select<kRegs>(v[u], E, k, renormalize, lane, &id, &w);
     if (lane < k) {
       topk_ids[t * k + lane] = id;
       topk_w[t * k + lane] = w;
@@ -56,57 +70,105 @@ __global__ __launch_bounds__(256) void route_chunk_kernel(
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) chunk_masks[chunk * E + e] = mask[e];
 
-  // Activation rows of this chunk to fp16 (8 elements per thread and step).
+  // Activation rows of this chunk to fp16, 8 elements per 16-byte access,
+  // four accesses in flight per thread.
   if (x16 != nullptr && x_bf16) {
     const int64_t rows = (T - t0) < kRouteChunk ? (T - t0) : kRouteChunk;
     const int64_t n8 = rows * H / 8;
     const uint16_t* src = reinterpret_cast<const uint16_t*>(x_in) + t0 * H;
     _Float16* dst = x16 + t0 * H;
-    for (int64_t i = tid; i < n8; i += blockDim.x) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + i * 8);
-      u32x4 o;
-      o.x = pack_half2((_Float16)bf16_bits_to_f32(v.x & 0xffffu), (_Float16)bf16_bits_to_f32(v.x >> 16));
-      o.y = pack_half2((_Float16)bf16_bits_to_f32(v.y & 0xffffu), (_Float16)bf16_bits_to_f32(v.y >> 16));
-      o.z = pack_half2((_Float16)bf16_bits_to_f32(v.z & 0xffffu), (_Float16)bf16_bits_to_f32(v.z >> 16));
-      o.w = pack_half2((_Float16)bf16_bits_to_f32(v.w & 0xffffu), (_Float16)bf16_bits_to_f32(v.w >> 16));
-      *reinterpret_cast<u32x4*>(dst + i * 8) = o;
+    for (int64_t i0 = tid; i0 < n8; i0 += 4 * (int64_t)blockDim.x) {
+      u32x4 v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x;
+        if (i < n8) v4[u] = *reinterpret_cast<const u32x4*>(src + i * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x;
+        if (i < n8) {
+          const u32x4 a = v4[u];
+          u32x4 o;
+          o.x = pack_half2((_Float16)bf16_bits_to_f32(a.x & 0xffffu), (_Float16)bf16_bits_to_f32(a.x >> 16));
+          o.y = pack_half2((_Float16)bf16_bits_to_f32(a.y & 0xffffu), (_Float16)bf16_bits_to_f32(a.y >> 16));
+          o.z = pack_half2((_Float16)bf16_bits_to_f32(a.z & 0xffffu), (_Float16)bf16_bits_to_f32(a.z >> 16));
+          o.w = pack_half2((_Float16)bf16_bits_to_f32(a.w & 0xffffu), (_Float16)bf16_bits_to_f32(a.w >> 16));
+          *reinterpret_cast<u32x4*>(dst + i * 8) = o;
+        }
+      }
     }
   }
 }
 
-// Single workgroup of 1024 threads; thread e owns expert e.
+// Single workgroup of 1024 threads.  Thread t owns expert e = t % Ep (Ep =
+// E rounded up to a power of two) and a contiguous group of chunks
+// t / Ep; group partial counts meet in LDS for the expert totals, the
+// exclusive scan over experts gives the offsets, and each thread then writes
+// the running bases of its own chunks.
+constexpr int kScanCache = 16;
+
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     const uint32_t* __restrict__ chunk_masks, int64_t nchunks, int E,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ chunk_base) {
+  __shared__ int32_t s_part[1024];
   __shared__ int32_t s_cnt[kMaxExperts];
-  const int e = threadIdx.x;
-  int32_t total = 0;
+  const int t = threadIdx.x;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  const int groups = 1024 / Ep;
+  const int e = t % Ep;
+  const int grp = t / Ep;
+  const int64_t cpg = (nchunks + groups - 1) / groups;
+  const int64_t c0 = (int64_t)grp * cpg;
+  int64_t c1 = c0 + cpg;
+  if (c1 > nchunks) c1 = nchunks;
+  int32_t cached[kScanCache];
+  int32_t part = 0;
   if (e < E) {
-    int64_t c = 0;
-    int32_t acc[4] = {0, 0, 0, 0};
-    for (; c + 4 <= nchunks; c += 4) {
+    if (cpg <= kScanCache) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += __popc(chunk_masks[(c + u) * E + e]);
+      for (int u = 0; u < kScanCache; ++u) {
+        const int64_t c = c0 + u;
+        cached[u] = (c < c1) ? __popc(chunk_masks[c * E + e]) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kScanCache; ++u) part += cached[u];
+    } else {
+      for (int64_t c = c0; c < c1; ++c) part += __popc(chunk_masks[c * E + e]);
     }
-    for (; c < nchunks; ++c) acc[0] += __popc(chunk_masks[c * E + e]);
-    total = acc[0] + acc[1] + acc[2] + acc[3];
   }
-  s_cnt[e] = (e < E) ? total : 0;
+  s_part[t] = part;
   __syncthreads();
-  // Inclusive Hillis-Steele scan over 1024 entries.
+  int32_t total = 0;
+  if (t < E)
+    for (int gi = 0; gi < groups; ++gi) total += s_part[gi * Ep + t];
+  s_cnt[t] = (t < E) ? total : 0;
+  __syncthreads();
   for (int off = 1; off < kMaxExperts; off <<= 1) {
-    const int32_t a = (e >= off) ? s_cnt[e - off] : 0;
+    const int32_t a = (t >= off) ? s_cnt[t - off] : 0;
     __syncthreads();
-    s_cnt[e] += a;
+    s_cnt[t] += a;
     __syncthreads();
   }
-  if (e < E) {
-    const int32_t excl = s_cnt[e] - total;
-    expert_offsets[e] = excl;
-    if (e == E - 1) expert_offsets[E] = s_cnt[e];
-    if (chunk_base != nullptr) {
-      int32_t run = excl;
-      for (int64_t c = 0; c < nchunks; ++c) {
+  if (t < E) {
+    expert_offsets[t] = s_cnt[t] - total;
+    if (t == E - 1) expert_offsets[E] = s_cnt[t];
+  }
+  if (e < E && chunk_base != nullptr) {
+    int32_t run = (e == 0) ? 0 : s_cnt[e - 1];  // exclusive offset of expert e
+    for (int gi = 0; gi < grp; ++gi) run += s_part[gi * Ep + e];
+    if (cpg <= kScanCache) {
+#pragma unroll
+      for (int u = 0; u < kScanCache; ++u) {
+        const int64_t c = c0 + u;
+        if (c < c1) {
+          chunk_base[c * E + e] = run;
+          run += cached[u];
+        }
+      }
+    } else {
+      for (int64_t c = c0; c < c1; ++c) {
         chunk_base[c * E + e] = run;
         run += __popc(chunk_masks[c * E + e]);
       }
@@ -184,7 +246,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int64_t nchunks = (a.T + kRouteChunk - 1) / kRouteChunk;
   const int regs = (a.E + 63) / 64;
-  const dim3 grid((unsigned)nchunks), block(256);
+  const dim3 grid((unsigned)nchunks), block(64 * kRouteWaves);
 #define NF4MOE_ROUTE_CASE(R)                                                  \
   case R:                                                                     \
     hipLaunchKernelGGL(route_chunk_kernel<R>, grid, block, 0, stream,         \
@@ -220,7 +282,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
                      a.chunk_masks, nchunks, a.E, a.expert_offsets, a.chunk_base);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, grid, block, 0, stream, a.topk_ids,
+  hipLaunchKernelGGL(route_scatter_kernel, grid, dim3(256), 0, stream, a.topk_ids,
                      a.chunk_masks, a.chunk_base, a.T, a.E, a.k, a.sorted_pair,
                      a.pair_pos);
   return hipGetLastError();

@@ -16,18 +16,23 @@ __device__ __forceinline__ bool better(float bv, int bid, float av, int aid) {
 }  // namespace route_detail
 
 // One wave routes one token at a time.  Logit e of the token lives in lane
-// e % 64, register e / 64.
+// e % 64, register e / 64 (route_load); route_select then picks the top k.
 template <int kRegs>
-__device__ __forceinline__ void route_one_token(
-    const float* __restrict__ lg_row, int E, int k, int renormalize,
-    int lane, int* out_id, float* out_w) {
-  float v[kRegs];
-  uint32_t taken = 0u;
+__device__ __forceinline__ void route_load(const float* __restrict__ lg_row, int E,
+                                           int lane, float v[kRegs]) {
 #pragma unroll
   for (int r = 0; r < kRegs; ++r) {
     const int e = lane + 64 * r;
     v[r] = (e < E) ? lg_row[e] : -__builtin_inff();
   }
+}
+
+// Lane j < k receives slot j: the expert id and its routing weight.
+template <int kRegs>
+__device__ __forceinline__ void route_select(const float v[kRegs], int E, int k,
+                                             int renormalize, int lane, int* out_id,
+                                             float* out_w) {
+  uint32_t taken = 0u;
   float my_v = 0.f;
   int my_id = 0;
   float top = 0.f;
@@ -60,7 +65,7 @@ __device__ __forceinline__ void route_one_token(
     if (j == 0) top = bv;
   }
   float s;
-  float ej = (lane < k) ? expf(my_v - top) : 0.f;
+  const float ej = (lane < k) ? expf(my_v - top) : 0.f;
   if (renormalize) {
     s = wave_sum(ej);
   } else {
@@ -74,6 +79,15 @@ __device__ __forceinline__ void route_one_token(
   }
   *out_id = my_id;
   *out_w = ej / s;
+}
+
+template <int kRegs>
+__device__ __forceinline__ void route_one_token(const float* __restrict__ lg_row, int E,
+                                                int k, int renormalize, int lane,
+                                                int* out_id, float* out_w) {
+  float v[kRegs];
+  route_load<kRegs>(lg_row, E, lane, v);
+  route_select<kRegs>(v, E, k, renormalize, lane, out_id, out_w);
 }
 
 }  // namespace nf4moe
