@@ -359,8 +359,8 @@ int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
   int st = check_lora(lora, "lora");
   if (st != NF4MOE_OK) return st;
   if (!aligned(a, 16) || !aligned(packed, 16) || !aligned(absmax, 4) ||
-      !aligned(out, out_dtype == NF4MOE_F32 ? 4 : 2))
-    return fail(NF4MOE_EINVAL, "misaligned buffer (a and packed need 16 bytes)");
+      !aligned(out, 16))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (a, packed and out need 16 bytes)");
   if (P == 0) return ok();
   st = gemm_common(a, a_dtype, a_rows, gather, gather_div, packed, absmax, expert_offsets,
                    E, P, N, K, lora, epilogue, row_scale, scatter, out, out_dtype,

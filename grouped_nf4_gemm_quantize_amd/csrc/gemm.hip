@@ -81,6 +81,8 @@ __shared__ __attribute__((aligned(16))) _Float16 g_u[BM * kMaxLoraR];
 __shared__ int32_t g_tiles[kMaxExperts + 1];
 __shared__ uint16_t g_lstage[16];
 __shared__ int32_t g_wsum[NWAVES];
+__shared__ int32_t g_orow[2][BM];    // output row of each tile row (by tile parity)
+__shared__ float g_rscale[2][BM];    // row scale of each tile row
 
 namespace {
 
@@ -134,6 +136,17 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(v);
   } else {
     reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
+  }
+}
+
+template <int kOut>
+__device__ __forceinline__ void stage_out(char* p, float v) {
+  if constexpr (kOut == kF32) {
+    *reinterpret_cast<float*>(p) = v;
+  } else if constexpr (kOut == kBF16) {
+    *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
+  } else {
+    *reinterpret_cast<_Float16*>(p) = (_Float16)v;
   }
 }
 
@@ -208,80 +221,170 @@ struct Rd {
   uint32_t lane_off;
 };
 
-// One k-step on the stage at LDS byte offset `st`.  MTV = m-tiles (of 32
-// rows) holding valid rows.
-template <int MTV, bool kLora, bool kABf16>
-__device__ __forceinline__ void compute_step(const char* st, const Rd& rd, int lora_r,
-                                             int lora_bf16, int lane,
-                                             f32x16 (&acc)[MT][NT], f32x4 (&acc_u)[2]) {
-  // this wave's packed weights and absmax for the step
+// Registers of one step that come from the stage: this wave's packed
+// weights (4 n-tiles x 16 B) and their absmax as an fp16 pair.
+struct StepRegs {
   u32x4 bq[NT];
   f16x2 sc[NT];
+};
+
+__device__ __forceinline__ void load_step_regs(const char* st, const Rd& rd, StepRegs& r) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    bq[nt] = *reinterpret_cast<const u32x4*>(st + OFF_B + rd.b + nt * 1024);
+    r.bq[nt] = *reinterpret_cast<const u32x4*>(st + OFF_B + rd.b + nt * 1024);
     const _Float16 sh = (_Float16)*reinterpret_cast<const float*>(st + OFF_S + rd.s + nt * 128);
-    sc[nt] = f16x2{sh, sh};
-  }
-
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f16x8 af[MT];
-#pragma unroll
-    for (int mt = 0; mt < MTV; ++mt) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.a[s] + mt * 4096);
-      if constexpr (kABf16) v = bf16x8_to_f16x8(v);
-      af[mt] = as_f16x8(v);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t q = s == 0 ? bq[nt].x : (s == 1 ? bq[nt].y : (s == 2 ? bq[nt].z : bq[nt].w));
-      const f16x8 bf = decode_scaled(q, rd.lane_off, sc[nt]);
-#pragma unroll
-      for (int mt = 0; mt < MTV; ++mt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf, acc[mt][nt], 0, 0, 0);
-    }
-  }
-
-  if constexpr (kLora) {
-    // u[32 rows of this wave][16 ranks] += X . A_e^T over this step's 64 k
-    const bool live = (lane & 15) < lora_r;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 l = *reinterpret_cast<const u32x4*>(st + OFF_L + rd.ul + s2 * 64);
-      if (lora_bf16) l = bf16x8_to_f16x8(l);
-      if (!live) l = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int m16 = 0; m16 < 2; ++m16) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.ua[m16 * 2 + s2]);
-        if constexpr (kABf16) v = bf16x8_to_f16x8(v);
-        acc_u[m16] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l),
-                                                            acc_u[m16], 0, 0, 0);
-      }
-    }
+    r.sc[nt] = f16x2{sh, sh};
   }
 }
 
-// The k-loop of one tile: copies run two steps ahead through the ring.
+template <int MTV, bool kABf16>
+__device__ __forceinline__ void load_a(const char* st, const Rd& rd, int s, f16x8 (&af)[MT]) {
+#pragma unroll
+  for (int mt = 0; mt < MTV; ++mt) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.a[s] + mt * 4096);
+    if constexpr (kABf16) v = bf16x8_to_f16x8(v);
+    af[mt] = as_f16x8(v);
+  }
+}
+
+__device__ __forceinline__ uint32_t q_of(const u32x4& v, int s) {
+  return s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
+}
+
+// Table lookups of substep s for all n-tiles (raw half2 pairs, unscaled).
+__device__ __forceinline__ void lut_lookups(const StepRegs& r, int s, uint32_t lane_off,
+                                            uint32_t (&d)[NT][4]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint32_t q = q_of(r.bq[nt], s);
+    d[nt][0] = lut_read(lut_addr<kCopies, 0>(q, lane_off));
+    d[nt][1] = lut_read(lut_addr<kCopies, 1>(q, lane_off));
+    d[nt][2] = lut_read(lut_addr<kCopies, 2>(q, lane_off));
+    d[nt][3] = lut_read(lut_addr<kCopies, 3>(q, lane_off));
+  }
+}
+
+__device__ __forceinline__ void scale_b(const StepRegs& r, const uint32_t (&d)[NT][4],
+                                        f16x8 (&bf)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const u32x4 v = {half2_as_u32(u32_as_half2(d[nt][0]) * r.sc[nt]),
+                     half2_as_u32(u32_as_half2(d[nt][1]) * r.sc[nt]),
+                     half2_as_u32(u32_as_half2(d[nt][2]) * r.sc[nt]),
+                     half2_as_u32(u32_as_half2(d[nt][3]) * r.sc[nt])};
+    bf[nt] = as_f16x8(v);
+  }
+}
+
+// Interleave of one substep's M MFMAs with the other instructions of its
+// region: the scaling of the first n-tile's operand first, then per MFMA a
+// few LDS reads and VALU operations, so the matrix pipe stays fed while the
+// next substep's operands are read.
+template <int M>
+__device__ __forceinline__ void interleave() {
+  constexpr int kDs = M >= 16 ? 2 : (M >= 8 ? 3 : 6);
+  constexpr int kValu = M >= 16 ? 4 : (M >= 8 ? 7 : 14);
+  __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // VALU: first operand
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);    // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+  }
+}
+
+// Substep S of a step: its MFMAs, with A fragments `af` and the raw table
+// words `d` of its weights already in registers (scaled here, one n-tile
+// ahead of use), while the A fragments and table words of the next substep
+// are read -- for S = 3 those of substep 0 of the next step, from the next
+// stage `nst` (valid once the barrier before substep 3 has passed).
+template <int S, int MTV, bool kLora, bool kABf16>
+__device__ __forceinline__ void substep(const char* st, const char* nst, const Rd& rd,
+                                        const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
+                                        uint32_t (&d)[NT][4], int lora_live, int lora_bf16,
+                                        f32x16 (&acc)[MT][NT], f32x4 (&acc_u)[2]) {
+  f16x8 af_n[MT];
+  uint32_t dn[NT][4];
+  if constexpr (S < 3) {
+    load_a<MTV, kABf16>(st, rd, S + 1, af_n);
+    lut_lookups(cur, S + 1, rd.lane_off, dn);
+  } else {
+    load_step_regs(nst, rd, nxt);
+    load_a<MTV, kABf16>(nst, rd, 0, af_n);
+    lut_lookups(nxt, 0, rd.lane_off, dn);
+  }
+  // LoRA: u[this wave's 32 rows][16 ranks] += X A_e^T, k half S - 1
+  if constexpr (kLora && (S == 1 || S == 2)) {
+    constexpr int s2 = S - 1;
+    u32x4 l = *reinterpret_cast<const u32x4*>(st + OFF_L + rd.ul + s2 * 64);
+    if (lora_bf16) l = bf16x8_to_f16x8(l);
+    if (!lora_live) l = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int m16 = 0; m16 < 2; ++m16) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.ua[m16 * 2 + s2]);
+      if constexpr (kABf16) v = bf16x8_to_f16x8(v);
+      acc_u[m16] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_u[m16],
+                                                          0, 0, 0);
+    }
+  }
+  f16x8 bf[NT];
+  scale_b(cur, d, bf);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MTV; ++mt)
+      acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+#pragma unroll
+  for (int mt = 0; mt < MTV; ++mt) af[mt] = af_n[mt];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[nt][j] = dn[nt][j];
+  interleave<MTV * NT>();
+  // keep the next substep's MFMAs (same accumulators) out of this region
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The k-loop of one tile.  Copies run up to three steps ahead through the
+// ring: the copy of step kb + 3 goes into step kb's stage as soon as every
+// wave has read it (the barrier before substep 3).  Past the last step the
+// copy of the last step is repeated, so every step issues the same number of
+// copies and one wait count holds throughout.
 template <int MTV, bool kLora, bool kABf16>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
                                       int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
                                       f32x4 (&acc_u)[2]) {
   constexpr int ND = dma_per_step<kLora>();
   const uint32_t ring = lds_addr(g_ring);
+  const int last = nk - 1;
   issue_step<kLora>(src, 0, ring, wave);
-  if (nk > 1) issue_step<kLora>(src, 1, ring + STAGE, wave);
-  int cur = 0;  // stage of step kb
+  issue_step<kLora>(src, min(1, last), ring + STAGE, wave);
+  issue_step<kLora>(src, min(2, last), ring + 2 * STAGE, wave);
+  const int lora_live = (lane & 15) < lora_r;
+
+  // stage 0 complete: at most the copies of steps 1 and 2 pending
+  wait_vm_barrier<2 * ND>();
+  StepRegs cur, nxt;
+  f16x8 af[MT];
+  uint32_t d[NT][4];
+  load_step_regs(g_ring, rd, cur);
+  load_a<MTV, kABf16>(g_ring, rd, 0, af);
+  lut_lookups(cur, 0, rd.lane_off, d);
+  int st = 0;  // stage of step kb
   for (int kb = 0; kb < nk; ++kb) {
-    // stage kb is complete once only step kb+1's copies may still be pending
-    if (kb + 1 < nk) wait_vm_barrier<ND>(); else wait_vm_barrier<0>();
-    if (kb + 2 < nk) {
-      const int nxt = cur == 0 ? 2 : cur - 1;  // (cur + 2) mod 3
-      issue_step<kLora>(src, kb + 2, ring + nxt * STAGE, wave);
-    }
-    compute_step<MTV, kLora, kABf16>(g_ring + cur * STAGE, rd, lora_r, lora_bf16, lane, acc,
-                                     acc_u);
-    cur = cur == 2 ? 0 : cur + 1;
+    const int sn = st == 2 ? 0 : st + 1;
+    const char* sp = g_ring + st * STAGE;
+    const char* np = g_ring + sn * STAGE;
+    substep<0, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<1, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<2, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    // stage kb + 1 complete (at most step kb + 2's copies pending), and every
+    // wave is done reading stage kb: refill it with step kb + 3
+    wait_vm_barrier<ND>();
+    issue_step<kLora>(src, min(kb + 3, last), ring + st * STAGE, wave);
+    substep<3, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    cur = nxt;
+    st = sn;
   }
 }
 
@@ -431,6 +534,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       src.l_off[0] = src.l_off[1] = 0;
     }
 
+    // output row and row scale of every tile row, for the epilogue
+    const int par = r & 1;
+    if (tid < BM) {
+      const int grow = row0 + (tid < rows_valid ? tid : 0);
+      g_orow[par][tid] = g.scatter ? g.scatter[grow] : grow;
+      g_rscale[par][tid] = g.row_scale ? g.row_scale[grow] : 1.0f;
+    }
+
     f32x16 acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -449,6 +560,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       case 3: kloop<3, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
       default: kloop<4, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
     }
+    // every copy has landed and every wave is done with the ring: the
+    // epilogue stages its output there
+    wait_vm_barrier<0>();
 
     // ---- LoRA: G += (scale * u) B_e^T, u exchanged between the waves in fp16
     if constexpr (kLora) {
@@ -486,38 +600,60 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       }
     }
 
-    // ---- epilogue: SwiGLU / row scale / scatter, convert and store.
+    // ---- epilogue: SwiGLU, row scale, conversion to the output dtype, then
+    // coalesced stores.  Each wave stages its 32-row slices of the tile in a
+    // private LDS region (rows of COLS values, padded by 16 bytes so the two
+    // lane halves write different banks) and stores them as 16-byte row
+    // chunks, scattered to their output rows.
     // 32x32 accumulator layout: lane holds column (lane & 31) and, for
     // j = 0..15, row 8*(j/4) + 4*(lane/32) + (j%4) of the 32x32 tile.
+    {
+      constexpr int ESZ = kOut == kF32 ? 4 : 2;
+      constexpr int COLS = kSwiglu ? 64 : BNW;      // output columns of this wave
+      constexpr int PITCH = COLS * ESZ + 16;
+      constexpr int CPR = COLS * ESZ / 16;          // 16-byte chunks per row
+      constexpr int EPC = 16 / ESZ;                 // elements per chunk
+      static_assert(NWAVES * 32 * PITCH <= kStages * STAGE, "staging fits the ring");
+      char* ws = g_ring + wave * 32 * PITCH;
+      const int ncols = kSwiglu ? I : N;
+      const int cbase = kSwiglu ? n_idx * 256 + wave * 64 : n_idx * BN + wave * BNW;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt >= mtv) continue;
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt >= mtv) continue;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = mt * 32 + 8 * (j >> 2) + 4 * g2 + (j & 3);
-        if (row >= rows_valid) continue;
-        const int grow = row0 + row;
-        const int64_t orow = g.scatter ? (int64_t)g.scatter[grow] : (int64_t)grow;
-        const float rs = g.row_scale ? g.row_scale[grow] : 1.0f;
-        if constexpr (kSwiglu) {
+        for (int j = 0; j < 16; ++j) {
+          const int rr = 8 * (j >> 2) + 4 * g2 + (j & 3);
+          const float rs = g_rscale[par][mt * 32 + rr];
+          char* prow = ws + rr * PITCH;
+          if constexpr (kSwiglu) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int col = n_idx * 256 + wave * 64 + nt * 32 + n32;
-            if (col < I) {
-              const float h = silu_f(acc[mt][nt][j]) * acc[mt][nt + 2][j];
-              store_out<kOut>(g.out, orow * I + col, h * rs);
-            }
+            for (int nt = 0; nt < 2; ++nt)
+              stage_out<kOut>(prow + (nt * 32 + n32) * ESZ,
+                              silu_f(acc[mt][nt][j]) * acc[mt][nt + 2][j] * rs);
+          } else {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              stage_out<kOut>(prow + (nt * 32 + n32) * ESZ, acc[mt][nt][j] * rs);
           }
-        } else {
+        }
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int col = n_idx * 512 + wave * 128 + nt * 32 + n32;
-            if (col < N) store_out<kOut>(g.out, orow * N + col, acc[mt][nt][j] * rs);
+        for (int it = 0; it < CPR / 2; ++it) {
+          const int idx = it * 64 + lane;
+          const int rr = idx / CPR, c = idx % CPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ws + rr * PITCH + c * 16);
+          const int row = mt * 32 + rr;
+          const int col = cbase + c * EPC;
+          if (row < rows_valid && col < ncols) {
+            const int64_t orow = g_orow[par][row];
+            *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(g.out) +
+                                      (orow * ncols + col) * ESZ) = v;
           }
         }
       }
     }
   }
+  // the repeated copies past a tile's last step may still be landing in LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <bool kSwiglu, bool kLora, bool kABf16>

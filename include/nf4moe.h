@@ -179,7 +179,9 @@ typedef struct {
  *   row_scale       nullable fp32 [P], multiplies output row i;
  *   scatter         nullable int32 [P]; output row i is written to row
  *                   scatter[i] of out, else to row i;
- *   out             F32, F16 or BF16 rows of N (or N/2) elements.
+ *   out             F32, F16 or BF16 rows of N (or N/2) elements, 16-byte
+ *                   aligned (rows are written as 16-byte chunks).
+ * Buffers: a and packed 16-byte aligned, absmax 4-byte aligned, else EINVAL.
  * One kernel launch; no workspace (the per-expert tile table is rebuilt from
  * expert_offsets inside the kernel).
  */
