@@ -170,7 +170,7 @@ FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k) {
 bool use_decode_path(int64_t T, int H, int I, int k, const nf4moe_lora* a,
                      const nf4moe_lora* b) {
   return T == 1 && a == nullptr && b == nullptr && H <= 8192 &&
-         (int64_t)k * I <= 32768;
+         (int64_t)k * I <= 16384;
 }
 
 }  // namespace
@@ -454,7 +454,7 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
     g.dn_absmax = dn_absmax;
     g.topk_ids = ids;
     g.topk_w = wts;
-    g.hbuf = (float*)(ws + L.hbuf);
+    g.hbuf = ws + L.hbuf;
     g.y = y;
     g.y_dtype = y_dtype;
     hipError_t err = launch_decode(g, cus, s);

@@ -132,17 +132,56 @@ __device__ __forceinline__ void decode8(const uint32_t* lut, uint32_t lane_off,
   out[3] = lds_read_u32(lut, lut_addr<kLutCopies, 3>(q, lane_off));
 }
 
-// ---- wave reductions (wave64) ----------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// ---- cross-lane reductions (wave64) ---------------------------------------
+// Within a row of 16 lanes the butterfly runs on DPP lane moves (VALU
+// latency): quad_perm [1,0,3,2] and [2,3,0,1] combine lanes i^1 and i^2,
+// row_half_mirror (i <-> 7-i) and row_mirror (i <-> 15-i) then combine the
+// already-uniform quads and half rows.  The four row results are combined
+// through v_readlane into scalars, so every lane ends with the same value
+// and no step goes through LDS (a ds_bpermute costs an LDS round trip).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, kCtrl, 0xf, 0xf, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<kCtrl>(__float_as_int(v)));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over the 16 lanes of each row, in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
   return v;
+}
+
+// Wave-wide sum / max, returned (uniform) to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 }  // namespace nf4moe

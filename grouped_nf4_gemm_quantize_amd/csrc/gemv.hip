@@ -4,14 +4,16 @@
 // expert that streams the packed bytes once (experts4bit-qlora 0.22.0 README,
 // "Inference": the single-token decode fast path uses a fused 4-bit GEMV).  HBM
 // bandwidth on the NF4 codes + absmax is the roofline, and with only ~21 MB
-// per layer the time is dominated by how early the loads are issued, so both
-// kernels issue every weight load of a wave before doing any arithmetic.
+// per layer the time is set by the chain of dependent memory round trips, so
+// each kernel issues its weight loads as early as their addresses are known
+// and overlaps everything else (activation staging, the decode table) with
+// them.
 //
-//   gemv_gate_up_kernel  routes the token (every workgroup recomputes the
-//     top-k of its E logits -- a few hundred cycles -- so no extra launch),
-//     then one wave per (slot j, column i) item computes the gate row i and
-//     the up row I+i of expert ids[j] against x and writes
-//     h[j, i] = w_j * silu(gate) * up  (fp32).
+//   gemv_gate_up_kernel  every wave routes the token itself (a top-k over the
+//     E logits costs a few hundred cycles -- cheaper than a barrier), then
+//     owns up to kMaxItems (slot j, column i) items: the gate row i and the
+//     up row I+i of expert ids[j], dotted with x; it writes
+//     h[j, i] = w_j * silu(gate) * up  (fp16).
 //   gemv_down_kernel  one wave per output row n: the K of the row is the
 //     concatenation of the k routed experts' I inputs, so the combine over
 //     the slots is part of the dot product; y[n] is written directly.
@@ -32,7 +34,9 @@ __constant__ float c_levels_gemv[16] = NF4MOE_LEVELS_INIT;
 
 namespace {
 constexpr int kCopies = 32;
-constexpr int kMaxItems = 4;          // gate/up items preloaded per wave and round
+constexpr int kThreads = 512;          // 8 waves per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxItems = 4;           // gate/up items per wave and round
 constexpr int kMaxChunksPerLane = 16;  // down: chunks of the concatenated K
 
 __device__ __forceinline__ float dot_chunk(const uint32_t* lut, uint32_t lane_off,
@@ -69,15 +73,18 @@ __device__ __forceinline__ void store1(void* out, int64_t idx, float v) {
   }
 }
 
+// 16-bit activation -> fp16 (bf16 rounds to nearest even; fp16 passes through)
+__device__ __forceinline__ _Float16 to_f16(uint16_t raw, bool bf16) {
+  return bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
+}
+
 }  // namespace
 
 // kCpl = ceil(H / 2048) <= 4: 32-weight chunks of one row per lane.
 template <int kRegs, int kCpl>
-__global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvArgs g) {
+__global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
   __shared__ uint32_t s_lut[256 * kCopies];
   __shared__ uint16_t s_stage[16];
-  __shared__ int s_ids[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
   extern __shared__ __attribute__((aligned(16))) _Float16 s_x[];  // [H]
 
   const int tid = threadIdx.x;
@@ -85,79 +92,92 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GemvArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = g.H, I = g.I, k = g.k;
 
-  if (wave == 0) {
-    int id;
-    float w;
-    route_one_token<kRegs>(g.logits, g.E, k, g.renormalize, lane, &id, &w);
-    if (lane < k) {
-      s_ids[lane] = id;
-      s_w[lane] = w;
-      if (blockIdx.x == 0) {
-        g.topk_ids[lane] = id;
-        g.topk_w[lane] = w;
-      }
-    }
+  // activations: issued first, consumed after the weight loads are out
+  constexpr int kXPer = 4;  // x elements per thread and pass
+  uint2 xr[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i0 = (p * kThreads + tid) * kXPer;
+    xr[p] = i0 < H ? *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) + i0)
+                   : make_uint2(0u, 0u);
   }
-  for (int i = tid; i < H; i += 256) {
-    const uint16_t raw = reinterpret_cast<const uint16_t*>(g.x)[i];
-    s_x[i] = g.x_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
-  }
-  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, 256);  // ends with a barrier
 
-  const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
+  // route in every wave: lane j < k holds slot j
+  int id;
+  float w;
+  route_one_token<kRegs>(g.logits, g.E, k, g.renormalize, lane, &id, &w);
+  if (blockIdx.x == 0 && wave == 0 && lane < k) {
+    g.topk_ids[lane] = id;
+    g.topk_w[lane] = w;
+  }
+
+  // this wave's items, every load issued before any arithmetic
   const int chunks = H / 32;
   const int64_t row_bytes = H / 2;
   const int64_t row_blocks = H / 64;
-  const int nw = gridDim.x * 4;
+  const int nw = gridDim.x * kWaves;
   const int items = k * I;
-  for (int q0 = blockIdx.x * 4 + wave; q0 < items; q0 += nw * kMaxItems) {
-    // issue every load of this round first
-    u32x4 qg[kMaxItems][kCpl], qu[kMaxItems][kCpl];
-    float sg[kMaxItems][kCpl], su[kMaxItems][kCpl];
+  const int q0 = blockIdx.x * kWaves + wave;
+  u32x4 qg[kMaxItems][kCpl], qu[kMaxItems][kCpl];
+  float sg[kMaxItems][kCpl], su[kMaxItems][kCpl];
 #pragma unroll
-    for (int it = 0; it < kMaxItems; ++it) {
-      const int q = q0 + it * nw;
-      const int qq = q < items ? q : q0;  // clamp: re-read a valid item
-      const int j = qq / I;
-      const int i = qq - j * I;
-      const int e = s_ids[j];
-      const int64_t rg = (int64_t)e * 2 * I + i;
-      const int64_t ru = rg + I;
+  for (int it = 0; it < kMaxItems; ++it) {
+    const int q = q0 + it * nw;
+    const int qq = q < items ? q : (q0 < items ? q0 : 0);  // clamp: re-read a valid item
+    const int j = qq / I;
+    const int i = qq - j * I;
+    const int e = __builtin_amdgcn_readlane(id, j);  // j is wave-uniform
+    const int64_t rg = (int64_t)e * 2 * I + i;
+    const int64_t ru = rg + I;
 #pragma unroll
-      for (int m = 0; m < kCpl; ++m) {
-        int c = lane + 64 * m;
-        if (c >= chunks) c = chunks - 1;
-        qg[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + rg * row_bytes + c * 16);
-        qu[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + ru * row_bytes + c * 16);
-        sg[it][m] = g.gu_absmax[rg * row_blocks + (c >> 1)];
-        su[it][m] = g.gu_absmax[ru * row_blocks + (c >> 1)];
+    for (int m = 0; m < kCpl; ++m) {
+      int c = lane + 64 * m;
+      if (c >= chunks) c = chunks - 1;
+      qg[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + rg * row_bytes + c * 16);
+      qu[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + ru * row_bytes + c * 16);
+      sg[it][m] = g.gu_absmax[rg * row_blocks + (c >> 1)];
+      su[it][m] = g.gu_absmax[ru * row_blocks + (c >> 1)];
+    }
+  }
+
+  // stage x as fp16 and build the table while the weights are in flight
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i0 = (p * kThreads + tid) * kXPer;
+    if (i0 < H) {
+      s_x[i0 + 0] = to_f16(xr[p].x & 0xffffu, g.x_bf16);
+      s_x[i0 + 1] = to_f16(xr[p].x >> 16, g.x_bf16);
+      s_x[i0 + 2] = to_f16(xr[p].y & 0xffffu, g.x_bf16);
+      s_x[i0 + 3] = to_f16(xr[p].y >> 16, g.x_bf16);
+    }
+  }
+  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, kThreads);  // ends with a barrier
+
+  const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
+  _Float16* hout = reinterpret_cast<_Float16*>(g.hbuf);
+#pragma unroll
+  for (int it = 0; it < kMaxItems; ++it) {
+    const int q = q0 + it * nw;
+    float accg = 0.f, accu = 0.f;
+#pragma unroll
+    for (int m = 0; m < kCpl; ++m) {
+      const int c = lane + 64 * m;
+      if (c < chunks) {
+        const _Float16* xs = s_x + c * 32;
+        accg = fmaf(dot_chunk(s_lut, lane_off, qg[it][m], xs), sg[it][m], accg);
+        accu = fmaf(dot_chunk(s_lut, lane_off, qu[it][m], xs), su[it][m], accu);
       }
     }
-#pragma unroll
-    for (int it = 0; it < kMaxItems; ++it) {
-      const int q = q0 + it * nw;
-      float accg = 0.f, accu = 0.f;
-#pragma unroll
-      for (int m = 0; m < kCpl; ++m) {
-        const int c = lane + 64 * m;
-        if (c < chunks) {
-          const _Float16* xs = s_x + c * 32;
-          accg = fmaf(dot_chunk(s_lut, lane_off, qg[it][m], xs), sg[it][m], accg);
-          accu = fmaf(dot_chunk(s_lut, lane_off, qu[it][m], xs), su[it][m], accu);
-        }
-      }
-      accg = wave_sum(accg);
-      accu = wave_sum(accu);
-      if (lane == 0 && q < items) {
-        const int j = q / I;
-        g.hbuf[q] = silu_g(accg) * accu * s_w[j];
-      }
-    }
+    accg = wave_sum(accg);
+    accu = wave_sum(accu);
+    const int j = q < items ? q / I : 0;
+    const float wj = lane_f(w, j);
+    if (lane == 0 && q < items) hout[q] = (_Float16)(silu_g(accg) * accu * wj);
   }
 }
 
 template <int kOut>
-__global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
+__global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
   __shared__ uint32_t s_lut[256 * kCopies];
   __shared__ uint16_t s_stage[16];
   extern __shared__ __attribute__((aligned(16))) _Float16 s_h[];  // [k, I]
@@ -166,6 +186,9 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = g.H, I = g.I, k = g.k;
+
+  // the routed experts (lane j < k holds slot j's id)
+  const int id = lane < k ? g.topk_ids[lane] : 0;
 
   // this lane's chunks of the concatenated K (the same for every output row)
   const int cps = I / 32;  // chunks per slot
@@ -177,23 +200,23 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
 #pragma unroll
   for (int m = 0; m < kMaxChunksPerLane; ++m) {
     const int cc = lane + 64 * m;
+    const int j = cc < total ? cc / cps : 0;
+    const int e = __shfl(id, j, 64);
     pk_off[m] = 0;
     am_off[m] = 0;
     h_off[m] = 0;
     if (cc < total) {
-      const int j = cc / cps;
       const int c = cc - j * cps;
-      const int e = g.topk_ids[j];
       pk_off[m] = (int64_t)e * H * (I / 2) + c * 16;
       am_off[m] = (int64_t)e * H * (I / 64) + (c >> 1);
       h_off[m] = j * I + c * 32;
       nc = m + 1;
     }
   }
-  // one output row per wave and round; issue the row's loads before the
-  // table fill so they are in flight meanwhile
-  const int nw = gridDim.x * 4;
-  int n = blockIdx.x * 4 + wave;
+  // one output row per wave and round; the first row's loads go out before
+  // h is staged and the table is built
+  const int nw = gridDim.x * kWaves;
+  int n = blockIdx.x * kWaves + wave;
   u32x4 q[kMaxChunksPerLane];
   float s[kMaxChunksPerLane];
   auto load_row = [&](int row) {
@@ -209,8 +232,11 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs g) {
   };
   if (n < H) load_row(n);
 
-  for (int i = tid; i < k * I; i += 256) s_h[i] = (_Float16)g.hbuf[i];
-  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, 256);  // ends with a barrier
+  // h (fp16, k*I values, a multiple of 8) -> LDS
+  const _Float16* hin = reinterpret_cast<const _Float16*>(g.hbuf);
+  for (int i = tid * 8; i < k * I; i += kThreads * 8)
+    *reinterpret_cast<u32x4*>(s_h + i) = *reinterpret_cast<const u32x4*>(hin + i);
+  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, kThreads);  // ends with a barrier
 
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
   for (; n < H; n += nw) {
@@ -229,20 +255,21 @@ template <int kRegs>
 static void launch_gate_up(const GemvArgs& g, int grid, size_t xs, hipStream_t stream) {
   const int cpl = (g.H + 2047) / 2048;
   if (cpl <= 1)
-    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 1>), dim3(grid), dim3(256), xs, stream, g);
+    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 1>), dim3(grid), dim3(kThreads), xs, stream, g);
   else if (cpl <= 2)
-    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 2>), dim3(grid), dim3(256), xs, stream, g);
+    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 2>), dim3(grid), dim3(kThreads), xs, stream, g);
   else
-    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 4>), dim3(grid), dim3(256), xs, stream, g);
+    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 4>), dim3(grid), dim3(kThreads), xs, stream, g);
 }
 
 hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream) {
   const int regs = (g.E + 63) / 64;
   const size_t xs = (size_t)g.H * sizeof(_Float16);
-  // gate/up: enough waves that every item is preloaded in one round
+  // gate/up: enough waves that every item is loaded in one round
   const int items = g.k * g.I;
-  int grid_gu = (items + 4 * kMaxItems - 1) / (4 * kMaxItems);
-  if (grid_gu > num_cus * 2) grid_gu = num_cus * 2;
+  int grid_gu = (items + kWaves * kMaxItems - 1) / (kWaves * kMaxItems);
+  if (grid_gu < num_cus) grid_gu = (items + kWaves - 1) / kWaves < num_cus
+                                       ? (items + kWaves - 1) / kWaves : num_cus;
   if (grid_gu < 1) grid_gu = 1;
   if (regs <= 1) launch_gate_up<1>(g, grid_gu, xs, stream);
   else if (regs <= 2) launch_gate_up<2>(g, grid_gu, xs, stream);
@@ -251,15 +278,15 @@ hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream) {
   else launch_gate_up<16>(g, grid_gu, xs, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int grid_dn = (g.H + 3) / 4;
+  int grid_dn = (g.H + kWaves - 1) / kWaves;
   if (grid_dn > num_cus * 2) grid_dn = num_cus * 2;
   const size_t hs = (size_t)g.k * g.I * sizeof(_Float16);
   if (g.y_dtype == kF32)
-    hipLaunchKernelGGL(gemv_down_kernel<kF32>, dim3(grid_dn), dim3(256), hs, stream, g);
+    hipLaunchKernelGGL(gemv_down_kernel<kF32>, dim3(grid_dn), dim3(kThreads), hs, stream, g);
   else if (g.y_dtype == kBF16)
-    hipLaunchKernelGGL(gemv_down_kernel<kBF16>, dim3(grid_dn), dim3(256), hs, stream, g);
+    hipLaunchKernelGGL(gemv_down_kernel<kBF16>, dim3(grid_dn), dim3(kThreads), hs, stream, g);
   else
-    hipLaunchKernelGGL(gemv_down_kernel<kF16>, dim3(grid_dn), dim3(256), hs, stream, g);
+    hipLaunchKernelGGL(gemv_down_kernel<kF16>, dim3(grid_dn), dim3(kThreads), hs, stream, g);
   return hipGetLastError();
 }
 

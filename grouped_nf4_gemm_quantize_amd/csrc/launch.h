@@ -89,7 +89,7 @@ struct GemvArgs {
   const float* dn_absmax;
   int32_t* topk_ids;  // [k]
   float* topk_w;      // [k]
-  float* hbuf;        // [k, I] fp32, already scaled by the routing weight
+  void* hbuf;         // [k, I] fp16 h, already scaled by the routing weight
   void* y;            // [H]
   int y_dtype;
 };

@@ -57,9 +57,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       bad |= !__builtin_isfinite(x[i]);
       a = fmaxf(a, fabsf(x[i]));
     }
-    // max over the 16 lanes of the block (lanes differ only in bits 0..3)
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    // max over the 16 lanes of the block (one DPP row: lanes differ only in
+    // bits 0..3); max is exact, so the order of the butterfly is immaterial
+    a = row16_max(a);
 
     uint32_t codes[4];
 #pragma unroll

@@ -13,6 +13,39 @@ __device__ __forceinline__ bool better(float bv, int bid, float av, int aid) {
   return bv > av || (bv == av && bid < aid);
 }
 
+template <int kCtrl>
+__device__ __forceinline__ void best_step(float& v, int& id) {
+  const float ov = dpp_f<kCtrl>(v);
+  const int oid = dpp_i<kCtrl>(id);
+  if (better(ov, oid, v, id)) {
+    v = ov;
+    id = oid;
+  }
+}
+
+// Wave-wide best (largest value, ties to the lower id), uniform in every
+// lane: DPP butterfly inside each row of 16 lanes, then the four row
+// winners compared as scalars.
+__device__ __forceinline__ void wave_best(float& v, int& id) {
+  best_step<kDppXor1>(v, id);
+  best_step<kDppXor2>(v, id);
+  best_step<kDppHalfMirror>(v, id);
+  best_step<kDppMirror>(v, id);
+  float bv = lane_f(v, 0);
+  int bid = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = lane_f(v, 16 * r);
+    const int rid = __builtin_amdgcn_readlane(id, 16 * r);
+    if (better(rv, rid, bv, bid)) {
+      bv = rv;
+      bid = rid;
+    }
+  }
+  v = bv;
+  id = bid;
+}
+
 }  // namespace route_detail
 
 // One wave routes one token at a time.  Logit e of the token lives in lane
@@ -47,15 +80,7 @@ __device__ __forceinline__ void route_select(const float v[kRegs], int E, int k,
         bid = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oid = __shfl_xor(bid, off, 64);
-      if (route_detail::better(ov, oid, bv, bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
+    route_detail::wave_best(bv, bid);
     // every lane now holds the winner of round j
     if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
     if (lane == j) {

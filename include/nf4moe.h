@@ -199,9 +199,10 @@ int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
  * experts the router picks for token t: route + permute, gate_up (+LoRA),
  * SwiGLU, down (+LoRA), combine over the slots in ascending slot order
  * (experts summed per token in group-sorted pair order, 0.22.0 README
- * "Which training path?").  T == 1 runs the split-K decode GEMV kernels (the
- * single-token fast path, 0.22.0 README "Inference"); otherwise the grouped
- * MFMA kernels.  Same contract either way.
+ * "Which training path?").  T == 1 without adapters (and H <= 8192,
+ * k*I <= 16384) runs the split-K decode GEMV kernels (the single-token fast
+ * path, 0.22.0 README "Inference"); otherwise the grouped MFMA kernels.  Same
+ * contract either way.
  *   x [T, H]        BF16 or F16 activations;
  *   router_logits   fp32 [T, E];
  *   H, I            multiples of 64; E <= NF4MOE_MAX_EXPERTS; k <= min(E, 32);
