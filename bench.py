@@ -1,7 +1,9 @@
 """Benchmark of the grouped NF4 MoE expert layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload olmoe]
-                    [--no-cpu-baseline] [--no-decode]
+                    [--no-cpu-baseline] [--no-decode] [--copy-calibration]
+    python bench.py --summarize-trace DIR
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR
 
 A step is one full routed-expert layer forward (route + permute, gate_up with
 SwiGLU, down, combine) over the whole batch, inputs resident in HBM.  The
@@ -18,11 +20,21 @@ I=1024, top-8, T=4096 tokens); the value is its algorithmic TFLOP/s
   cpu_baseline  the CPU oracle timed on this host on the same layer shape.
 
 Prints exactly one JSON line.
+
+--copy-calibration first copies a 512 MiB buffer three times (a plain copy
+of known size: its FETCH_SIZE / WRITE_SIZE counters scale the GEMM's).  The
+two --summarize modes turn rocprofv3 output (a --kernel-trace --stats run, or
+a FETCH_SIZE and a WRITE_SIZE --pmc run of this script with
+--copy-calibration) into the markdown summaries kept under profiles/; the
+counter summary carries the HBM bytes per gate_up launch that the roofline
+line reports as `traffic` while the GEMM source is unchanged.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -36,6 +48,9 @@ METRIC = "grouped NF4 MoE layer TFLOP/s (prefill) + packed-weight GB/s (decode M
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 DECODE_LAYERS = 48
+COPY_BYTES = 512 << 20
+COUNTERS_MD = os.path.join(ROOT, "profiles", "gate_up_gemm_olmoe_counters.md")
+GEMM_SRC = os.path.join(ROOT, "grouped_nf4_gemm_quantize_amd", "csrc", "gemm.hip")
 
 
 def log(msg: str) -> None:
@@ -79,20 +94,113 @@ def time_events(fn, iters: int, stream) -> float:
 
 
 def traffic_from_profiles(kernel_src: str):
-    """HBM bytes per launch of the gate_up GEMM from committed counter runs.
+    """HBM bytes per launch of the gate_up GEMM from the committed counter
+    summary (the JSON block of profiles/gate_up_gemm_olmoe_counters.md).
 
     Returns None when no counter summary exists or when the kernel source
     changed since the counters were taken.
     """
-    path = os.path.join(ROOT, "profiles", "gate_up_gemm_olmoe_counters.json")
-    if not os.path.exists(path):
+    if not os.path.exists(COUNTERS_MD):
         return None
-    with open(path) as f:
-        rec = json.load(f)
+    text = open(COUNTERS_MD).read()
+    if "```json" not in text:
+        return None
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _csv_rows(directory: str, suffix: str):
+    paths = glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(directory: str) -> int:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    print("| kernel | calls | avg us | min us | max us | total % |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows[:16]:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.2f} |")
+    return 0
+
+
+def _counter_means(directory: str, counter: str):
+    """Mean counter value per dispatch for the gate_up GEMM and the copy."""
+    gemm, copy = [], []
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        v = float(r["Counter_Value"])
+        if "grouped_gemm_kernel<true" in name:
+            gemm.append(v)
+        elif "copyBuffer" in name:
+            copy.append(v)
+    if not gemm or not copy:
+        raise SystemExit(f"{counter}: gate_up GEMM or copy dispatches missing in {directory}")
+    # the calibration copies are the largest copy dispatches
+    copy.sort()
+    return sum(gemm) / len(gemm), copy[-1], len(gemm)
+
+
+def summarize_counters(fetch_dir: str, write_dir: str) -> int:
+    """Markdown + JSON summary of the FETCH_SIZE and WRITE_SIZE runs."""
+    f_gemm, f_copy, n_f = _counter_means(fetch_dir, "FETCH_SIZE")
+    w_gemm, w_copy, n_w = _counter_means(write_dir, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    f_scale, w_scale = kib / f_copy, kib / w_copy
+    fetch_b = f_gemm * f_scale * 1024.0
+    write_b = w_gemm * w_scale * 1024.0
+    rec = {
+        "kernel": "grouped_gemm_kernel<true,false,false,2> (gate_up + SwiGLU, olmoe prefill)",
+        "kernel_source_sha256": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest(),
+        "fetch_kib_per_launch_raw": round(f_gemm, 1),
+        "write_kib_per_launch_raw": round(w_gemm, 1),
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib_raw": round(f_copy, 1),
+        "copy_write_kib_raw": round(w_copy, 1),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "hbm_fetch_bytes_per_launch": round(fetch_b),
+        "hbm_write_bytes_per_launch": round(write_b),
+        "hbm_bytes_per_launch": round(fetch_b + write_b),
+        "gemm_dispatches": [n_f, n_w],
+    }
+    print("| quantity | FETCH_SIZE | WRITE_SIZE |")
+    print("|---|---:|---:|")
+    print(f"| gate_up GEMM, KiB per launch (raw) | {f_gemm:.0f} | {w_gemm:.0f} |")
+    print(f"| 512 MiB copy, KiB (raw) | {f_copy:.0f} | {w_copy:.0f} |")
+    print(f"| scale = 524288 KiB / copy reading | {f_scale:.4f} | {w_scale:.4f} |")
+    print(f"| gate_up GEMM, HBM MB per launch (scaled) | {fetch_b / 1e6:.1f} | {write_b / 1e6:.1f} |")
+    print()
+    print("```json")
+    print(json.dumps(rec, indent=1))
+    print("```")
+    return 0
+
+
+def copy_calibration(dev) -> None:
+    """Three copies of a 512 MiB buffer: the plain copy of known size."""
+    import torch
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline(cfg, seconds_target: float = 10.0):
@@ -203,7 +311,14 @@ def main() -> int:
                     choices=["olmoe", "qwen3_zipf", "qlora"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -215,6 +330,8 @@ def main() -> int:
 
     binding.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
     cfg = synth.config(args.workload)
     log(f"[bench] workload {cfg}")
     st = gpu_stacks(cfg, dev)
@@ -284,8 +401,7 @@ def main() -> int:
     dn_tf = dn_flops / (dn_ms * 1e-3) / 1e12
     log(f"[bench] gate_up GEMM {gu_ms * 1e3:.1f} us {gu_tf:.1f} TFLOP/s; "
         f"down GEMM {dn_ms * 1e3:.1f} us {dn_tf:.1f} TFLOP/s")
-    traffic = traffic_from_profiles(os.path.join(
-        ROOT, "grouped_nf4_gemm_quantize_amd", "csrc", "gemm.hip"))
+    traffic = traffic_from_profiles(GEMM_SRC)
     del h, o, x16
 
     result = {
