@@ -139,14 +139,18 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   }
 }
 
+// Four consecutive output values -> one 8-byte (16-byte for fp32) LDS write.
 template <int kOut>
-__device__ __forceinline__ void stage_out(char* p, float v) {
+__device__ __forceinline__ void stage_out4(char* p, const float (&v)[4]) {
   if constexpr (kOut == kF32) {
-    *reinterpret_cast<float*>(p) = v;
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
   } else if constexpr (kOut == kBF16) {
-    *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
+    *reinterpret_cast<u32x2*>(p) =
+        u32x2{(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+              (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
   } else {
-    *reinterpret_cast<_Float16*>(p) = (_Float16)v;
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_half2((_Float16)v[0], (_Float16)v[1]),
+                                         pack_half2((_Float16)v[2], (_Float16)v[3])};
   }
 }
 
@@ -333,7 +337,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const R
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MTV; ++mt)
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+      acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nt], af[mt], acc[mt][nt], 0, 0, 0);
 #pragma unroll
   for (int mt = 0; mt < MTV; ++mt) af[mt] = af_n[mt];
 #pragma unroll
@@ -596,17 +600,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
         const f16x8 au = *reinterpret_cast<const f16x8*>(&g_u[(mt * 32 + n32) * kMaxLoraR + g2 * 8]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(au, bl2[nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bl2[nt], au, acc[mt][nt], 0, 0, 0);
       }
     }
 
     // ---- epilogue: SwiGLU, row scale, conversion to the output dtype, then
     // coalesced stores.  Each wave stages its 32-row slices of the tile in a
-    // private LDS region (rows of COLS values, padded by 16 bytes so the two
-    // lane halves write different banks) and stores them as 16-byte row
-    // chunks, scattered to their output rows.
-    // 32x32 accumulator layout: lane holds column (lane & 31) and, for
-    // j = 0..15, row 8*(j/4) + 4*(lane/32) + (j%4) of the 32x32 tile.
+    // private LDS region (rows of COLS values, padded by 16 bytes) and stores
+    // them as 16-byte row chunks, scattered to their output rows.
+    // The MFMAs take the weights as their first operand, so an accumulator
+    // tile is the transposed output block: lane holds output row (lane & 31)
+    // of the m-tile and, for j = 0..15, output column
+    // 8*(j/4) + 4*(lane/32) + (j%4) of the n-tile -- four consecutive columns
+    // per j/4, one 8-byte (16-byte for fp32) LDS write.
     {
       constexpr int ESZ = kOut == kF32 ? 4 : 2;
       constexpr int COLS = kSwiglu ? 64 : BNW;      // output columns of this wave
@@ -620,20 +626,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt >= mtv) continue;
+        const float rs = g_rscale[par][mt * 32 + n32];
+        char* prow = ws + n32 * PITCH;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int rr = 8 * (j >> 2) + 4 * g2 + (j & 3);
-          const float rs = g_rscale[par][mt * 32 + rr];
-          char* prow = ws + rr * PITCH;
-          if constexpr (kSwiglu) {
+        for (int jj = 0; jj < 4; ++jj) {
+          constexpr int NTO = kSwiglu ? 2 : NT;  // output n-tiles of this wave
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-              stage_out<kOut>(prow + (nt * 32 + n32) * ESZ,
-                              silu_f(acc[mt][nt][j]) * acc[mt][nt + 2][j] * rs);
-          } else {
+          for (int nt = 0; nt < NTO; ++nt) {
+            float v[4];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              stage_out<kOut>(prow + (nt * 32 + n32) * ESZ, acc[mt][nt][j] * rs);
+            for (int i = 0; i < 4; ++i) {
+              const int j = 4 * jj + i;
+              if constexpr (kSwiglu)
+                v[i] = silu_f(acc[mt][nt][j]) * acc[mt][nt + 2][j] * rs;
+              else
+                v[i] = acc[mt][nt][j] * rs;
+            }
+            stage_out4<kOut>(prow + (nt * 32 + 8 * jj + 4 * g2) * ESZ, v);
           }
         }
 #pragma unroll

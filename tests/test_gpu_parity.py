@@ -235,6 +235,95 @@ def test_grouped_gemm_leaves_rows_beyond_offsets_untouched(gpu_lib):
     assert torch.all(out[7:] == 7.0)
 
 
+def test_grouped_gemm_single_expert_is_a_dense_matmul(gpu_lib):
+    """E = 1, no gather: one dense GEMM against torch.matmul (library routine)
+    on the oracle-dequantised weights, in fp32 on the GPU."""
+    rng = np.random.default_rng(31)
+    N, K, P = 384, 448, 333
+    packed, absmax, offsets, a = _random_gemm_case(rng, 1, N, K, [P], P)
+    wdq = oracle.dequantize_blockwise(packed, absmax)[0].astype(np.float32)
+    # the kernel's operands are fp16: compare with the matmul of fp16-rounded
+    # weights, which leaves only accumulation-order differences
+    w16 = (oracle.nf4_codebook()[oracle.unpack_codes(packed)].astype(np.float16).astype(np.float32)
+           * np.repeat(absmax.astype(np.float16).astype(np.float32), 64, axis=-1))[0]
+    w16 = w16.astype(np.float16).astype(np.float32)
+    out = gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                               out_dtype=torch.float32)
+    want = torch.matmul(gpu(a).float(), gpu(w16).t())
+    ref = torch.matmul(gpu(a).float(), gpu(wdq).t())
+    assert torch.allclose(out, want, rtol=1e-5, atol=1e-4)
+    m = metrics(host(out), host(ref), "f32")
+    assert m["fro"] < 2e-3
+
+
+def test_grouped_gemm_empty_and_many_experts(gpu_lib):
+    """P = 0 launches nothing; E = 1024 with most experts empty matches the oracle."""
+    rng = np.random.default_rng(5)
+    N, K = 64, 128
+    packed, absmax, offsets, a = _random_gemm_case(rng, 2, N, K, [0, 0], 4)
+    out = torch.full((4, N), 3.0, dtype=torch.float32, device=DEV)
+    gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), 0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    E = 1024
+    counts = np.zeros(E, dtype=np.int64)
+    counts[[0, 3, 500, 1023]] = [1, 129, 40, 7]
+    P = int(counts.sum())
+    w = rng.standard_normal((E, N, K), dtype=np.float32) * np.float32(0.05)
+    packed, absmax = oracle.quantize_blockwise(w)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = rng.standard_normal((P, K)).astype(np.float16)
+    out = gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                               out_dtype=torch.float32)
+    ref = oracle.grouped_gemm(a.astype(np.float64), packed, absmax, offsets)
+    assert_parity(host(out), ref, fro_tol=2e-3, what="E=1024", out_dtype="f32")
+
+
+def test_lora_with_zero_b_is_bitwise_no_lora(gpu_lib):
+    rng = np.random.default_rng(12)
+    E, N, K = 3, 256, 192
+    counts = [70, 0, 150]
+    P = sum(counts)
+    packed, absmax, offsets, a = _random_gemm_case(rng, E, N, K, counts, P)
+    A = gpu(rng.standard_normal((E, 8, K), dtype=np.float32) * 0.05, torch.bfloat16)
+    B0 = torch.zeros((E, N, 8), dtype=torch.bfloat16, device=DEV)
+    for swiglu in (False, True):
+        plain = gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                                     swiglu=swiglu, out_dtype=torch.float32)
+        zero = gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                                    lora=(A, B0, 2.0), swiglu=swiglu, out_dtype=torch.float32)
+        assert torch.equal(plain, zero)
+
+
+def test_forward_token_permutation_equivariance(gpu_lib):
+    """Permuting the tokens permutes the output rows, bit for bit."""
+    cfg = synth.config("tiny", T=96)
+    gp, ga, dp, da = _stacks(cfg)
+    x, lg = synth.activations(cfg), synth.router_logits(cfg)
+    perm = np.random.default_rng(3).permutation(cfg.T)
+    y1 = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gp), gpu(ga),
+                             gpu(dp), gpu(da), y_dtype=torch.float32)
+    y2 = gpu_lib.moe_forward(gpu(x[perm], torch.bfloat16), gpu(lg[perm]), cfg.k, gpu(gp),
+                             gpu(ga), gpu(dp), gpu(da), y_dtype=torch.float32)
+    assert torch.equal(y1[torch.from_numpy(perm).to(DEV)], y2)
+
+
+def test_top1_unit_weight_is_the_expert_mlp(gpu_lib):
+    """k = 1 (softmax over one expert = 1): y is that expert's SwiGLU MLP."""
+    cfg = synth.config("tiny", k=1)
+    gp, ga, dp, da = _stacks(cfg)
+    x, lg = synth.activations(cfg), synth.router_logits(cfg)
+    y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), 1, gpu(gp), gpu(ga), gpu(dp),
+                            gpu(da), y_dtype=torch.float32)
+    ids, w = oracle.route_topk(lg, 1)
+    assert np.all(w == 1.0)
+    gu = oracle.dequantize_blockwise(gp, ga)
+    dn = oracle.dequantize_blockwise(dp, da)
+    ref = np.concatenate([oracle.expert_mlp(x[t:t + 1], gu[ids[t, 0]], dn[ids[t, 0]])[0]
+                          for t in range(cfg.T)])
+    assert_parity(host(y), ref, fro_tol=2e-3, what="top-1", out_dtype="f32")
+
+
 # ------------------------------------------------------------- full forward
 
 def _stacks(cfg, experts=None):
