@@ -19,20 +19,22 @@
 //   that gives the 32 workgroups of one XCD consecutive tiles (tiles sharing
 //   activation rows or weight rows meet in that XCD's L2).
 //
-// Operand staging: activations (fp16), packed weights, absmax (and the LoRA
-// A rows) of a step are copied global -> LDS by buffer loads that write LDS
-// directly (no VGPR staging) into a 3-stage ring, two steps ahead of use.
-// The copies are issued from inline assembly, so the compiler does not track
-// them: the kernel itself waits with a counted s_waitcnt on the vector-memory
-// counter (the stage in use is complete once at most the newer stage's
-// copies are pending) followed by s_barrier, which keeps the newer stage in
-// flight across the barrier.  Every wave issues the same number of copies
-// per step, so one immediate count holds for all of them.
+// Operand staging: activations (fp16), packed weights (and the LoRA A rows)
+// of a step are copied global -> LDS by buffer loads that write LDS directly
+// (no VGPR staging) into a 3-stage ring, up to three steps ahead of use.
+// absmax travels in groups of four steps (16 bytes per weight row, a quarter
+// of the L2 requests of one copy per step) into a double buffer, carried by
+// every fourth copy batch.  The copies are issued from inline assembly, so
+// the compiler does not track them: the kernel itself waits with a counted
+// s_waitcnt on the vector-memory counter (the stage in use is complete once
+// at most the newer batch's copies are pending; every wave issues the same
+// copies, so one immediate per batch kind holds for all of them) followed by
+// s_barrier, which keeps the newer batch in flight across the barrier.
 //   A stage: 128 rows x 128 B; the 16-byte chunk c of row r sits at chunk
 //            c ^ (r & 7) (XOR swizzle: fragment reads are conflict-free).
 //   B stage: 512 rows x 32 B (64 codes of a block); the 16-byte half h of
 //            row l sits at half h ^ ((l >> 2) & 1).
-//   S stage: 512 fp32 absmax.   L stage: 16 LoRA A rows x 128 B.
+//   L stage: 16 LoRA A rows x 128 B.   absmax group: 512 rows x 4 fp32.
 // Buffer resources bound every copy: a source offset outside the tensor
 // reads zeros instead of faulting.
 // Decode: the lane's 8 codes for one MFMA operand (one u32) go through the
@@ -65,9 +67,9 @@ constexpr int BNW = NT * 32;      // 128 weight rows per wave
 constexpr int BN = NWAVES * BNW;  // 512 weight rows per workgroup
 constexpr int kCopies = 32;
 constexpr int OFF_B = BM * BK * 2;             // A: 16384 B
-constexpr int OFF_S = OFF_B + BN * BK / 2;     // B: 16384 B
-constexpr int OFF_L = OFF_S + BN * 4;          // S: 2048 B
-constexpr int STAGE = OFF_L + kMaxLoraR * BK * 2;  // L: 2048 B -> 36864 B
+constexpr int OFF_L = OFF_B + BN * BK / 2;     // B: 16384 B
+constexpr int STAGE = OFF_L + kMaxLoraR * BK * 2;  // L: 2048 B -> 34816 B
+constexpr int kAbsGroup = 4;                   // steps of absmax per copy (16 B per row)
 constexpr int kStages = 3;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -77,7 +79,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __shared__ __attribute__((aligned(16))) char g_ring[kStages * STAGE];
 __shared__ uint32_t g_lut[256 * kCopies];
-__shared__ __attribute__((aligned(16))) _Float16 g_u[BM * kMaxLoraR];
+// absmax of kAbsGroup consecutive steps for the tile's 512 weight rows, two
+// groups in flight: g_sabs[group & 1][row * kAbsGroup + step % kAbsGroup]
+__shared__ __attribute__((aligned(16))) float g_sabs[2][BN * kAbsGroup];
 __shared__ int32_t g_tiles[kMaxExperts + 1];
 __shared__ uint16_t g_lstage[16];
 __shared__ int32_t g_wsum[NWAVES];
@@ -85,6 +89,13 @@ __shared__ int32_t g_orow[2][BM];    // output row of each tile row (by tile par
 __shared__ float g_rscale[2][BM];    // row scale of each tile row
 
 namespace {
+
+// LoRA u of the tile (fp16 [BM][16]) at the end of the ring, which is free
+// once the k-loop has drained; the epilogue staging uses the ring's start.
+constexpr int OFF_U = kStages * STAGE - BM * kMaxLoraR * 2;
+__device__ __forceinline__ _Float16* u_buf() {
+  return reinterpret_cast<_Float16*>(g_ring + OFF_U);
+}
 
 // ---- buffer resources and the direct-to-LDS copies -------------------------
 
@@ -190,28 +201,40 @@ struct Src {
   i32x4 a_rsrc, b_rsrc, s_rsrc, l_rsrc;
   uint32_t a_off[4];  // A: 4 x 16 B per lane (1 KB per wave instruction)
   uint32_t b_off[4];  // B: 4 x 16 B
-  uint32_t s_off[2];  // absmax: 2 x 4 B
+  uint32_t s_off[2];  // absmax: 2 x 16 B (kAbsGroup steps of one row per lane)
   uint32_t l_off[2];  // LoRA A: 2 x 4 B
 };
 
 template <bool kLora>
-constexpr int dma_per_step() { return kLora ? 12 : 10; }
+constexpr int dma_per_step() { return kLora ? 10 : 8; }   // without the absmax group
+constexpr int kDmaAbs = 2;                                 // absmax group copies per wave
 
+// The copies of step `kb` (clamped to the last step) into the stage at LDS
+// address `st`.  Batch `s` (the unclamped step index) also carries the absmax
+// of steps [s, s + kAbsGroup) when s is a multiple of kAbsGroup, into buffer
+// (s / kAbsGroup) & 1: that buffer last served steps s - 8 .. s - 5, whose
+// reads ended before the barrier of step s - 5, and the batch is issued at
+// step s - 3.
 template <bool kLora>
-__device__ __forceinline__ void issue_step(const Src& s, int kb, uint32_t st, int wave) {
+__device__ __forceinline__ void issue_step(const Src& s, int kb, int sidx, int last,
+                                           uint32_t st, int wave) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     dma16(s.a_rsrc, s.a_off[i], (uint32_t)kb * (BK * 2), st + (wave * 4 + i) * 1024);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     dma16(s.b_rsrc, s.b_off[i], (uint32_t)kb * (BK / 2), st + OFF_B + (wave * 4 + i) * 1024);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma4(s.s_rsrc, s.s_off[i], (uint32_t)kb * 4, st + OFF_S + (wave * 2 + i) * 256);
   if constexpr (kLora) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       dma4(s.l_rsrc, s.l_off[i], (uint32_t)kb * (BK * 2), st + OFF_L + (wave * 2 + i) * 256);
+  }
+  if (sidx % kAbsGroup == 0) {
+    const int grp = min(sidx, last) / kAbsGroup;
+    const uint32_t buf = lds_addr(&g_sabs[(sidx / kAbsGroup) & 1][0]);
+#pragma unroll
+    for (int i = 0; i < kDmaAbs; ++i)
+      dma16(s.s_rsrc, s.s_off[i], (uint32_t)grp * (kAbsGroup * 4), buf + (wave * 2 + i) * 1024);
   }
 }
 
@@ -219,7 +242,7 @@ __device__ __forceinline__ void issue_step(const Src& s, int kb, uint32_t st, in
 struct Rd {
   uint32_t a[4];   // A fragment of substep s (m-tile 0; + 4096 per m-tile)
   uint32_t b;      // packed row of n-tile 0 (+ 1024 per n-tile)
-  uint32_t s;      // absmax of n-tile 0 (+ 128 per n-tile)
+  uint32_t s;      // absmax element of n-tile 0's row (+ 32 rows per n-tile)
   uint32_t ua[4];  // LoRA: A fragment (16x16x32) of this wave's rows, [m16 * 2 + k half]
   uint32_t ul;     // LoRA: A_e fragment of this lane (k half 0; + 64 B for half 1)
   uint32_t lane_off;
@@ -232,11 +255,13 @@ struct StepRegs {
   f16x2 sc[NT];
 };
 
-__device__ __forceinline__ void load_step_regs(const char* st, const Rd& rd, StepRegs& r) {
+__device__ __forceinline__ void load_step_regs(const char* st, int step, const Rd& rd,
+                                               StepRegs& r) {
+  const float* sab = &g_sabs[(step / kAbsGroup) & 1][step % kAbsGroup];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     r.bq[nt] = *reinterpret_cast<const u32x4*>(st + OFF_B + rd.b + nt * 1024);
-    const _Float16 sh = (_Float16)*reinterpret_cast<const float*>(st + OFF_S + rd.s + nt * 128);
+    const _Float16 sh = (_Float16)sab[rd.s + nt * 32 * kAbsGroup];
     r.sc[nt] = f16x2{sh, sh};
   }
 }
@@ -303,7 +328,8 @@ __device__ __forceinline__ void interleave() {
 // are read -- for S = 3 those of substep 0 of the next step, from the next
 // stage `nst` (valid once the barrier before substep 3 has passed).
 template <int S, int MTV, bool kLora, bool kABf16>
-__device__ __forceinline__ void substep(const char* st, const char* nst, const Rd& rd,
+__device__ __forceinline__ void substep(const char* st, const char* nst, int next_step,
+                                        const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
                                         uint32_t (&d)[NT][4], int lora_live, int lora_bf16,
                                         f32x16 (&acc)[MT][NT], f32x4 (&acc_u)[2]) {
@@ -313,7 +339,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const R
     load_a<MTV, kABf16>(st, rd, S + 1, af_n);
     lut_lookups(cur, S + 1, rd.lane_off, dn);
   } else {
-    load_step_regs(nst, rd, nxt);
+    load_step_regs(nst, next_step, rd, nxt);
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
     lut_lookups(nxt, 0, rd.lane_off, dn);
   }
@@ -361,17 +387,17 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
   constexpr int ND = dma_per_step<kLora>();
   const uint32_t ring = lds_addr(g_ring);
   const int last = nk - 1;
-  issue_step<kLora>(src, 0, ring, wave);
-  issue_step<kLora>(src, min(1, last), ring + STAGE, wave);
-  issue_step<kLora>(src, min(2, last), ring + 2 * STAGE, wave);
+  issue_step<kLora>(src, 0, 0, last, ring, wave);
+  issue_step<kLora>(src, min(1, last), 1, last, ring + STAGE, wave);
+  issue_step<kLora>(src, min(2, last), 2, last, ring + 2 * STAGE, wave);
   const int lora_live = (lane & 15) < lora_r;
 
-  // stage 0 complete: at most the copies of steps 1 and 2 pending
+  // stage 0 (and absmax group 0) complete: at most batches 1 and 2 pending
   wait_vm_barrier<2 * ND>();
   StepRegs cur, nxt;
   f16x8 af[MT];
   uint32_t d[NT][4];
-  load_step_regs(g_ring, rd, cur);
+  load_step_regs(g_ring, 0, rd, cur);
   load_a<MTV, kABf16>(g_ring, rd, 0, af);
   lut_lookups(cur, 0, rd.lane_off, d);
   int st = 0;  // stage of step kb
@@ -379,14 +405,16 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
     const int sn = st == 2 ? 0 : st + 1;
     const char* sp = g_ring + st * STAGE;
     const char* np = g_ring + sn * STAGE;
-    substep<0, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<1, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<2, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    // stage kb + 1 complete (at most step kb + 2's copies pending), and every
-    // wave is done reading stage kb: refill it with step kb + 3
-    wait_vm_barrier<ND>();
-    issue_step<kLora>(src, min(kb + 3, last), ring + st * STAGE, wave);
-    substep<3, MTV, kLora, kABf16>(sp, np, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<0, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<1, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<2, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    // stage kb + 1 complete (at most batch kb + 2 pending, which carries the
+    // absmax group when kb + 2 is a multiple of kAbsGroup), and every wave is
+    // done reading stage kb: refill it with step kb + 3
+    if ((kb + 2) % kAbsGroup == 0) wait_vm_barrier<ND + kDmaAbs>();
+    else wait_vm_barrier<ND>();
+    issue_step<kLora>(src, min(kb + 3, last), kb + 3, last, ring + st * STAGE, wave);
+    substep<3, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
     cur = nxt;
     st = sn;
   }
@@ -445,7 +473,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
 #pragma unroll
   for (int s = 0; s < 4; ++s) rd.a[s] = n32 * 128 + (((g2 * 4 + s) ^ (n32 & 7)) << 4);
   rd.b = (wave * BNW + n32) * 32 + ((g2 ^ ((n32 >> 2) & 1)) << 4);
-  rd.s = (wave * BNW + n32) * 4;
+  rd.s = (wave * BNW + n32) * kAbsGroup;
   // LoRA operands of 16x16x32: A row m16*16 + c16 of this wave's 32 rows and
   // k chunk 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
 #pragma unroll
@@ -517,8 +545,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       const int half = (c & 1) ^ ((l >> 2) & 1);
       src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + half * 16;
     }
+    // absmax groups: wave instruction i covers rows [64 i, 64 i + 64) of this
+    // wave's quarter, 16 bytes (kAbsGroup steps) per row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kDmaAbs; ++i) {
       const int l = (wave * 2 + i) * 64 + lane;
       src.s_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)nk * 4u;
     }
@@ -575,7 +605,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       for (int m16 = 0; m16 < 2; ++m16)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          g_u[(wave * 32 + m16 * 16 + g4 * 4 + i) * kMaxLoraR + c16] =
+          u_buf()[(wave * 32 + m16 * 16 + g4 * 4 + i) * kMaxLoraR + c16] =
               (_Float16)(acc_u[m16][i] * g.lora_scale);
       lds_barrier();
       f16x8 bl2[NT];
@@ -597,7 +627,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const f16x8 au = *reinterpret_cast<const f16x8*>(&g_u[(mt * 32 + n32) * kMaxLoraR + g2 * 8]);
+        const f16x8 au = *reinterpret_cast<const f16x8*>(&u_buf()[(mt * 32 + n32) * kMaxLoraR + g2 * 8]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bl2[nt], au, acc[mt][nt], 0, 0, 0);
