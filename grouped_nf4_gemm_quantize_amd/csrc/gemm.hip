@@ -31,9 +31,13 @@
 // copies, so one immediate per batch kind holds for all of them) followed by
 // s_barrier, which keeps the newer batch in flight across the barrier.
 //   A stage: 128 rows x 128 B; the 16-byte chunk c of row r sits at chunk
-//            c ^ (r & 7) (XOR swizzle: fragment reads are conflict-free).
+//            c ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes and
+//            serves a 16-byte read per lane in groups of 16 lanes: 16
+//            fragment rows r..r+15 must cover all 64 banks, and two rows
+//            2 apart (same bank half) must differ in the swizzled chunk.
 //   B stage: 512 rows x 32 B (64 codes of a block); the 16-byte half h of
-//            row l sits at half h ^ ((l >> 2) & 1).
+//            row l sits at half h ^ ((l >> 3) & 1) (16 consecutive rows
+//            then cover all 64 banks).
 //   L stage: 16 LoRA A rows x 128 B.   absmax group: 512 rows x 4 fp32.
 // Buffer resources bound every copy: a source offset outside the tensor
 // reads zeros instead of faulting.
@@ -471,8 +475,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
 
   Rd rd;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) rd.a[s] = n32 * 128 + (((g2 * 4 + s) ^ (n32 & 7)) << 4);
-  rd.b = (wave * BNW + n32) * 32 + ((g2 ^ ((n32 >> 2) & 1)) << 4);
+  for (int s = 0; s < 4; ++s) rd.a[s] = n32 * 128 + (((g2 * 4 + s) ^ ((n32 >> 1) & 7)) << 4);
+  rd.b = (wave * BNW + n32) * 32 + ((g2 ^ ((n32 >> 3) & 1)) << 4);
   rd.s = (wave * BNW + n32) * kAbsGroup;
   // LoRA operands of 16x16x32: A row m16*16 + c16 of this wave's 32 rows and
   // k chunk 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int row = wave * 32 + m16 * 16 + c16;
-      rd.ua[m16 * 2 + s2] = row * 128 + (((4 * s2 + g4) ^ (row & 7)) << 4);
+      rd.ua[m16 * 2 + s2] = row * 128 + (((4 * s2 + g4) ^ ((row >> 1) & 7)) << 4);
     }
   rd.ul = c16 * 128 + g4 * 16;
   rd.lane_off = (uint32_t)(lane & 31) * 4u;
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
     for (int i = 0; i < 4; ++i) {
       const int c = (wave * 4 + i) * 64 + lane;
       const int row = c >> 3;
-      const int gchunk = (c & 7) ^ (row & 7);
+      const int gchunk = (c & 7) ^ ((row >> 1) & 7);
       const int rr = row < rows_valid ? row : 0;
       const int idx = row0 + rr;
       const uint32_t a_src = g.gather ? (uint32_t)(g.gather[idx] / g.gather_div) : (uint32_t)idx;
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
     for (int i = 0; i < 4; ++i) {
       const int c = (wave * 4 + i) * 64 + lane;
       const int l = c >> 1;
-      const int half = (c & 1) ^ ((l >> 2) & 1);
+      const int half = (c & 1) ^ ((l >> 3) & 1);
       src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + half * 16;
     }
     // absmax groups: wave instruction i covers rows [64 i, 64 i + 64) of this
