@@ -9,10 +9,12 @@
 //
 // Work decomposition (gfx950, wave64, v_mfma_f32_32x32x16_f16):
 //   A tile = 128 rows of ONE expert (an M-tile) x 512 weight rows (N).
-//   Workgroup = 4 waves; the waves split N only, so wave w owns 128 weight
-//   rows (4 n-tiles of 32) against all 128 rows (4 m-tiles of 32): 256 fp32
-//   accumulators per lane (the accumulation registers), and every weight is
-//   decoded exactly once per tile.
+//   Workgroup = 8 waves, two per SIMD; the waves split N only, so wave w
+//   owns 64 weight rows (2 n-tiles of 32) against all 128 rows (4 m-tiles
+//   of 32): 128 fp32 accumulators per lane, and every weight is decoded
+//   exactly once per tile.  With two waves per SIMD, one wave's MFMAs run
+//   while the other waits on LDS reads, copy issue or the step barrier (one
+//   wave per SIMD leaves the matrix pipe idle through every such stall).
 //   K advances 64 per step (one absmax block) in four MFMA substeps of 16.
 //   Workgroups are persistent (one per CU): the decode table and the
 //   per-expert tile table are built once, then tiles are taken in an order
@@ -64,10 +66,11 @@ namespace {
 
 constexpr int BM = kGemmBM;       // 128 rows per M-tile
 constexpr int BK = 64;            // k per step (one absmax block)
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = NWAVES * 64;
 constexpr int MT = BM / 32;       // 4 m-tiles of 32 rows
-constexpr int NT = 4;             // 4 n-tiles of 32 weight rows per wave
-constexpr int BNW = NT * 32;      // 128 weight rows per wave
+constexpr int NT = 2;             // 2 n-tiles of 32 weight rows per wave
+constexpr int BNW = NT * 32;      // 64 weight rows per wave
 constexpr int BN = NWAVES * BNW;  // 512 weight rows per workgroup
 constexpr int kCopies = 32;
 constexpr int OFF_B = BM * BK * 2;             // A: 16384 B
@@ -203,15 +206,15 @@ __device__ __forceinline__ f16x8 decode_scaled(uint32_t q, uint32_t lane_off, f1
 // offsets (fixed for the tile; the step adds a scalar offset).
 struct Src {
   i32x4 a_rsrc, b_rsrc, s_rsrc, l_rsrc;
-  uint32_t a_off[4];  // A: 4 x 16 B per lane (1 KB per wave instruction)
-  uint32_t b_off[4];  // B: 4 x 16 B
-  uint32_t s_off[2];  // absmax: 2 x 16 B (kAbsGroup steps of one row per lane)
-  uint32_t l_off[2];  // LoRA A: 2 x 4 B
+  uint32_t a_off[2];  // A: 2 x 16 B per lane (1 KB per wave instruction)
+  uint32_t b_off[2];  // B: 2 x 16 B
+  uint32_t s_off;     // absmax: 16 B (kAbsGroup steps of one row per lane)
+  uint32_t l_off;     // LoRA A: 4 B
 };
 
 template <bool kLora>
-constexpr int dma_per_step() { return kLora ? 10 : 8; }   // without the absmax group
-constexpr int kDmaAbs = 2;                                 // absmax group copies per wave
+constexpr int dma_per_step() { return kLora ? 5 : 4; }    // without the absmax group
+constexpr int kDmaAbs = 1;                                 // absmax group copies per wave
 
 // The copies of step `kb` (clamped to the last step) into the stage at LDS
 // address `st`.  Batch `s` (the unclamped step index) also carries the absmax
@@ -223,22 +226,17 @@ template <bool kLora>
 __device__ __forceinline__ void issue_step(const Src& s, int kb, int sidx, int last,
                                            uint32_t st, int wave) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma16(s.a_rsrc, s.a_off[i], (uint32_t)kb * (BK * 2), st + (wave * 4 + i) * 1024);
+  for (int i = 0; i < 2; ++i)
+    dma16(s.a_rsrc, s.a_off[i], (uint32_t)kb * (BK * 2), st + (wave * 2 + i) * 1024);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma16(s.b_rsrc, s.b_off[i], (uint32_t)kb * (BK / 2), st + OFF_B + (wave * 4 + i) * 1024);
-  if constexpr (kLora) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma4(s.l_rsrc, s.l_off[i], (uint32_t)kb * (BK * 2), st + OFF_L + (wave * 2 + i) * 256);
-  }
+  for (int i = 0; i < 2; ++i)
+    dma16(s.b_rsrc, s.b_off[i], (uint32_t)kb * (BK / 2), st + OFF_B + (wave * 2 + i) * 1024);
+  if constexpr (kLora)
+    dma4(s.l_rsrc, s.l_off, (uint32_t)kb * (BK * 2), st + OFF_L + wave * 256);
   if (sidx % kAbsGroup == 0) {
     const int grp = min(sidx, last) / kAbsGroup;
     const uint32_t buf = lds_addr(&g_sabs[(sidx / kAbsGroup) & 1][0]);
-#pragma unroll
-    for (int i = 0; i < kDmaAbs; ++i)
-      dma16(s.s_rsrc, s.s_off[i], (uint32_t)grp * (kAbsGroup * 4), buf + (wave * 2 + i) * 1024);
+    dma16(s.s_rsrc, s.s_off, (uint32_t)grp * (kAbsGroup * 4), buf + wave * 1024);
   }
 }
 
@@ -247,7 +245,7 @@ struct Rd {
   uint32_t a[4];   // A fragment of substep s (m-tile 0; + 4096 per m-tile)
   uint32_t b;      // packed row of n-tile 0 (+ 1024 per n-tile)
   uint32_t s;      // absmax element of n-tile 0's row (+ 32 rows per n-tile)
-  uint32_t ua[4];  // LoRA: A fragment (16x16x32) of this wave's rows, [m16 * 2 + k half]
+  uint32_t ua[2];  // LoRA: A fragment (16x16x32) of this wave's 16 rows, [k half]
   uint32_t ul;     // LoRA: A_e fragment of this lane (k half 0; + 64 B for half 1)
   uint32_t lane_off;
 };
@@ -336,7 +334,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int nex
                                         const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
                                         uint32_t (&d)[NT][4], int lora_live, int lora_bf16,
-                                        f32x16 (&acc)[MT][NT], f32x4 (&acc_u)[2]) {
+                                        f32x16 (&acc)[MT][NT], f32x4& acc_u) {
   f16x8 af_n[MT];
   uint32_t dn[NT][4];
   if constexpr (S < 3) {
@@ -347,19 +345,15 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int nex
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
     lut_lookups(nxt, 0, rd.lane_off, dn);
   }
-  // LoRA: u[this wave's 32 rows][16 ranks] += X A_e^T, k half S - 1
+  // LoRA: u[this wave's 16 rows][16 ranks] += X A_e^T, k half S - 1
   if constexpr (kLora && (S == 1 || S == 2)) {
     constexpr int s2 = S - 1;
     u32x4 l = *reinterpret_cast<const u32x4*>(st + OFF_L + rd.ul + s2 * 64);
     if (lora_bf16) l = bf16x8_to_f16x8(l);
     if (!lora_live) l = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int m16 = 0; m16 < 2; ++m16) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.ua[m16 * 2 + s2]);
-      if constexpr (kABf16) v = bf16x8_to_f16x8(v);
-      acc_u[m16] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_u[m16],
-                                                          0, 0, 0);
-    }
+    u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.ua[s2]);
+    if constexpr (kABf16) v = bf16x8_to_f16x8(v);
+    acc_u = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_u, 0, 0, 0);
   }
   f16x8 bf[NT];
   scale_b(cur, d, bf);
@@ -387,7 +381,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int nex
 template <int MTV, bool kLora, bool kABf16>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
                                       int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
-                                      f32x4 (&acc_u)[2]) {
+                                      f32x4& acc_u) {
   constexpr int ND = dma_per_step<kLora>();
   const uint32_t ring = lds_addr(g_ring);
   const int last = nk - 1;
@@ -427,7 +421,7 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
 }  // namespace
 
 template <bool kSwiglu, bool kLora, bool kABf16, int kOut>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
+__global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -435,15 +429,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
   const int g2 = lane >> 5;   // k half of the operands
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16x32 operand coordinates
 
-  lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm, tid, 256);
+  lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm, tid, NTHREADS);
 
-  // M-tile table from the offsets: thread t owns experts 4t..4t+3
+  // M-tile table from the offsets: thread t owns experts 2t, 2t + 1
   {
-    int32_t cnt[4];
+    constexpr int kPer = kMaxExperts / NTHREADS;
+    int32_t cnt[kPer];
     int32_t local = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ex = tid * 4 + u;
+    for (int u = 0; u < kPer; ++u) {
+      const int ex = tid * kPer + u;
       cnt[u] = 0;
       if (ex < g.E) cnt[u] = (g.offsets[ex + 1] - g.offsets[ex] + BM - 1) / BM;
       local += cnt[u];
@@ -459,12 +454,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
     int32_t run = incl - local;
     for (int w = 0; w < wave; ++w) run += g_wsum[w];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ex = tid * 4 + u;
+    for (int u = 0; u < kPer; ++u) {
+      const int ex = tid * kPer + u;
       if (ex < g.E) g_tiles[ex] = run;
       run += cnt[u];
     }
-    if (tid == 255) g_tiles[g.E] = run;
+    if (tid == NTHREADS - 1) g_tiles[g.E] = run;
   }
   __syncthreads();
 
@@ -478,27 +473,27 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
   for (int s = 0; s < 4; ++s) rd.a[s] = n32 * 128 + (((g2 * 4 + s) ^ ((n32 >> 1) & 7)) << 4);
   rd.b = (wave * BNW + n32) * 32 + ((g2 ^ ((n32 >> 3) & 1)) << 4);
   rd.s = (wave * BNW + n32) * kAbsGroup;
-  // LoRA operands of 16x16x32: A row m16*16 + c16 of this wave's 32 rows and
-  // k chunk 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
+  // LoRA operands of 16x16x32: A row c16 of this wave's 16 rows and k chunk
+  // 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
 #pragma unroll
-  for (int m16 = 0; m16 < 2; ++m16)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int row = wave * 32 + m16 * 16 + c16;
-      rd.ua[m16 * 2 + s2] = row * 128 + (((4 * s2 + g4) ^ ((row >> 1) & 7)) << 4);
-    }
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int row = wave * 16 + c16;
+    rd.ua[s2] = row * 128 + (((4 * s2 + g4) ^ ((row >> 1) & 7)) << 4);
+  }
   rd.ul = c16 * 128 + g4 * 16;
   rd.lane_off = (uint32_t)(lane & 31) * 4u;
 
-  // weight row of LDS B row l (0..511) of N-tile n_idx, clamped to a valid row
+  // weight row of LDS B row l (0..511) of N-tile n_idx, clamped to a valid
+  // row.  SwiGLU: wave w's n-tile 0 holds the gate rows and n-tile 1 the up
+  // rows of output columns n_idx*256 + 32w + [0, 32).
   auto weight_row = [&](int l, int n_idx) -> int {
-    const int w = l >> 7, nt = (l >> 5) & 3, n = l & 31;
+    const int w = l / BNW, nt = (l >> 5) % NT, n = l & 31;
     int row;
     if constexpr (kSwiglu) {
-      const int col = n_idx * 256 + w * 64 + (nt & 1) * 32 + n;
-      row = (col < I ? col : I - 1) + (nt >= 2 ? I : 0);
+      const int col = n_idx * 256 + w * 32 + n;
+      row = (col < I ? col : I - 1) + (nt == 1 ? I : 0);
     } else {
-      const int col = n_idx * 512 + w * 128 + nt * 32 + n;
+      const int col = n_idx * 512 + w * BNW + nt * 32 + n;
       row = col < N ? col : N - 1;
     }
     return row;
@@ -530,10 +525,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
     const uint32_t s_bytes = (uint32_t)N * (uint32_t)nk * 4u;
     src.b_rsrc = make_rsrc(reinterpret_cast<const char*>(g.packed) + (int64_t)e * b_bytes, b_bytes);
     src.s_rsrc = make_rsrc(reinterpret_cast<const char*>(g.absmax) + (int64_t)e * s_bytes, s_bytes);
-    // A: wave instruction i covers LDS chunks [64 i, 64 i + 64) = rows 8i..8i+7
+    // A: wave instruction i covers LDS chunks [64 j, 64 j + 64) = rows
+    // 8j..8j+7, j = 2 wave + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (wave * 4 + i) * 64 + lane;
+    for (int i = 0; i < 2; ++i) {
+      const int c = (wave * 2 + i) * 64 + lane;
       const int row = c >> 3;
       const int gchunk = (c & 7) ^ ((row >> 1) & 7);
       const int rr = row < rows_valid ? row : 0;
@@ -541,35 +537,29 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       const uint32_t a_src = g.gather ? (uint32_t)(g.gather[idx] / g.gather_div) : (uint32_t)idx;
       src.a_off[i] = (a_src * (uint32_t)K + gchunk * 8) * 2;
     }
-    // B: wave instruction i covers LDS rows [32 i, 32 i + 32), two 16-B halves each
+    // B: wave instruction i covers LDS rows [32 j, 32 j + 32), two 16-B
+    // halves each, j = 2 wave + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (wave * 4 + i) * 64 + lane;
+    for (int i = 0; i < 2; ++i) {
+      const int c = (wave * 2 + i) * 64 + lane;
       const int l = c >> 1;
       const int half = (c & 1) ^ ((l >> 3) & 1);
       src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + half * 16;
     }
-    // absmax groups: wave instruction i covers rows [64 i, 64 i + 64) of this
-    // wave's quarter, 16 bytes (kAbsGroup steps) per row
-#pragma unroll
-    for (int i = 0; i < kDmaAbs; ++i) {
-      const int l = (wave * 2 + i) * 64 + lane;
-      src.s_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)nk * 4u;
-    }
+    // absmax groups: the wave's instruction covers rows [64 wave, 64 wave +
+    // 64), 16 bytes (kAbsGroup steps) per row
+    src.s_off = (uint32_t)weight_row(wave * 64 + lane, n_idx) * (uint32_t)nk * 4u;
     if constexpr (kLora) {
       const uint32_t l_bytes = (uint32_t)g.lora_r * (uint32_t)K * 2u;
       src.l_rsrc = make_rsrc(reinterpret_cast<const char*>(g.lora_a) + (int64_t)e * l_bytes, l_bytes);
       // LoRA A: 16 rows x 128 B per step; dword d of the block is row d / 32
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int d = (wave * 2 + i) * 64 + lane;
-        const int rho = d >> 5;
-        const int rc = rho < g.lora_r ? rho : 0;
-        src.l_off[i] = (uint32_t)rc * (uint32_t)K * 2u + (uint32_t)(d & 31) * 4u;
-      }
+      const int d = wave * 64 + lane;
+      const int rho = d >> 5;
+      const int rc = rho < g.lora_r ? rho : 0;
+      src.l_off = (uint32_t)rc * (uint32_t)K * 2u + (uint32_t)(d & 31) * 4u;
     } else {
       src.l_rsrc = i32x4{0, 0, 0, 0};
-      src.l_off[0] = src.l_off[1] = 0;
+      src.l_off = 0;
     }
 
     // output row and row scale of every tile row, for the epilogue
@@ -587,8 +577,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
-    f32x4 acc_u[2];
-    acc_u[0] = acc_u[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc_u = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // every wave is done with the previous tile's stages (and LoRA exchange)
     lds_barrier();
@@ -606,11 +595,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
     if constexpr (kLora) {
       // 16x16 accumulator layout: lane holds rank c16 of rows 4*g4 + i
 #pragma unroll
-      for (int m16 = 0; m16 < 2; ++m16)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          u_buf()[(wave * 32 + m16 * 16 + g4 * 4 + i) * kMaxLoraR + c16] =
-              (_Float16)(acc_u[m16][i] * g.lora_scale);
+      for (int i = 0; i < 4; ++i)
+        u_buf()[(wave * 16 + g4 * 4 + i) * kMaxLoraR + c16] = (_Float16)(acc_u[i] * g.lora_scale);
       lds_barrier();
       f16x8 bl2[NT];
 #pragma unroll
@@ -649,14 +635,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
     // per j/4, one 8-byte (16-byte for fp32) LDS write.
     {
       constexpr int ESZ = kOut == kF32 ? 4 : 2;
-      constexpr int COLS = kSwiglu ? 64 : BNW;      // output columns of this wave
+      constexpr int COLS = kSwiglu ? BNW / 2 : BNW;  // output columns of this wave
       constexpr int PITCH = COLS * ESZ + 16;
       constexpr int CPR = COLS * ESZ / 16;          // 16-byte chunks per row
       constexpr int EPC = 16 / ESZ;                 // elements per chunk
       static_assert(NWAVES * 32 * PITCH <= kStages * STAGE, "staging fits the ring");
       char* ws = g_ring + wave * 32 * PITCH;
       const int ncols = kSwiglu ? I : N;
-      const int cbase = kSwiglu ? n_idx * 256 + wave * 64 : n_idx * BN + wave * BNW;
+      const int cbase = kSwiglu ? n_idx * 256 + wave * (BNW / 2) : n_idx * BN + wave * BNW;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt >= mtv) continue;
@@ -664,7 +650,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
         char* prow = ws + n32 * PITCH;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          constexpr int NTO = kSwiglu ? 2 : NT;  // output n-tiles of this wave
+          constexpr int NTO = kSwiglu ? NT / 2 : NT;  // output n-tiles of this wave
 #pragma unroll
           for (int nt = 0; nt < NTO; ++nt) {
             float v[4];
@@ -672,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs g, int n_
             for (int i = 0; i < 4; ++i) {
               const int j = 4 * jj + i;
               if constexpr (kSwiglu)
-                v[i] = silu_f(acc[mt][nt][j]) * acc[mt][nt + 2][j] * rs;
+                v[i] = silu_f(acc[mt][nt][j]) * acc[mt][nt + NTO][j] * rs;
               else
                 v[i] = acc[mt][nt][j] * rs;
             }
@@ -704,15 +690,15 @@ static void launch_out(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s)
   switch (g.out_dtype) {
     case kF32:
       hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF32>), grid,
-                         dim3(256), 0, s, g, n_tiles);
+                         dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     case kBF16:
       hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kBF16>), grid,
-                         dim3(256), 0, s, g, n_tiles);
+                         dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     default:
       hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF16>), grid,
-                         dim3(256), 0, s, g, n_tiles);
+                         dim3(NTHREADS), 0, s, g, n_tiles);
       break;
   }
 }
