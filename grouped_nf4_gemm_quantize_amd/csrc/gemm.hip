@@ -89,15 +89,7 @@ __shared__ uint32_t g_lut[256 * kCopies];
 // absmax of kAbsGroup consecutive steps for the tile's 512 weight rows, two
 // groups in flight: g_sabs[group & 1][row * kAbsGroup + step % kAbsGroup]
 __shared__ __attribute__((aligned(16))) float g_sabs[2][BN * kAbsGroup];
-// Tile order, longest first: every expert's full M-tiles (g_tiles[e] = full
-// M-tiles of experts < e), then the partial M-tiles (the last, short M-tile
-// of an expert) by their 32-row slices, 4 down to 1: g_part lists their
-// experts.  Taken round-robin by the persistent workgroups, the short tiles
-// come last and even out the workgroups' finishing times.
 __shared__ int32_t g_tiles[kMaxExperts + 1];
-__shared__ uint16_t g_part[kMaxExperts];
-__shared__ uint64_t g_wsum_p[NWAVES];
-__shared__ int32_t g_npart;   // partial M-tiles
 __shared__ uint16_t g_lstage[16];
 __shared__ int32_t g_wsum[NWAVES];
 __shared__ int32_t g_orow[2][BM];    // output row of each tile row (by tile parity)
@@ -359,6 +351,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int nex
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) d[nt][j] = dn[nt][j];
+
 }
 
 // The k-loop of one tile.  Copies run up to three steps ahead through the
@@ -419,76 +412,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
 
   lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm, tid, NTHREADS);
 
-  // M-tile tables from the offsets: thread t owns experts 2t, 2t + 1.  Each
-  // expert counts its full M-tiles, and its partial M-tile (if any) in one
-  // 16-bit field of a packed counter: field 4 - s for s valid 32-row slices.
+  // M-tile table from the offsets: thread t owns experts 2t, 2t + 1
   {
     constexpr int kPer = kMaxExperts / NTHREADS;
-    int32_t full[kPer];
-    uint64_t part[kPer];
+    int32_t cnt[kPer];
     int32_t local = 0;
-    uint64_t local_p = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int ex = tid * kPer + u;
-      full[u] = 0;
-      part[u] = 0;
-      if (ex < g.E) {
-        const int rows = g.offsets[ex + 1] - g.offsets[ex];
-        full[u] = rows / BM;
-        const int slices = (rows % BM + 31) / 32;
-        if (slices > 0) part[u] = 1ull << (16 * (4 - slices));
-      }
-      local += full[u];
-      local_p += part[u];
+      cnt[u] = 0;
+      if (ex < g.E) cnt[u] = (g.offsets[ex + 1] - g.offsets[ex] + BM - 1) / BM;
+      local += cnt[u];
     }
     int32_t incl = local;
-    uint64_t incl_p = local_p;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int32_t v = __shfl_up(incl, off, 64);
-      const uint32_t vlo = __shfl_up((uint32_t)incl_p, off, 64);
-      const uint32_t vhi = __shfl_up((uint32_t)(incl_p >> 32), off, 64);
-      if (lane >= off) {
-        incl += v;
-        incl_p += ((uint64_t)vhi << 32) | vlo;
-      }
+      if (lane >= off) incl += v;
     }
-    if (lane == 63) {
-      g_wsum[wave] = incl;
-      g_wsum_p[wave] = incl_p;
-    }
+    if (lane == 63) g_wsum[wave] = incl;
     __syncthreads();
     int32_t run = incl - local;
-    uint64_t run_p = incl_p - local_p;
-    uint64_t tot_p = 0;
-    for (int w = 0; w < NWAVES; ++w) {
-      if (w < wave) {
-        run += g_wsum[w];
-        run_p += g_wsum_p[w];
-      }
-      tot_p += g_wsum_p[w];
-    }
-    // start of each field's run in g_part: fields 0..3 (4 down to 1 slices)
-    int base[4];
-    base[0] = 0;
-#pragma unroll
-    for (int f = 1; f < 4; ++f) base[f] = base[f - 1] + (int)((tot_p >> (16 * (f - 1))) & 0xffff);
+    for (int w = 0; w < wave; ++w) run += g_wsum[w];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int ex = tid * kPer + u;
-      if (ex < g.E) {
-        g_tiles[ex] = run;
-        if (part[u] != 0) {
-          const int f = (63 - __builtin_clzll(part[u])) / 16;
-          g_part[base[f] + (int)((run_p >> (16 * f)) & 0xffff)] = (uint16_t)ex;
-        }
-      }
-      run += full[u];
-      run_p += part[u];
+      if (ex < g.E) g_tiles[ex] = run;
+      run += cnt[u];
     }
     if (tid == NTHREADS - 1) g_tiles[g.E] = run;
-    if (tid == 0) g_npart = base[3] + (int)((tot_p >> 48) & 0xffff);
   }
   __syncthreads();
 
@@ -529,8 +481,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   };
 
   const i32x4 a_rsrc = make_rsrc(g.a, (uint32_t)(g.a_rows * (int64_t)K * 2));
-  const int n_full = __builtin_amdgcn_readfirstlane(g_tiles[g.E]);
-  const int total = (n_full + __builtin_amdgcn_readfirstlane(g_npart)) * n_tiles;
+  const int total = __builtin_amdgcn_readfirstlane(g_tiles[g.E]) * n_tiles;
   const int G = gridDim.x;  // a multiple of 8
   const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
   for (int r = 0;; ++r) {
@@ -538,20 +489,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     if (tix >= total) break;
     const int mt_global = tix / n_tiles;
     const int n_idx = tix - mt_global * n_tiles;
-    int e, m_local;
-    if (mt_global < n_full) {
-      int lo = 0, hi = g.E;  // g_tiles[lo] <= mt_global < g_tiles[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (g_tiles[mid] <= mt_global) lo = mid; else hi = mid;
-      }
-      e = __builtin_amdgcn_readfirstlane(lo);
-      m_local = mt_global - __builtin_amdgcn_readfirstlane(g_tiles[e]);
-    } else {
-      e = __builtin_amdgcn_readfirstlane((int)g_part[mt_global - n_full]);
-      m_local = (__builtin_amdgcn_readfirstlane(g.offsets[e + 1]) -
-                 __builtin_amdgcn_readfirstlane(g.offsets[e])) / BM;
+    int lo = 0, hi = g.E;  // g_tiles[lo] <= mt_global < g_tiles[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g_tiles[mid] <= mt_global) lo = mid; else hi = mid;
     }
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int m_local = mt_global - __builtin_amdgcn_readfirstlane(g_tiles[e]);
     const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + m_local * BM;
     const int rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
     const int mtv = (rows_valid + 31) >> 5;
