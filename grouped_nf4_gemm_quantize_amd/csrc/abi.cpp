@@ -480,6 +480,7 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
   r.x_bf16 = conv ? 1 : 0;
   r.x16 = conv ? (_Float16*)(ws + L.x16) : nullptr;
   r.H = H;
+  r.num_cus = cus;
   hipError_t err = launch_route(r, s);
   if (err != hipSuccess) return hip_fail(err, "route launch");
 

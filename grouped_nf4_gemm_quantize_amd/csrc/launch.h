@@ -36,6 +36,7 @@ struct RouteArgs {
   int x_bf16;
   _Float16* x16;            // null: no conversion
   int H;
+  int num_cus;              // sizes the conversion's grid
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);

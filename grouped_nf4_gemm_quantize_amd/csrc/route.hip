@@ -16,9 +16,15 @@
 // Kernels (in launch order):
 //   route_chunk_kernel  top-k + softmax weights per token (one wave per
 //                       token), per-chunk expert masks; optionally converts
-//                       the chunk's activation rows to fp16 for the GEMMs;
+//                       the activation rows to fp16 for the GEMMs (spread
+//                       over every workgroup of the launch, which has at
+//                       least two per CU);
 //   route_scan_kernel   per-expert totals -> offsets and per-chunk bases;
 //   route_scatter_kernel  sorted_pair / pair_pos from the masks.
+// When the masks are few (chunks x E <= kFuseMasks), one kernel replaces
+// the last two: route_scan_scatter_kernel, in which every chunk's workgroup
+// recomputes the expert totals and its own bases from all the masks (a few
+// KB of L2 reads each) instead of waiting for a separate scan launch.
 
 #include "common.h"
 #include "launch.h"
@@ -43,6 +49,7 @@ __global__ __launch_bounds__(512) void route_chunk_kernel(
   const int wave = tid >> 6;
   const int64_t chunk = blockIdx.x;
   const int64_t t0 = chunk * kRouteChunk;
+  if (t0 < T) {  // workgroups past the last chunk only convert activations
   for (int e = tid; e < E; e += blockDim.x) mask[e] = 0u;
 
   float v[kTokPerWave][kRegs];
@@ -69,24 +76,33 @@ __global__ __launch_bounds__(512) void route_chunk_kernel(
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) chunk_masks[chunk * E + e] = mask[e];
+  }
 
-  // Activation rows of this chunk to fp16, 8 elements per 16-byte access,
-  // four accesses in flight per thread.
+  // Activation rows to fp16, 8 elements per 16-byte access, four accesses in
+  // flight per thread, grid-strided over the whole [T, H] block -- by the
+  // workgroups past the last chunk alone when there are at least as many of
+  // them as chunks (the routing workgroups then finish with the routing).
   if (x16 != nullptr && x_bf16) {
-    const int64_t rows = (T - t0) < kRouteChunk ? (T - t0) : kRouteChunk;
-    const int64_t n8 = rows * H / 8;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(x_in) + t0 * H;
-    _Float16* dst = x16 + t0 * H;
-    for (int64_t i0 = tid; i0 < n8; i0 += 4 * (int64_t)blockDim.x) {
+    const int64_t nchunks = (T + kRouteChunk - 1) / kRouteChunk;
+    const int64_t extra = (int64_t)gridDim.x - nchunks;
+    const bool split = extra >= nchunks;
+    if (split && chunk < nchunks) return;
+    const int64_t wg = split ? chunk - nchunks : chunk;
+    const int64_t nwg = split ? extra : (int64_t)gridDim.x;
+    const int64_t n8 = T * H / 8;
+    const int64_t stride = nwg * blockDim.x;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(x_in);
+    _Float16* dst = x16;
+    for (int64_t i0 = wg * blockDim.x + tid; i0 < n8; i0 += 4 * stride) {
       u32x4 v4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t i = i0 + u * (int64_t)blockDim.x;
+        const int64_t i = i0 + u * stride;
         if (i < n8) v4[u] = *reinterpret_cast<const u32x4*>(src + i * 8);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t i = i0 + u * (int64_t)blockDim.x;
+        const int64_t i = i0 + u * stride;
         if (i < n8) {
           const u32x4 a = v4[u];
           u32x4 o;
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     for (int gi = 0; gi < groups; ++gi) total += s_part[gi * Ep + t];
   s_cnt[t] = (t < E) ? total : 0;
   __syncthreads();
-  for (int off = 1; off < kMaxExperts; off <<= 1) {
+  for (int off = 1; off < Ep; off <<= 1) {
     const int32_t a = (t >= off) ? s_cnt[t - off] : 0;
     __syncthreads();
     s_cnt[t] += a;
@@ -190,6 +206,95 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
     const uint32_t m = chunk_masks[chunk * E + e];
     const uint32_t below = (1u << (uint32_t)(t - t0)) - 1u;
     const int32_t rank = chunk_base[chunk * E + e] + __popc(m & below);
+    sorted_pair[rank] = (int32_t)p;
+    if (pair_pos != nullptr) pair_pos[p] = rank;
+  }
+}
+
+// Fused scan + scatter (E <= kFuseThreads and chunks x E <= kFuseMasks).
+// Workgroup c: thread t counts expert e = t % Ep over the chunks of its
+// group t / Ep -- all of them for the expert's total, those before c for
+// this chunk's base; the groups meet in LDS; an exclusive scan over the
+// experts gives the offsets (workgroup 0 writes them); then the pairs of
+// chunk c are placed as in route_scatter_kernel.
+constexpr int kFuseThreads = 512;
+constexpr int64_t kFuseMasks = 16384;
+constexpr int kFuseBatch = 16;  // mask loads in flight per thread
+
+__global__ __launch_bounds__(kFuseThreads) void route_scan_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, const uint32_t* __restrict__ chunk_masks,
+    int64_t T, int E, int k, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+  __shared__ int32_t s_tot[kFuseThreads];
+  __shared__ int32_t s_pre[kFuseThreads];
+  __shared__ int32_t s_base[kFuseThreads];
+  __shared__ int32_t s_wsum[kFuseThreads / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t chunk = blockIdx.x;
+  const int64_t nchunks = (T + kRouteChunk - 1) / kRouteChunk;
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  const int groups = kFuseThreads / Ep;
+  const int e = t % Ep, grp = t / Ep;
+  const int64_t cpg = (nchunks + groups - 1) / groups;
+  const int64_t c0 = (int64_t)grp * cpg;
+  const int64_t c1 = c0 + cpg < nchunks ? c0 + cpg : nchunks;
+  int32_t tot = 0, pre = 0;
+  for (int64_t cb = c0; cb < c1; cb += kFuseBatch) {
+    uint32_t mv[kFuseBatch];
+#pragma unroll
+    for (int u = 0; u < kFuseBatch; ++u) {
+      const int64_t c = cb + u;
+      mv[u] = (e < E && c < c1) ? chunk_masks[c * E + e] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kFuseBatch; ++u) {
+      const int32_t n = __popc(mv[u]);
+      tot += n;
+      pre += (cb + u < chunk) ? n : 0;
+    }
+  }
+  s_tot[t] = tot;
+  s_pre[t] = pre;
+  __syncthreads();
+  // expert t's total and prefix: the sum over the groups
+  tot = 0;
+  pre = 0;
+  if (t < E) {
+    for (int gi = 0; gi < groups; ++gi) {
+      tot += s_tot[gi * Ep + t];
+      pre += s_pre[gi * Ep + t];
+    }
+  }
+  // exclusive scan of the totals over the experts
+  int32_t incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int32_t excl = incl - tot;
+  for (int w = 0; w < wave; ++w) excl += s_wsum[w];
+  if (t < E) {
+    s_base[t] = excl + pre;
+    if (chunk == 0) {
+      expert_offsets[t] = excl;
+      if (t == E - 1) expert_offsets[E] = excl + tot;
+    }
+  }
+  __syncthreads();
+  const int64_t t0 = chunk * kRouteChunk;
+  int64_t t1 = t0 + kRouteChunk;
+  if (t1 > T) t1 = T;
+  for (int64_t p = t0 * k + t; p < t1 * k; p += kFuseThreads) {
+    const int64_t tk = p / k;
+    const int ex = topk_ids[p];
+    const uint32_t m = chunk_masks[chunk * E + ex];
+    const uint32_t below = (1u << (uint32_t)(tk - t0)) - 1u;
+    const int32_t rank = s_base[ex] + __popc(m & below);
     sorted_pair[rank] = (int32_t)p;
     if (pair_pos != nullptr) pair_pos[p] = rank;
   }
@@ -246,7 +351,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int64_t nchunks = (a.T + kRouteChunk - 1) / kRouteChunk;
   const int regs = (a.E + 63) / 64;
-  const dim3 grid((unsigned)nchunks), block(64 * kRouteWaves);
+  // with an activation conversion, at least two workgroups per CU share it
+  int64_t g0 = nchunks;
+  if (a.x16 != nullptr && a.x_bf16 && g0 < 2 * (int64_t)a.num_cus) g0 = 2 * (int64_t)a.num_cus;
+  const dim3 grid((unsigned)g0), block(64 * kRouteWaves);
+  const dim3 cgrid((unsigned)nchunks);
 #define NF4MOE_ROUTE_CASE(R)                                                  \
   case R:                                                                     \
     hipLaunchKernelGGL(route_chunk_kernel<R>, grid, block, 0, stream,         \
@@ -278,11 +387,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
 #undef NF4MOE_ROUTE_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.E <= kFuseThreads && nchunks * a.E <= kFuseMasks) {
+    hipLaunchKernelGGL(route_scan_scatter_kernel, cgrid, dim3(kFuseThreads), 0, stream,
+                       a.topk_ids, a.chunk_masks, a.T, a.E, a.k, a.expert_offsets,
+                       a.sorted_pair, a.pair_pos);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream,
                      a.chunk_masks, nchunks, a.E, a.expert_offsets, a.chunk_base);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scatter_kernel, grid, dim3(256), 0, stream, a.topk_ids,
+  hipLaunchKernelGGL(route_scatter_kernel, cgrid, dim3(256), 0, stream, a.topk_ids,
                      a.chunk_masks, a.chunk_base, a.T, a.E, a.k, a.sorted_pair,
                      a.pair_pos);
   return hipGetLastError();

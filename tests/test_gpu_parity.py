@@ -113,8 +113,12 @@ def _check_route(gpu_lib, lg, k, renorm=True):
     assert np.max(np.abs(w - w_ref) / w_ref) < 1e-6
 
 
+# (5000, 128, 8) and (9000, 64, 8) have more chunk masks than the fused
+# scan+scatter kernel takes (three-kernel path); (1000, 300, 4) is fused with
+# E above 256.
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (64, 8, 2), (33, 64, 8), (4096, 64, 8),
-                                   (4096, 128, 8), (100, 1024, 32), (77, 5, 5), (40, 1, 1)])
+                                   (4096, 128, 8), (100, 1024, 32), (77, 5, 5), (40, 1, 1),
+                                   (5000, 128, 8), (9000, 64, 8), (1000, 300, 4)])
 def test_route_permute_matches_oracle(gpu_lib, T, E, k):
     lg = np.random.default_rng(T * 7 + E).standard_normal((T, E), dtype=np.float32)
     _check_route(gpu_lib, lg, k)
