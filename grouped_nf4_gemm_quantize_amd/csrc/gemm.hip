@@ -21,26 +21,30 @@
 //   that gives the 32 workgroups of one XCD consecutive tiles (tiles sharing
 //   activation rows or weight rows meet in that XCD's L2).
 //
-// Operand staging: activations (fp16), packed weights (and the LoRA A rows)
-// of a step are copied global -> LDS by buffer loads that write LDS directly
-// (no VGPR staging) into a 3-stage ring, up to three steps ahead of use.
-// absmax travels in groups of four steps (16 bytes per weight row, a quarter
-// of the L2 requests of one copy per step) into a double buffer, carried by
-// every fourth copy batch.  The copies are issued from inline assembly, so
-// the compiler does not track them: the kernel itself waits with a counted
-// s_waitcnt on the vector-memory counter (the stage in use is complete once
-// at most the newer batch's copies are pending; every wave issues the same
-// copies, so one immediate per batch kind holds for all of them) followed by
-// s_barrier, which keeps the newer batch in flight across the barrier.
+// Operand staging: buffer loads that write LDS directly (no VGPR staging)
+// copy the operands global -> LDS ahead of use:
+//   activations (fp16) and the LoRA A rows of one step into a 2-stage ring,
+//   one step ahead;
+//   packed codes of a step PAIR (64 bytes of every weight row: half the
+//   address-unit work of 32-byte rows, which cost as much per row as full
+//   64-byte segments) into a 2-stage ring, two steps ahead;
+//   absmax in groups of four steps (16 bytes per weight row) into a double
+//   buffer, two steps ahead.
+// The copies are issued from inline assembly, so the compiler does not
+// track them: the kernel itself waits with a counted s_waitcnt on the
+// vector-memory counter (copies complete in issue order; every wave issues
+// the same copies, so one immediate per step phase holds for all of them)
+// followed by s_barrier; see kloop for the schedule.
 //   A stage: 128 rows x 128 B; the 16-byte chunk c of row r sits at chunk
 //            c ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes and
 //            serves a 16-byte read per lane in groups of 16 lanes: 16
 //            fragment rows r..r+15 must cover all 64 banks, and two rows
 //            2 apart (same bank half) must differ in the swizzled chunk.
-//   B stage: 512 rows x 32 B (64 codes of a block); the 16-byte half h of
-//            row l sits at half h ^ ((l >> 3) & 1) (16 consecutive rows
-//            then cover all 64 banks).
-//   L stage: 16 LoRA A rows x 128 B.   absmax group: 512 rows x 4 fp32.
+//   pair stage: 512 rows x 64 B (steps 2p, 2p + 1: 64 codes each); the
+//            16-byte chunk c of row l sits at c ^ ((l >> 2) & 3), so 16
+//            consecutive rows cover all 64 banks.
+//   L (after A in the A stage): 16 LoRA A rows x 128 B.
+//   absmax group: 512 rows x 4 fp32.
 // Buffer resources bound every copy: a source offset outside the tensor
 // reads zeros instead of faulting.
 // Decode: the lane's 8 codes for one MFMA operand (one u32) go through the
@@ -73,18 +77,21 @@ constexpr int NT = 2;             // 2 n-tiles of 32 weight rows per wave
 constexpr int BNW = NT * 32;      // 64 weight rows per wave
 constexpr int BN = NWAVES * BNW;  // 512 weight rows per workgroup
 constexpr int kCopies = 32;
-constexpr int OFF_B = BM * BK * 2;             // A: 16384 B
-constexpr int OFF_L = OFF_B + BN * BK / 2;     // B: 16384 B
-constexpr int STAGE = OFF_L + kMaxLoraR * BK * 2;  // L: 2048 B -> 34816 B
+// Activation ring: 2 stages of one step (A 16384 B, then the LoRA A rows
+// 2048 B).  Packed-code ring: 2 stages of one step PAIR (512 rows x 64 B).
+constexpr int OFF_L = BM * BK * 2;                   // A: 16384 B
+constexpr int ASTAGE = OFF_L + kMaxLoraR * BK * 2;   // + L: 2048 B -> 18432 B
+constexpr int OFF_BR = 2 * ASTAGE;                   // packed-code ring
+constexpr int BPAIR = BN * BK;                       // 512 rows x 64 B = 32768 B
+constexpr int RING = OFF_BR + 2 * BPAIR;             // 102400 B
 constexpr int kAbsGroup = 4;                   // steps of absmax per copy (16 B per row)
-constexpr int kStages = 3;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
-__shared__ __attribute__((aligned(16))) char g_ring[kStages * STAGE];
+__shared__ __attribute__((aligned(16))) char g_ring[RING];
 __shared__ uint32_t g_lut[256 * kCopies];
 // absmax of kAbsGroup consecutive steps for the tile's 512 weight rows, two
 // groups in flight: g_sabs[group & 1][row * kAbsGroup + step % kAbsGroup]
@@ -99,7 +106,7 @@ namespace {
 
 // LoRA u of the tile (fp16 [BM][16]) at the end of the ring, which is free
 // once the k-loop has drained; the epilogue staging uses the ring's start.
-constexpr int OFF_U = kStages * STAGE - BM * kMaxLoraR * 2;
+constexpr int OFF_U = RING - BM * kMaxLoraR * 2;
 __device__ __forceinline__ _Float16* u_buf() {
   return reinterpret_cast<_Float16*>(g_ring + OFF_U);
 }
@@ -207,43 +214,47 @@ __device__ __forceinline__ f16x8 decode_scaled(uint32_t q, uint32_t lane_off, f1
 struct Src {
   i32x4 a_rsrc, b_rsrc, s_rsrc, l_rsrc;
   uint32_t a_off[2];  // A: 2 x 16 B per lane (1 KB per wave instruction)
-  uint32_t b_off[2];  // B: 2 x 16 B
+  uint32_t b_off[4];  // packed codes of a step pair: 4 x 16 B
   uint32_t s_off;     // absmax: 16 B (kAbsGroup steps of one row per lane)
   uint32_t l_off;     // LoRA A: 4 B
 };
 
+// Copies per wave: activations of one step (+ LoRA A), the packed codes of
+// a step pair, an absmax group.
 template <bool kLora>
-constexpr int dma_per_step() { return kLora ? 5 : 4; }    // without the absmax group
-constexpr int kDmaAbs = 1;                                 // absmax group copies per wave
+constexpr int kDmaA() { return kLora ? 3 : 2; }
+constexpr int kDmaB = 4;
+constexpr int kDmaAbs = 1;
 
-// The copies of step `kb` (clamped to the last step) into the stage at LDS
-// address `st`.  Batch `s` (the unclamped step index) also carries the absmax
-// of steps [s, s + kAbsGroup) when s is a multiple of kAbsGroup, into buffer
-// (s / kAbsGroup) & 1: that buffer last served steps s - 8 .. s - 5, whose
-// reads ended before the barrier of step s - 5, and the batch is issued at
-// step s - 3.
+// Activations (and LoRA A rows) of step `kb` (clamped) into the A stage at
+// LDS address `st`.
 template <bool kLora>
-__device__ __forceinline__ void issue_step(const Src& s, int kb, int sidx, int last,
-                                           uint32_t st, int wave) {
+__device__ __forceinline__ void issue_a(const Src& s, int kb, uint32_t st, int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     dma16(s.a_rsrc, s.a_off[i], (uint32_t)kb * (BK * 2), st + (wave * 2 + i) * 1024);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma16(s.b_rsrc, s.b_off[i], (uint32_t)kb * (BK / 2), st + OFF_B + (wave * 2 + i) * 1024);
   if constexpr (kLora)
     dma4(s.l_rsrc, s.l_off, (uint32_t)kb * (BK * 2), st + OFF_L + wave * 256);
-  if (sidx % kAbsGroup == 0) {
-    const int grp = min(sidx, last) / kAbsGroup;
-    const uint32_t buf = lds_addr(&g_sabs[(sidx / kAbsGroup) & 1][0]);
-    dma16(s.s_rsrc, s.s_off, (uint32_t)grp * (kAbsGroup * 4), buf + wave * 1024);
-  }
+}
+
+// Packed codes of step pair `p` (clamped; steps 2p, 2p + 1: 64 bytes of
+// every weight row) into the pair stage at LDS address `bst`.
+__device__ __forceinline__ void issue_b(const Src& s, int p, uint32_t bst, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(s.b_rsrc, s.b_off[i], (uint32_t)p * BK, bst + (wave * 4 + i) * 1024);
+}
+
+// The absmax of steps [4 grp, 4 grp + 4) into buffer `buf`.
+__device__ __forceinline__ void issue_abs(const Src& s, int grp, int buf, int wave) {
+  dma16(s.s_rsrc, s.s_off, (uint32_t)grp * (kAbsGroup * 4),
+        lds_addr(&g_sabs[buf][0]) + wave * 1024);
 }
 
 // Per-lane LDS read offsets, fixed for the kernel.
 struct Rd {
   uint32_t a[4];   // A fragment of substep s (m-tile 0; + 4096 per m-tile)
-  uint32_t b;      // packed row of n-tile 0 (+ 1024 per n-tile)
+  uint32_t b[2];   // packed codes of n-tile 0 in a pair stage, by step parity (+ 2048 per n-tile)
   uint32_t s;      // absmax element of n-tile 0's row (+ 32 rows per n-tile)
   uint32_t ua[2];  // LoRA: A fragment (16x16x32) of this wave's 16 rows, [k half]
   uint32_t ul;     // LoRA: A_e fragment of this lane (k half 0; + 64 B for half 1)
@@ -257,12 +268,13 @@ struct StepRegs {
   f16x2 sc[NT];
 };
 
-__device__ __forceinline__ void load_step_regs(const char* st, int step, const Rd& rd,
+__device__ __forceinline__ void load_step_regs(const char* bst, int step, const Rd& rd,
                                                StepRegs& r) {
   const float* sab = &g_sabs[(step / kAbsGroup) & 1][step % kAbsGroup];
+  const uint32_t bo = (step & 1) ? rd.b[1] : rd.b[0];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    r.bq[nt] = *reinterpret_cast<const u32x4*>(st + OFF_B + rd.b + nt * 1024);
+    r.bq[nt] = *reinterpret_cast<const u32x4*>(bst + bo + nt * 2048);
     const _Float16 sh = (_Float16)sab[rd.s + nt * 32 * kAbsGroup];
     r.sc[nt] = f16x2{sh, sh};
   }
@@ -313,8 +325,8 @@ __device__ __forceinline__ void scale_b(const StepRegs& r, const uint32_t (&d)[N
 // are read -- for S = 3 those of substep 0 of the next step, from the next
 // stage `nst` (valid once the barrier before substep 3 has passed).
 template <int S, int MTV, bool kLora, bool kABf16>
-__device__ __forceinline__ void substep(const char* st, const char* nst, int next_step,
-                                        const Rd& rd,
+__device__ __forceinline__ void substep(const char* st, const char* nst, const char* nbst,
+                                        int next_step, const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
                                         uint32_t (&d)[NT][4], int lora_live, int lora_bf16,
                                         f32x16 (&acc)[MT][NT], f32x4& acc_u) {
@@ -324,7 +336,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int nex
     load_a<MTV, kABf16>(st, rd, S + 1, af_n);
     lut_lookups(cur, S + 1, rd.lane_off, dn);
   } else {
-    load_step_regs(nst, next_step, rd, nxt);
+    load_step_regs(nbst, next_step, rd, nxt);
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
     lut_lookups(nxt, 0, rd.lane_off, dn);
   }
@@ -354,48 +366,70 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int nex
 
 }
 
-// The k-loop of one tile.  Copies run up to three steps ahead through the
-// ring: the copy of step kb + 3 goes into step kb's stage as soon as every
-// wave has read it (the barrier before substep 3).  Past the last step the
-// copy of the last step is repeated, so every step issues the same number of
-// copies and one wait count holds throughout.
+// The k-loop of one tile.  After the barrier of step kb (every wave is done
+// reading step kb's activations and, for odd kb, the pair stage of steps
+// kb - 1 and kb) the wave issues batch kb, in this order:
+//   activations of step kb + 2 into A stage kb % 2;
+//   odd kb: codes of pair (kb + 3) / 2 into that pair stage;
+//   kb % 4 == 1: absmax group (kb + 3) / 4 -- buffer ((kb + 3) / 4) & 1 last
+//     served steps kb - 5 .. kb - 2, whose reads ended at the barrier of kb - 2.
+// Before substep 3 of step kb the activations of step kb + 1 (batch kb - 1,
+// issued first in it) must have landed: at most the copies issued after them
+// in batch kb - 1 may be pending -- 4 when kb - 1 is odd, +1 when it carried
+// an absmax group; anything older (codes and absmax needed by step kb + 1,
+// issued two or more steps earlier) has landed with them, since copies
+// complete in order.  Pairs and activations are issued at least one full
+// step before use, codes and absmax two.  Past the last step the copies of
+// the last step / pair / group are repeated, so the counts hold throughout.
 template <int MTV, bool kLora, bool kABf16>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
                                       int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
                                       f32x4& acc_u) {
-  constexpr int ND = dma_per_step<kLora>();
+  constexpr int NA = kDmaA<kLora>();
   const uint32_t ring = lds_addr(g_ring);
   const int last = nk - 1;
-  issue_step<kLora>(src, 0, 0, last, ring, wave);
-  issue_step<kLora>(src, min(1, last), 1, last, ring + STAGE, wave);
-  issue_step<kLora>(src, min(2, last), 2, last, ring + 2 * STAGE, wave);
+  const int last_pair = last >> 1;
+  // prologue: absmax group 0, pair 0, activations of steps 0 and 1, pair 1 --
+  // as if batch -1 (odd, activations then a pair) were the last one issued
+  issue_abs(src, 0, 0, wave);
+  issue_b(src, 0, ring + OFF_BR, wave);
+  issue_a<kLora>(src, 0, ring, wave);
+  issue_a<kLora>(src, min(1, last), ring + ASTAGE, wave);
+  issue_b(src, min(1, last_pair), ring + OFF_BR + BPAIR, wave);
   const int lora_live = (lane & 15) < lora_r;
 
-  // stage 0 (and absmax group 0) complete: at most batches 1 and 2 pending
-  wait_vm_barrier<2 * ND>();
+  // absmax group 0, pair 0 and step 0's activations complete
+  wait_vm_barrier<NA + kDmaB>();
   StepRegs cur, nxt;
   f16x8 af[MT];
   uint32_t d[NT][4];
-  load_step_regs(g_ring, 0, rd, cur);
+  load_step_regs(g_ring + OFF_BR, 0, rd, cur);
   load_a<MTV, kABf16>(g_ring, rd, 0, af);
   lut_lookups(cur, 0, rd.lane_off, d);
-  int st = 0;  // stage of step kb
   for (int kb = 0; kb < nk; ++kb) {
-    const int sn = st == 2 ? 0 : st + 1;
-    const char* sp = g_ring + st * STAGE;
-    const char* np = g_ring + sn * STAGE;
-    substep<0, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<1, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<2, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    // stage kb + 1 complete (at most batch kb + 2 pending, which carries the
-    // absmax group when kb + 2 is a multiple of kAbsGroup), and every wave is
-    // done reading stage kb: refill it with step kb + 3
-    if ((kb + 2) % kAbsGroup == 0) wait_vm_barrier<ND + kDmaAbs>();
-    else wait_vm_barrier<ND>();
-    issue_step<kLora>(src, min(kb + 3, last), kb + 3, last, ring + st * STAGE, wave);
-    substep<3, MTV, kLora, kABf16>(sp, np, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    const int a = kb & 1;
+    const char* sp = g_ring + a * ASTAGE;              // step kb's activations
+    const char* np = g_ring + (a ^ 1) * ASTAGE;        // step kb + 1's
+    const char* nbp = g_ring + OFF_BR + (((kb + 1) >> 1) & 1) * BPAIR;  // kb + 1's codes
+    substep<0, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<1, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<2, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    switch (kb & 3) {
+      case 0: wait_vm_barrier<kDmaB>(); break;             // batch kb - 1 = 3 mod 4
+      case 2: wait_vm_barrier<kDmaB + kDmaAbs>(); break;   // batch kb - 1 = 1 mod 4
+      default: wait_vm_barrier<0>(); break;                // batch kb - 1 even
+    }
+    issue_a<kLora>(src, min(kb + 2, last), ring + a * ASTAGE, wave);
+    if (kb & 1) {
+      const int pn = (kb + 3) >> 1;
+      issue_b(src, min(pn, last_pair), ring + OFF_BR + (pn & 1) * BPAIR, wave);
+      if ((kb & 3) == 1) {
+        const int grp = (kb + 3) >> 2;
+        issue_abs(src, min(grp, last >> 2), grp & 1, wave);
+      }
+    }
+    substep<3, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
     cur = nxt;
-    st = sn;
   }
 }
 
@@ -452,7 +486,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   Rd rd;
 #pragma unroll
   for (int s = 0; s < 4; ++s) rd.a[s] = n32 * 128 + (((g2 * 4 + s) ^ ((n32 >> 1) & 7)) << 4);
-  rd.b = (wave * BNW + n32) * 32 + ((g2 ^ ((n32 >> 3) & 1)) << 4);
+  // pair stage: weight row l's 64 bytes hold steps 2p (chunks 0, 1) and
+  // 2p + 1 (chunks 2, 3), 16-byte chunk c at c ^ ((l >> 2) & 3), so 16
+  // consecutive rows cover all 64 banks
+#pragma unroll
+  for (int sp2 = 0; sp2 < 2; ++sp2)
+    rd.b[sp2] = (wave * BNW + n32) * 64 + (((sp2 * 2 + g2) ^ ((n32 >> 2) & 3)) << 4);
   rd.s = (wave * BNW + n32) * kAbsGroup;
   // LoRA operands of 16x16x32: A row c16 of this wave's 16 rows and k chunk
   // 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
@@ -518,14 +557,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       const uint32_t a_src = g.gather ? (uint32_t)(g.gather[idx] / g.gather_div) : (uint32_t)idx;
       src.a_off[i] = (a_src * (uint32_t)K + gchunk * 8) * 2;
     }
-    // B: wave instruction i covers LDS rows [32 j, 32 j + 32), two 16-B
-    // halves each, j = 2 wave + i
+    // packed codes of a step pair: wave instruction i covers pair-stage
+    // rows [16 j, 16 j + 16), four 16-B chunks each, j = 4 wave + i; the
+    // chunk at position q of row l is chunk q ^ ((l >> 2) & 3) of the row's
+    // 64 bytes (steps 2p, 2p + 1)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = (wave * 2 + i) * 64 + lane;
-      const int l = c >> 1;
-      const int half = (c & 1) ^ ((l >> 3) & 1);
-      src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + half * 16;
+    for (int i = 0; i < 4; ++i) {
+      const int l = (wave * 4 + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((l >> 2) & 3);
+      src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + c * 16;
     }
     // absmax groups: the wave's instruction covers rows [64 wave, 64 wave +
     // 64), 16 bytes (kAbsGroup steps) per row
@@ -620,7 +660,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       constexpr int PITCH = COLS * ESZ + 16;
       constexpr int CPR = COLS * ESZ / 16;          // 16-byte chunks per row
       constexpr int EPC = 16 / ESZ;                 // elements per chunk
-      static_assert(NWAVES * 32 * PITCH <= kStages * STAGE, "staging fits the ring");
+      static_assert(NWAVES * 32 * PITCH <= RING, "staging fits the ring");
       char* ws = g_ring + wave * 32 * PITCH;
       const int ncols = kSwiglu ? I : N;
       const int cbase = kSwiglu ? n_idx * 256 + wave * (BNW / 2) : n_idx * BN + wave * BNW;
