@@ -523,9 +523,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   const int total = __builtin_amdgcn_readfirstlane(g_tiles[g.E]) * n_tiles;
   const int G = gridDim.x;  // a multiple of 8
   const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  // A last, partial round of rem <= G/2 tiles would leave most workgroups
+  // idle while the others finish: its tiles are split into two 64-row
+  // halves (the same weights, half the rows each), one per workgroup.
+  const int q = total / G, rem = total - q * G;
+  const bool split_tail = rem > 0 && 2 * rem <= G;
   for (int r = 0;; ++r) {
-    const int tix = r * G + xcd * (G >> 3) + pos;
-    if (tix >= total) break;
+    const int u = xcd * (G >> 3) + pos;  // position within the round
+    int tix, half = -1;
+    if (split_tail && r == q) {
+      if (u >= 2 * rem) break;
+      tix = q * G + (u >> 1);
+      half = u & 1;
+    } else {
+      tix = r * G + u;
+      if (tix >= total) break;
+    }
     const int mt_global = tix / n_tiles;
     const int n_idx = tix - mt_global * n_tiles;
     int lo = 0, hi = g.E;  // g_tiles[lo] <= mt_global < g_tiles[hi]
@@ -535,8 +548,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     }
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int m_local = mt_global - __builtin_amdgcn_readfirstlane(g_tiles[e]);
-    const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + m_local * BM;
-    const int rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
+    int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + m_local * BM;
+    int rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
+    if (half >= 0) {
+      row0 += half * (BM / 2);
+      rows_valid = min(BM / 2, rows_valid - half * (BM / 2));
+      if (rows_valid <= 0) break;  // the tile's rows fit its first half
+    }
     const int mtv = (rows_valid + 31) >> 5;
 
     Src src;
