@@ -302,6 +302,73 @@ def bench_decode(dev, steps: int):
     return out
 
 
+def control_lane(cfg, st, x16, off, sp, stream, iters: int):
+    """Dequantise-then-GEMM control (a benchmark control, never a product
+    path): the whole stack is dequantised to fp16 with plain torch ops, then
+    the experts run as padded batched library GEMMs (hipBLASLt through
+    torch.bmm) with torch SwiGLU between them.  It measures the round trip
+    the in-register decode removes (grouped-nf4-gemm solutions entry "How do
+    I run a grouped GEMM directly on NF4 packed MoE expert weights"; README
+    "The package family").  The dequantisation is an upper bound (several
+    generic kernels); the GEMM part alone is a lower bound for any
+    dequantise-first path."""
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding
+
+    dev = x16.device
+    levels = torch.tensor(binding.codebook(), dtype=torch.float32, device=dev)
+    E = cfg.E
+    offs = off.cpu().tolist()
+    counts = [offs[e + 1] - offs[e] for e in range(E)]
+    mmax = max(max(counts), 1)
+
+    def dequant_t(p, a):
+        # [E, N, K/2] codes + [E, N, K/64] absmax -> W^T [E, K, N] fp16
+        n = p.shape[1]
+        kk = p.shape[2] * 2
+        codes = torch.stack(((p >> 4), (p & 15)), dim=-1).reshape(E, n, kk).long()
+        w = levels[codes] * a.repeat_interleave(64, dim=-1)
+        return w.to(torch.float16).transpose(1, 2).contiguous()
+
+    (gp, ga), (dp, da) = st["gu"], st["dn"]
+    out = {}
+
+    def deq():
+        out["wgu"] = dequant_t(gp, ga)
+        out["wdn"] = dequant_t(dp, da)
+
+    deq()
+    deq_ms = time_events(deq, 2, stream)
+    # activations gathered per expert into a padded [E, mmax, H] block
+    xp = torch.zeros((E, mmax, cfg.H), dtype=torch.float16, device=dev)
+    rows = (sp // cfg.k).long()
+    for e in range(E):
+        if counts[e]:
+            xp[e, :counts[e]] = x16[rows[offs[e]:offs[e + 1]]]
+    I = cfg.I
+
+    def gemms():
+        g = torch.bmm(xp, out["wgu"])
+        hh = torch.nn.functional.silu(g[..., :I]) * g[..., I:]
+        out["o"] = torch.bmm(hh, out["wdn"])
+        out["h"] = hh
+
+    gemms()
+    gemm_ms = time_events(gemms, iters, stream)
+    # HBM floor of any dequantisation: read codes + absmax, write fp16 W^T
+    deq_bytes = sum(t.numel() * t.element_size() for t in (gp, ga, dp, da)) + \
+        2 * (out["wgu"].numel() + out["wdn"].numel())
+    floor_us = deq_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
+    res = {"dequant_us": round(deq_ms * 1e3, 1), "dequant_hbm_floor_us": round(floor_us, 1),
+           "dequant_bytes": deq_bytes, "gemm_swiglu_us": round(gemm_ms * 1e3, 1),
+           "total_us": round((deq_ms + gemm_ms) * 1e3, 1),
+           "total_at_dequant_floor_us": round(floor_us + gemm_ms * 1e3, 1),
+           "padded_rows_per_expert": mmax}
+    del out["wgu"], out["wdn"], xp
+    return res, out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +378,8 @@ def main() -> int:
                     choices=["olmoe", "qwen3_zipf", "qlora"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-control", action="store_true",
+                    help="skip the dequantise-then-GEMM control lane")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -402,6 +471,23 @@ def main() -> int:
     log(f"[bench] gate_up GEMM {gu_ms * 1e3:.1f} us {gu_tf:.1f} TFLOP/s; "
         f"down GEMM {dn_ms * 1e3:.1f} us {dn_tf:.1f} TFLOP/s")
     traffic = traffic_from_profiles(GEMM_SRC)
+    control = None
+    if glo is None and not args.no_control:
+        control, cout = control_lane(cfg, st, x16, off, sp, stream, max(args.steps, 10))
+        control["fused_gemms_us"] = round((gu_ms + dn_ms) * 1e3, 1)
+        control["speedup_vs_control_total"] = round(control["total_us"] / control["fused_gemms_us"], 3)
+        control["speedup_vs_control_gemm_only"] = round(control["gemm_swiglu_us"] / control["fused_gemms_us"], 3)
+        control["speedup_vs_control_at_dequant_floor"] = round(
+            control["total_at_dequant_floor_us"] / control["fused_gemms_us"], 3)
+        # the control computes the same thing: expert 0's h rows against ours
+        offs0 = off[:2].cpu().tolist()
+        n0 = offs0[1] - offs0[0]
+        if n0:
+            ref = cout["h"][0, :n0].float()
+            got = h[offs0[0]:offs0[1]].float()
+            control["h_rel_fro_vs_fused"] = float(((got - ref).norm() / ref.norm()).item())
+        del cout
+        log(f"[bench] dequantise-then-GEMM control {control}")
     del h, o, x16
 
     result = {
@@ -440,6 +526,8 @@ def main() -> int:
             "down_us": round(dn_ms * 1e3, 3), "down_tflops": round(dn_tf, 3),
         },
     }
+    if control is not None:
+        result["control_dequant_then_gemm"] = control
     del gp, ga, dp, da, st, y, ws
     torch.cuda.empty_cache()
     if not args.no_decode:
