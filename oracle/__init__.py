@@ -37,6 +37,12 @@ from .nf4 import (  # noqa: F401
     nf4_codebook,
     nf4_codebook_f64,
     nf4_levels_unnormalised,
+    fp4_codebook,
+    fp4_codebook_f64,
+    fp4_code,
+    codebook,
+    QUANT_TYPES,
+    block_error_bound,
     nearest_code,
     quantize_blockwise,
     dequantize_blockwise,

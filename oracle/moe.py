@@ -44,8 +44,8 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def _deq64(packed_e: np.ndarray, absmax_e: np.ndarray) -> np.ndarray:
-    return dequantize_blockwise(packed_e, absmax_e).astype(np.float64)
+def _deq64(packed_e: np.ndarray, absmax_e: np.ndarray, quant_type: str = "nf4") -> np.ndarray:
+    return dequantize_blockwise(packed_e, absmax_e, quant_type=quant_type).astype(np.float64)
 
 
 def _lora_delta(a_rows: np.ndarray, lora, e: int) -> np.ndarray:
@@ -74,7 +74,7 @@ def expert_mlp(x_rows, w_gu, w_dn, lora_gu=None, lora_dn=None, e=0):
 
 
 def grouped_gemm(a, packed, absmax, offsets, gather=None, gather_div=1,
-                 lora=None, swiglu=False, row_scale=None):
+                 lora=None, swiglu=False, row_scale=None, quant_type="nf4"):
     """Rows of ``a`` times each expert's dequantised weight, per group.
 
     Row i of the output belongs to expert e when
@@ -98,7 +98,7 @@ def grouped_gemm(a, packed, absmax, offsets, gather=None, gather_div=1,
         idx = np.arange(lo, hi)
         src = idx if gather is None else np.asarray(gather)[idx] // gather_div
         rows = a[src]
-        g = rows @ _deq64(packed[e], absmax[e]).T + _lora_delta(rows, lora, e)
+        g = rows @ _deq64(packed[e], absmax[e], quant_type).T + _lora_delta(rows, lora, e)
         if swiglu:
             g = silu(g[:, : N // 2]) * g[:, N // 2 :]
         out[lo:hi] = g
@@ -108,7 +108,7 @@ def grouped_gemm(a, packed, absmax, offsets, gather=None, gather_div=1,
 
 
 def moe_forward(x, logits, k, gu_packed, gu_absmax, dn_packed, dn_absmax,
-                lora_gu=None, lora_dn=None, renormalize=True):
+                lora_gu=None, lora_dn=None, renormalize=True, quant_type="nf4"):
     """Full routed-expert layer, the plain per-expert loop, in fp64.
 
     ``x`` [T, H] holds the activation values (bf16 values widened exactly);
@@ -128,8 +128,8 @@ def moe_forward(x, logits, k, gu_packed, gu_absmax, dn_packed, dn_absmax,
             continue
         pairs = sorted_pair[lo:hi].astype(np.int64)
         toks = pairs // k  # each token appears at most once per expert
-        o, _, _ = expert_mlp(x[toks], _deq64(gu_packed[e], gu_absmax[e]),
-                             _deq64(dn_packed[e], dn_absmax[e]),
+        o, _, _ = expert_mlp(x[toks], _deq64(gu_packed[e], gu_absmax[e], quant_type),
+                             _deq64(dn_packed[e], dn_absmax[e], quant_type),
                              lora_gu, lora_dn, e)
         y[toks] += w_flat[pairs][:, None] * o
     info = dict(ids=ids, w=w, sorted_pair=sorted_pair, pair_pos=pair_pos,
@@ -139,7 +139,7 @@ def moe_forward(x, logits, k, gu_packed, gu_absmax, dn_packed, dn_absmax,
 
 def moe_forward_tokens(tokens, x, logits, k, gu_packed, gu_absmax, dn_packed,
                        dn_absmax, lora_gu=None, lora_dn=None,
-                       renormalize=True):
+                       renormalize=True, quant_type="nf4"):
     """Outputs y[t] for the listed tokens only (fp64 [len(tokens), H]).
 
     Used to check full-size runs on a sample of tokens: each token is routed
@@ -151,8 +151,8 @@ def moe_forward_tokens(tokens, x, logits, k, gu_packed, gu_absmax, dn_packed,
 
     def weights(e):
         if e not in cache:
-            cache[e] = (_deq64(gu_packed[e], gu_absmax[e]),
-                        _deq64(dn_packed[e], dn_absmax[e]))
+            cache[e] = (_deq64(gu_packed[e], gu_absmax[e], quant_type),
+                        _deq64(dn_packed[e], dn_absmax[e], quant_type))
         return cache[e]
 
     out = np.zeros((len(tokens), x.shape[1]), dtype=np.float64)

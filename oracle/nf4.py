@@ -29,6 +29,19 @@ Readings taken where the pages are silent (each listed in the design notes):
   the lower index.  An all-zero block stores absmax 0 and code 7 (level 0).
 * Packing: two codes per byte, the even element in the high nibble.
 * Dequantise: fl32(level[code] * absmax), in fp32.
+
+The other 4-bit packed mode, fp4 (README, "The problem": nf4 / fp4 are the
+4-bit packed storage modes, with a test-pinned fidelity ordering in which
+nf4 reconstructs better than fp4).  The pages give no fp4 codebook; the
+plainest reading, taken here, is the OCP e2m1 element format scaled so that
+the block's absmax maps to its largest magnitude (6):
+* code = s << 3 | m: sign bit s, magnitude index m, magnitudes
+  {0, 0.5, 1, 1.5, 2, 3, 4, 6} / 6 (m = 0..7); code 8 is -0.
+* Code of an element: xn = fl32(x / absmax) as for nf4; s = (xn < 0); m =
+  the nearest fp32 magnitude level to |xn| in exact arithmetic, an exact tie
+  going to the even m (round half to even, as e2m1 conversion does).  An
+  all-zero block stores absmax 0 and code 0.
+* Same packing, absmax and dequantisation as nf4.
 """
 
 from __future__ import annotations
@@ -69,6 +82,51 @@ def nf4_codebook_f64(ppf=_norm_ppf) -> np.ndarray:
 def nf4_codebook() -> np.ndarray:
     """NF4 levels rounded once to fp32 (the stored codebook)."""
     return nf4_codebook_f64().astype(np.float32)
+
+
+QUANT_TYPES = ("nf4", "fp4")
+
+_E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def fp4_codebook_f64() -> np.ndarray:
+    """fp4 levels by code (not sorted): codes 0..7 = +magnitude/6, 8..15 the
+    negatives (code 8 is -0)."""
+    mags = np.array(_E2M1_MAGNITUDES, dtype=np.float64) / 6.0
+    return np.concatenate([mags, -mags])
+
+
+def fp4_codebook() -> np.ndarray:
+    """fp4 levels rounded once to fp32, by code."""
+    return fp4_codebook_f64().astype(np.float32)
+
+
+def codebook(quant_type: str = "nf4") -> np.ndarray:
+    """The 16 fp32 levels of a storage mode, indexed by code."""
+    if quant_type == "nf4":
+        return nf4_codebook()
+    if quant_type == "fp4":
+        return fp4_codebook()
+    raise ValueError(f"unknown quant_type {quant_type!r}")
+
+
+def fp4_code(xn: np.ndarray) -> np.ndarray:
+    """fp4 code of each fp32 value in ``xn``: sign bit (xn < 0) and the
+    nearest magnitude level (fp64 distances), exact ties to the even index."""
+    x = np.asarray(xn, dtype=np.float32)
+    mags = fp4_codebook()[:8].astype(np.float64)
+    ax = np.abs(x.astype(np.float64)).reshape(-1)
+    m = np.empty(ax.shape, dtype=np.uint8)
+    step = 1 << 20
+    for s0 in range(0, ax.size, step):
+        d = np.abs(ax[s0:s0 + step, None] - mags[None, :])
+        best = np.min(d, axis=1, keepdims=True)
+        hit = d == best  # one or (at an exact tie) two adjacent indices
+        even = hit & ((np.arange(8) % 2) == 0)[None, :]
+        idx = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(hit, axis=1))
+        m[s0:s0 + step] = idx.astype(np.uint8)
+    sign = (x.reshape(-1) < 0).astype(np.uint8)
+    return ((sign << 3) | m).reshape(x.shape).astype(np.uint8)
 
 
 def packed_bytes(E: int, N: int, K: int, blocksize: int = BLOCKSIZE) -> int:
@@ -113,33 +171,38 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize_blockwise(w: np.ndarray, blocksize: int = BLOCKSIZE):
+def quantize_blockwise(w: np.ndarray, blocksize: int = BLOCKSIZE, quant_type: str = "nf4"):
     """Quantise ``w`` [..., K] (fp32) blockwise along the last axis.
 
     Returns ``(packed uint8 [..., K/2], absmax fp32 [..., K/blocksize])``.
     The leading axes are (expert, row): a block is ``blocksize`` consecutive
     elements of one row of one expert, so it never crosses either.
+    ``quant_type`` is "nf4" or "fp4".
     """
     w = np.asarray(w)
     assert w.dtype == np.float32, "the oracle quantises fp32 values"
     assert w.shape[-1] % blocksize == 0
     assert np.all(np.isfinite(w)), "non-finite input is outside the definition"
-    levels = nf4_codebook()
+    assert quant_type in QUANT_TYPES
     blocks = w.reshape(w.shape[:-1] + (w.shape[-1] // blocksize, blocksize))
     absmax = np.max(np.abs(blocks), axis=-1)  # exact in fp32
     safe = np.where(absmax == 0, np.float32(1), absmax).astype(np.float32)
     # IEEE fp32 division, round to nearest even (numpy float32 '/').
     xn = (blocks / safe[..., None]).astype(np.float32)
-    codes = nearest_code(xn, levels)
-    codes[absmax == 0] = 7  # all-zero block -> the exact-zero level
+    if quant_type == "nf4":
+        codes = nearest_code(xn, nf4_codebook())
+        codes[absmax == 0] = 7  # all-zero block -> the exact-zero level
+    else:
+        codes = fp4_code(xn)
+        codes[absmax == 0] = 0  # all-zero block -> +0
     codes = codes.reshape(w.shape)
     return pack_codes(codes), absmax.astype(np.float32)
 
 
 def dequantize_blockwise(packed: np.ndarray, absmax: np.ndarray,
-                         blocksize: int = BLOCKSIZE) -> np.ndarray:
+                         blocksize: int = BLOCKSIZE, quant_type: str = "nf4") -> np.ndarray:
     """fp32 weights: level[code] * absmax, one fp32 multiply per element."""
-    levels = nf4_codebook()
+    levels = codebook(quant_type)
     codes = unpack_codes(packed)
     vals = levels[codes]
     K = vals.shape[-1]
@@ -148,8 +211,8 @@ def dequantize_blockwise(packed: np.ndarray, absmax: np.ndarray,
     return (vals * scale).astype(np.float32)
 
 
-def block_error_bound(absmax: np.ndarray) -> np.ndarray:
+def block_error_bound(absmax: np.ndarray, quant_type: str = "nf4") -> np.ndarray:
     """Largest round-trip error a block can see: half the widest level gap."""
-    q = nf4_codebook().astype(np.float64)
+    q = np.unique(codebook(quant_type).astype(np.float64))
     return np.asarray(absmax, np.float64) * float(np.max(np.diff(q))) / 2.0
 
