@@ -67,7 +67,27 @@ _SIGNATURES = {
     "moe_expert_forward_routing": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int,
                                             ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp),
                                             ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp)]),
+    "nbit_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
+    "nbit_quantize_experts": (_c_int, [_c_int, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int,
+                                       _c_vp, _c_vp, _c_vp, _c_vp]),
+    "grouped_nbit_gemm": (_c_int, [_c_int, _c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_vp, _c_vp,
+                                   _c_vp, _c_int, _c_i64, _c_i64, _c_i64,
+                                   ctypes.POINTER(LoraStruct), _c_int, _c_vp, _c_vp,
+                                   _c_vp, _c_int, _c_vp]),
+    "moe_expert_forward_nbit": (_c_int, [_c_int, _c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_int,
+                                         _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                         ctypes.POINTER(LoraStruct), ctypes.POINTER(LoraStruct),
+                                         _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
 }
+
+# storage modes of the nbit entry points (NF4MOE_QT_* in include/nf4moe.h)
+QUANT_TYPES = {"nf4": 0, "fp4": 1}
+
+
+def _qt(quant_type: str) -> int:
+    if quant_type not in QUANT_TYPES:
+        raise ValueError(f"unknown quant_type {quant_type!r} (nf4 or fp4)")
+    return QUANT_TYPES[quant_type]
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -130,11 +150,14 @@ def _stream(device=None) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def codebook():
-    """The 16 fp32 NF4 levels of the library (list of floats)."""
+def codebook(quant_type: str = "nf4"):
+    """The 16 fp32 levels of a storage mode, by code (list of floats)."""
     lib = load()
     buf = (ctypes.c_float * 16)()
-    _check(lib.nf4moe_codebook(buf))
+    if quant_type == "nf4":
+        _check(lib.nf4moe_codebook(buf))
+    else:
+        _check(lib.nbit_codebook(_qt(quant_type), buf))
     return list(buf)
 
 
@@ -145,7 +168,7 @@ def packed_bytes(E: int, N: int, K: int) -> int:
     return int(n)
 
 
-def quantize(w, nonfinite_flag=None):
+def quantize(w, nonfinite_flag=None, quant_type: str = "nf4"):
     """Quantise w [E, N, K] (fp32 or bf16, GPU) -> (packed u8, absmax f32)."""
     torch = _torch()
     if w.dim() != 3:
@@ -153,9 +176,12 @@ def quantize(w, nonfinite_flag=None):
     E, N, K = w.shape
     packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
     absmax = torch.empty((E, N, max(K // 64, 1)), dtype=torch.float32, device=w.device)
-    _check(load().nf4_quantize_experts(_ptr(w), _dtype_code(w.dtype), E, N, K, 64,
-                                       _ptr(packed), _ptr(absmax), _ptr(nonfinite_flag),
-                                       _stream(w.device)))
+    args = (_ptr(w), _dtype_code(w.dtype), E, N, K, 64, _ptr(packed), _ptr(absmax),
+            _ptr(nonfinite_flag), _stream(w.device))
+    if quant_type == "nf4":
+        _check(load().nf4_quantize_experts(*args))
+    else:
+        _check(load().nbit_quantize_experts(_qt(quant_type), *args))
     return packed, absmax
 
 
@@ -195,7 +221,8 @@ def make_lora(A, B, scale: float):
 
 def grouped_gemm(a, packed, absmax, offsets, P: int, gather=None, gather_div: int = 1,
                  lora=None, swiglu: bool = False, row_scale=None, scatter=None,
-                 out=None, out_dtype=None, out_rows: Optional[int] = None):
+                 out=None, out_dtype=None, out_rows: Optional[int] = None,
+                 quant_type: str = "nf4"):
     """Grouped NF4 GEMM (see grouped_nf4_gemm in include/nf4moe.h).
 
     ``lora`` is ``(A, B, scale)`` or None.  Returns ``out``.
@@ -209,12 +236,15 @@ def grouped_gemm(a, packed, absmax, offsets, P: int, gather=None, gather_div: in
         out = torch.empty((rows, n_out), dtype=out_dtype or torch.float16, device=a.device)
     lib = load()
     ls = make_lora(*lora) if lora is not None else None
-    _check(lib.grouped_nf4_gemm(
-        _ptr(a), _dtype_code(a.dtype), a.shape[0], _ptr(gather), gather_div, _ptr(packed),
-        _ptr(absmax), _ptr(offsets), E, P, N, K,
-        ctypes.byref(ls) if ls is not None else None, EPI_SWIGLU if swiglu else EPI_NONE,
-        _ptr(row_scale), _ptr(scatter), _ptr(out), _dtype_code(out.dtype),
-        _stream(a.device)))
+    args = (_ptr(a), _dtype_code(a.dtype), a.shape[0], _ptr(gather), gather_div, _ptr(packed),
+            _ptr(absmax), _ptr(offsets), E, P, N, K,
+            ctypes.byref(ls) if ls is not None else None, EPI_SWIGLU if swiglu else EPI_NONE,
+            _ptr(row_scale), _ptr(scatter), _ptr(out), _dtype_code(out.dtype),
+            _stream(a.device))
+    if quant_type == "nf4":
+        _check(lib.grouped_nf4_gemm(*args))
+    else:
+        _check(lib.grouped_nbit_gemm(_qt(quant_type), *args))
     return out
 
 
@@ -224,7 +254,7 @@ def forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
 
 def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
                 gu_lora=None, dn_lora=None, renormalize: bool = True, y=None,
-                y_dtype=None, workspace=None):
+                y_dtype=None, workspace=None, quant_type: str = "nf4"):
     """Full routed-expert layer (see moe_expert_forward in include/nf4moe.h).
 
     ``gu_lora`` / ``dn_lora`` are ``(A, B, scale)`` or None.  ``workspace`` is an
@@ -242,13 +272,16 @@ def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     ls_gu = make_lora(*gu_lora) if gu_lora is not None else None
     ls_dn = make_lora(*dn_lora) if dn_lora is not None else None
-    _check(lib.moe_expert_forward(
-        _ptr(x), _dtype_code(x.dtype), _ptr(logits), T, H, I, E, k, int(bool(renormalize)),
-        _ptr(gu_packed), _ptr(gu_absmax), _ptr(dn_packed), _ptr(dn_absmax),
-        ctypes.byref(ls_gu) if ls_gu is not None else None,
-        ctypes.byref(ls_dn) if ls_dn is not None else None,
-        _ptr(y), _dtype_code(y.dtype), _ptr(workspace), workspace.numel(),
-        _stream(x.device)))
+    args = (_ptr(x), _dtype_code(x.dtype), _ptr(logits), T, H, I, E, k, int(bool(renormalize)),
+            _ptr(gu_packed), _ptr(gu_absmax), _ptr(dn_packed), _ptr(dn_absmax),
+            ctypes.byref(ls_gu) if ls_gu is not None else None,
+            ctypes.byref(ls_dn) if ls_dn is not None else None,
+            _ptr(y), _dtype_code(y.dtype), _ptr(workspace), workspace.numel(),
+            _stream(x.device))
+    if quant_type == "nf4":
+        _check(lib.moe_expert_forward(*args))
+    else:
+        _check(lib.moe_expert_forward_nbit(_qt(quant_type), *args))
     return y
 
 

@@ -59,10 +59,37 @@ QuantThresholds make_thresholds() {
   return th;
 }
 
-const QuantThresholds& thresholds() {
-  static const QuantThresholds th = make_thresholds();
+// fp4: thresholds between the 8 magnitude levels (codes 0..7); an exact tie
+// (a midpoint that is an fp32 value) goes to the even magnitude index.
+const float kLevelsFP4[16] = NF4MOE_FP4_LEVELS_INIT;
+
+QuantThresholds make_thresholds_fp4() {
+  QuantThresholds th;
+  for (int j = 0; j < 15; ++j) th.t[j] = INFINITY;
+  for (int j = 0; j < 7; ++j) {
+    const double mid = ((double)kLevelsFP4[j] + (double)kLevelsFP4[j + 1]) * 0.5;
+    float t = (float)mid;
+    if ((double)t > mid) t = std::nextafter(t, -INFINITY);
+    // x > t sends x to index j + 1; at an exact tie that must hold only when
+    // j + 1 is even
+    if ((double)t == mid && (j + 1) % 2 == 0) t = std::nextafter(t, -INFINITY);
+    th.t[j] = t;
+  }
+  th.qtype = kQtFP4;
   return th;
 }
+
+const QuantThresholds& thresholds(int qt) {
+  static const QuantThresholds nf4 = [] {
+    QuantThresholds t = make_thresholds();
+    t.qtype = kQtNF4;
+    return t;
+  }();
+  static const QuantThresholds fp4 = make_thresholds_fp4();
+  return qt == kQtFP4 ? fp4 : nf4;
+}
+
+bool valid_qtype(int qt) { return qt == kQtNF4 || qt == kQtFP4; }
 
 std::atomic<int> g_cu_cache[64];
 
@@ -202,6 +229,13 @@ int nf4moe_codebook(float* out16) {
   return ok();
 }
 
+int nbit_codebook(int quant_type, float* out16) {
+  if (out16 == nullptr) return fail(NF4MOE_EINVAL, "out16 is NULL");
+  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  std::memcpy(out16, quant_type == kQtFP4 ? kLevelsFP4 : kLevels, sizeof(kLevels));
+  return ok();
+}
+
 int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K) {
   if (E < 1 || N < 1 || K < 1) return fail(NF4MOE_EINVAL, "sizes must be positive");
   if (K % NF4MOE_BLOCKSIZE) return fail(NF4MOE_ESHAPE, "K=%lld is not a multiple of 64", (long long)K);
@@ -211,7 +245,7 @@ int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K) {
   return n / 2 + (n / NF4MOE_BLOCKSIZE) * 4;
 }
 
-int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
+static int quantize_impl(int qt, const void* w, int w_dtype, int64_t E, int64_t N,
                          int64_t K, int blocksize, uint8_t* packed,
                          float* absmax, int32_t* nonfinite_flag, void* stream) {
   if (w == nullptr || packed == nullptr || absmax == nullptr)
@@ -235,9 +269,24 @@ int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
   hipError_t err = launch_quantize(w, w_dtype, n, packed, absmax, nonfinite_flag,
-                                   thresholds(), cus, (hipStream_t)stream);
+                                   thresholds(qt), cus, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "quantize launch");
   return ok();
+}
+
+int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
+                         int64_t K, int blocksize, uint8_t* packed,
+                         float* absmax, int32_t* nonfinite_flag, void* stream) {
+  return quantize_impl(kQtNF4, w, w_dtype, E, N, K, blocksize, packed, absmax,
+                       nonfinite_flag, stream);
+}
+
+int nbit_quantize_experts(int quant_type, const void* w, int w_dtype, int64_t E,
+                          int64_t N, int64_t K, int blocksize, uint8_t* packed,
+                          float* absmax, int32_t* nonfinite_flag, void* stream) {
+  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  return quantize_impl(quant_type, w, w_dtype, E, N, K, blocksize, packed, absmax,
+                       nonfinite_flag, stream);
 }
 
 size_t moe_route_permute_workspace(int64_t T, int E, int k) {
@@ -288,7 +337,7 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
                        const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
                        const nf4moe_lora* lora, int epilogue,
                        const float* row_scale, const int32_t* scatter, void* out,
-                       int out_dtype, hipStream_t stream) {
+                       int out_dtype, int qt, hipStream_t stream) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
@@ -317,12 +366,13 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
   g.scatter = scatter;
   g.out = out;
   g.out_dtype = out_dtype;
+  g.qtype = qt;
   hipError_t err = launch_grouped_gemm(g, cus, stream);
   if (err != hipSuccess) return hip_fail(err, "grouped GEMM launch");
   return NF4MOE_OK;
 }
 
-int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
+static int gemm_impl(int qt, const void* a, int a_dtype, int64_t a_rows,
                      const int32_t* gather, int gather_div,
                      const uint8_t* packed, const float* absmax,
                      const int32_t* expert_offsets, int E, int64_t P,
@@ -363,10 +413,37 @@ int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
     return fail(NF4MOE_EINVAL, "misaligned buffer (a, packed and out need 16 bytes)");
   if (P == 0) return ok();
   st = gemm_common(a, a_dtype, a_rows, gather, gather_div, packed, absmax, expert_offsets,
-                   E, P, N, K, lora, epilogue, row_scale, scatter, out, out_dtype,
+                   E, P, N, K, lora, epilogue, row_scale, scatter, out, out_dtype, qt,
                    (hipStream_t)stream);
   if (st != NF4MOE_OK) return st;
   return ok();
+}
+
+int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
+                     const int32_t* gather, int gather_div,
+                     const uint8_t* packed, const float* absmax,
+                     const int32_t* expert_offsets, int E, int64_t P,
+                     int64_t N, int64_t K, const nf4moe_lora* lora,
+                     int epilogue, const float* row_scale,
+                     const int32_t* scatter, void* out, int out_dtype,
+                     void* stream) {
+  return gemm_impl(kQtNF4, a, a_dtype, a_rows, gather, gather_div, packed, absmax,
+                   expert_offsets, E, P, N, K, lora, epilogue, row_scale, scatter, out,
+                   out_dtype, stream);
+}
+
+int grouped_nbit_gemm(int quant_type, const void* a, int a_dtype, int64_t a_rows,
+                      const int32_t* gather, int gather_div,
+                      const uint8_t* packed, const float* absmax,
+                      const int32_t* expert_offsets, int E, int64_t P,
+                      int64_t N, int64_t K, const nf4moe_lora* lora,
+                      int epilogue, const float* row_scale,
+                      const int32_t* scatter, void* out, int out_dtype,
+                      void* stream) {
+  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  return gemm_impl(quant_type, a, a_dtype, a_rows, gather, gather_div, packed, absmax,
+                   expert_offsets, E, P, N, K, lora, epilogue, row_scale, scatter, out,
+                   out_dtype, stream);
 }
 
 size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k) {
@@ -390,7 +467,7 @@ int moe_expert_forward_routing(void* workspace, int64_t T, int H, int I, int E,
   return ok();
 }
 
-int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
+static int forward_impl(int qt, const void* x, int x_dtype, const float* router_logits,
                        int64_t T, int H, int I, int E, int k, int renormalize,
                        const uint8_t* gu_packed, const float* gu_absmax,
                        const uint8_t* dn_packed, const float* dn_absmax,
@@ -457,6 +534,7 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
     g.hbuf = ws + L.hbuf;
     g.y = y;
     g.y_dtype = y_dtype;
+    g.qtype = qt;
     hipError_t err = launch_decode(g, cus, s);
     if (err != hipSuccess) return hip_fail(err, "decode launch");
     return ok();
@@ -489,15 +567,40 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
   _Float16* o = (_Float16*)(ws + L.o);
   st = gemm_common(xa, NF4MOE_F16, T, r.sorted_pair, k, gu_packed, gu_absmax,
                    r.expert_offsets, E, P, 2 * (int64_t)I, H, gu_lora,
-                   NF4MOE_EPI_SWIGLU, nullptr, nullptr, h, NF4MOE_F16, s);
+                   NF4MOE_EPI_SWIGLU, nullptr, nullptr, h, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
   st = gemm_common(h, NF4MOE_F16, P, nullptr, 1, dn_packed, dn_absmax, r.expert_offsets,
                    E, P, H, I, dn_lora, NF4MOE_EPI_NONE, nullptr,
-                   r.sorted_pair, o, NF4MOE_F16, s);
+                   r.sorted_pair, o, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
   err = launch_combine(o, wts, T, k, H, y, y_dtype, cus, s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
   return ok();
+}
+
+int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
+                       int64_t T, int H, int I, int E, int k, int renormalize,
+                       const uint8_t* gu_packed, const float* gu_absmax,
+                       const uint8_t* dn_packed, const float* dn_absmax,
+                       const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora,
+                       void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  return forward_impl(kQtNF4, x, x_dtype, router_logits, T, H, I, E, k, renormalize,
+                      gu_packed, gu_absmax, dn_packed, dn_absmax, gu_lora, dn_lora, y,
+                      y_dtype, workspace, ws_bytes, stream);
+}
+
+int moe_expert_forward_nbit(int quant_type, const void* x, int x_dtype,
+                            const float* router_logits, int64_t T, int H, int I, int E,
+                            int k, int renormalize, const uint8_t* gu_packed,
+                            const float* gu_absmax, const uint8_t* dn_packed,
+                            const float* dn_absmax, const nf4moe_lora* gu_lora,
+                            const nf4moe_lora* dn_lora, void* y, int y_dtype,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  return forward_impl(quant_type, x, x_dtype, router_logits, T, H, I, E, k, renormalize,
+                      gu_packed, gu_absmax, dn_packed, dn_absmax, gu_lora, dn_lora, y,
+                      y_dtype, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

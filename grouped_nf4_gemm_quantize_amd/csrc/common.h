@@ -19,6 +19,21 @@
    0.0795803145f,  0.1609301418f,  0.2461122572f,  0.3379151225f,            \
    0.4407097399f,  0.5626168847f,  0.7229566574f,  1.0f}
 
+// fp4 storage mode: the e2m1 element values {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+// over 6 (the block's absmax maps to the largest), indexed by code = sign
+// bit << 3 | magnitude index; code 8 is -0.  Each value is the correctly
+// rounded fp32 quotient.
+#define NF4MOE_FP4_LEVELS_INIT                                                \
+  {0.0f,         0.5f / 6.0f,  1.0f / 6.0f,  1.5f / 6.0f,                     \
+   2.0f / 6.0f,  3.0f / 6.0f,  4.0f / 6.0f,  1.0f,                            \
+   -0.0f,        -0.5f / 6.0f, -1.0f / 6.0f, -1.5f / 6.0f,                    \
+   -2.0f / 6.0f, -3.0f / 6.0f, -4.0f / 6.0f, -1.0f}
+
+namespace nf4moe {
+constexpr int kQtNF4 = 0;
+constexpr int kQtFP4 = 1;
+}  // namespace nf4moe
+
 namespace nf4moe {
 
 constexpr int kBlock = 64;       // elements per absmax block

@@ -65,6 +65,7 @@
 namespace nf4moe {
 
 __constant__ float c_levels_gemm[16] = NF4MOE_LEVELS_INIT;
+__constant__ float c_levels_gemm_fp4[16] = NF4MOE_FP4_LEVELS_INIT;
 
 namespace {
 
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   const int g2 = lane >> 5;   // k half of the operands
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16x32 operand coordinates
 
-  lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm, tid, NTHREADS);
+  lut_fill<kCopies>(g_lut, g_lstage, g.qtype == kQtFP4 ? c_levels_gemm_fp4 : c_levels_gemm, tid, NTHREADS);
 
   // M-tile table from the offsets: thread t owns experts 2t, 2t + 1
   {

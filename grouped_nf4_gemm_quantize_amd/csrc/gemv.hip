@@ -31,6 +31,7 @@
 namespace nf4moe {
 
 __constant__ float c_levels_gemv[16] = NF4MOE_LEVELS_INIT;
+__constant__ float c_levels_gemv_fp4[16] = NF4MOE_FP4_LEVELS_INIT;
 
 namespace {
 constexpr int kCopies = 32;
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
       s_x[i0 + 3] = to_f16(xr[p].y >> 16, g.x_bf16);
     }
   }
-  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, kThreads);  // ends with a barrier
+  lut_fill<kCopies>(s_lut, s_stage, g.qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv, tid, kThreads);  // ends with a barrier
 
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
   _Float16* hout = reinterpret_cast<_Float16*>(g.hbuf);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
   const _Float16* hin = reinterpret_cast<const _Float16*>(g.hbuf);
   for (int i = tid * 8; i < k * I; i += kThreads * 8)
     *reinterpret_cast<u32x4*>(s_h + i) = *reinterpret_cast<const u32x4*>(hin + i);
-  lut_fill<kCopies>(s_lut, s_stage, c_levels_gemv, tid, kThreads);  // ends with a barrier
+  lut_fill<kCopies>(s_lut, s_stage, g.qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv, tid, kThreads);  // ends with a barrier
 
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
   for (; n < H; n += nw) {

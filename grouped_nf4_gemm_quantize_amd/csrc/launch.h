@@ -10,8 +10,12 @@ namespace nf4moe {
 // fp32 thresholds of the quantiser: t[j] is the largest fp32 value that is
 // <= the exact midpoint of levels j and j+1, so  xn > t[j]  <=>  xn lies
 // strictly above that midpoint (a tie goes to the lower level).
+// nf4: code = number of the 15 thresholds below x/absmax.  fp4: magnitude
+// index = number of the first 7 thresholds below |x/absmax|, code = sign
+// bit << 3 | index.
 struct QuantThresholds {
   float t[15];
+  int qtype;
 };
 
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t nelem,
@@ -68,6 +72,7 @@ struct GemmArgs {
   const int32_t* scatter;  // nullable
   void* out;
   int out_dtype;
+  int qtype;               // storage mode (kQtNF4 / kQtFP4)
 };
 
 constexpr int kGemmBM = 128;  // rows of an M-tile (one expert's rows only)
@@ -93,6 +98,7 @@ struct GemvArgs {
   void* hbuf;         // [k, I] fp16 h, already scaled by the routing weight
   void* y;            // [H]
   int y_dtype;
+  int qtype;          // storage mode of both stacks (kQtNF4 / kQtFP4)
 };
 
 hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream);

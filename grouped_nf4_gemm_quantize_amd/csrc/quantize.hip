@@ -1,4 +1,4 @@
-// NF4 blockwise quantiser for fused expert stacks.
+// NF4 (and fp4) blockwise quantiser for fused expert stacks.
 //
 // Experts4bit.from_float quantises the fused gate_up / down stacks to NF4
 // with one absmax per 64 elements (experts4bit-qlora 0.22.0 README,
@@ -16,7 +16,7 @@
 
 namespace nf4moe {
 
-template <bool kBF16>
+template <bool kBF16, bool kFP4>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const void* __restrict__ w, int64_t nblocks, uint8_t* __restrict__ packed,
     float* __restrict__ absmax, int32_t* __restrict__ nonfinite_flag,
@@ -64,12 +64,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     uint32_t codes[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t c = 7u;
+      uint32_t c = kFP4 ? 0u : 7u;  // all-zero block: the zero level (+0 for fp4)
       if (a != 0.f) {
         const float xn = x[i] / a;  // IEEE fp32 division (no fast-math)
         c = 0u;
+        if constexpr (kFP4) {
+          const float ax = fabsf(xn);
 #pragma unroll
-        for (int j = 0; j < 15; ++j) c += (xn > t[j]) ? 1u : 0u;
+          for (int j = 0; j < 7; ++j) c += (ax > t[j]) ? 1u : 0u;
+          c |= (xn < 0.f) ? 8u : 0u;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 15; ++j) c += (xn > t[j]) ? 1u : 0u;
+        }
       }
       codes[i] = c;
     }
@@ -93,12 +100,22 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t nelem,
   const int64_t cap = (int64_t)num_cus * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  if (w_dtype == kBF16)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)grid), dim3(256), 0,
-                       stream, w, nblocks, packed, absmax, flag, thr);
-  else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)grid), dim3(256), 0,
-                       stream, w, nblocks, packed, absmax, flag, thr);
+  const bool fp4 = thr.qtype == kQtFP4;
+  if (w_dtype == kBF16) {
+    if (fp4)
+      hipLaunchKernelGGL((quantize_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, w, nblocks, packed, absmax, flag, thr);
+    else
+      hipLaunchKernelGGL((quantize_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, w, nblocks, packed, absmax, flag, thr);
+  } else {
+    if (fp4)
+      hipLaunchKernelGGL((quantize_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, w, nblocks, packed, absmax, flag, thr);
+    else
+      hipLaunchKernelGGL((quantize_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, w, nblocks, packed, absmax, flag, thr);
+  }
   return hipGetLastError();
 }
 

@@ -220,6 +220,42 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
                        void* y, int y_dtype, void* workspace, size_t ws_bytes,
                        void* stream);
 
+/* ---- other 4-bit storage modes ---------------------------------------------
+ * ExpertsNbit stores the same fused stack at selectable precision; nf4 and
+ * fp4 are its two 4-bit packed modes, and nf4 reconstructs with less error
+ * than fp4 (0.22.0 README, "The problem").  These entry points take the mode
+ * first and are otherwise identical to the nf4 ones above (same packing, same
+ * absmax blocks, same kernels; only the 16 levels differ).
+ *   NF4MOE_QT_NF4  the NF4 levels of nf4moe_codebook;
+ *   NF4MOE_QT_FP4  e2m1 element values {0, .5, 1, 1.5, 2, 3, 4, 6} / 6 (the
+ *                  block's absmax maps to the largest), code = sign << 3 |
+ *                  magnitude index, code 8 = -0; quantiser: sign of
+ *                  x/absmax, nearest magnitude level (an exact tie goes to
+ *                  the even index), an all-zero block stores code 0.  The
+ *                  pages print no fp4 values; this is the OCP e2m1 format.
+ * An unknown mode returns NF4MOE_EINVAL. */
+#define NF4MOE_QT_NF4 0
+#define NF4MOE_QT_FP4 1
+int nbit_codebook(int quant_type, float* out16);  /* [host] levels by code */
+int nbit_quantize_experts(int quant_type, const void* w, int w_dtype, int64_t E,
+                          int64_t N, int64_t K, int blocksize, uint8_t* packed,
+                          float* absmax, int32_t* nonfinite_flag, void* stream);
+int grouped_nbit_gemm(int quant_type, const void* a, int a_dtype, int64_t a_rows,
+                      const int32_t* gather, int gather_div,
+                      const uint8_t* packed, const float* absmax,
+                      const int32_t* expert_offsets, int E, int64_t P,
+                      int64_t N, int64_t K, const nf4moe_lora* lora,
+                      int epilogue, const float* row_scale,
+                      const int32_t* scatter, void* out, int out_dtype,
+                      void* stream);
+int moe_expert_forward_nbit(int quant_type, const void* x, int x_dtype,
+                            const float* router_logits, int64_t T, int H, int I, int E,
+                            int k, int renormalize, const uint8_t* gu_packed,
+                            const float* gu_absmax, const uint8_t* dn_packed,
+                            const float* dn_absmax, const nf4moe_lora* gu_lora,
+                            const nf4moe_lora* dn_lora, void* y, int y_dtype,
+                            void* workspace, size_t ws_bytes, void* stream);
+
 /* Device-pointer views into a moe_expert_forward workspace (for inspection of
  * the routing a forward used; valid after the forward completes on its
  * stream).  Any out-pointer may be NULL.  Returns a negative status on bad

@@ -57,6 +57,30 @@ def test_codebook_bits_match_the_oracle(lib):
     assert lib.nf4moe_codebook(None) == -1
 
 
+def test_fp4_codebook_bits_match_the_oracle(lib):
+    buf = (ctypes.c_float * 16)()
+    assert lib.nbit_codebook(1, buf) == 0
+    got = np.array(list(buf), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.fp4_codebook().view(np.uint32))
+    assert lib.nbit_codebook(0, buf) == 0
+    got = np.array(list(buf), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+    assert lib.nbit_codebook(2, buf) == -1
+    assert lib.nbit_codebook(1, None) == -1
+
+
+def test_nbit_entry_points_reject_unknown_modes(lib):
+    assert lib.nbit_quantize_experts(7, FAKE, 0, 1, 1, 64, 64, FAKE, FAKE, None, None) == -1
+    assert "storage mode" in _last(lib)
+    assert lib.grouped_nbit_gemm(-1, FAKE, 2, 8, None, 1, FAKE, FAKE, FAKE, 1, 8, 64, 64,
+                                 None, 0, None, None, FAKE, 2, None) == -1
+    assert lib.moe_expert_forward_nbit(3, FAKE, 1, FAKE, 1, 64, 64, 8, 2, 1, FAKE, FAKE,
+                                       FAKE, FAKE, None, None, FAKE, 1, FAKE, 1 << 20,
+                                       None) == -1
+    # a known mode reaches the usual validation (blocksize)
+    assert lib.nbit_quantize_experts(1, FAKE, 0, 1, 1, 64, 32, FAKE, FAKE, None, None) == -3
+
+
 @pytest.mark.parametrize("E,N,K", [(128, 1536, 2048), (128, 2048, 768), (8, 256, 256),
                                    (64, 2048, 2048), (1, 16, 64)])
 def test_packed_bytes_matches_the_format(lib, E, N, K):

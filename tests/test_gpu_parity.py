@@ -525,3 +525,117 @@ def test_forward_full_size_sampled_tokens(gpu_lib, name):
     y, ref = _full_sampled(gpu_lib, name, n_tokens=1 if name == "decode" else 6)
     m = assert_parity(y, ref, what=name)
     print(name, m)
+
+
+# ------------------------------------------------- fp4 storage mode (4-bit)
+
+def _fp4_edge_case_stack():
+    rng = np.random.default_rng(321)
+    w = rng.standard_normal((3, 24, 192), dtype=np.float32) * np.float32(0.02)
+    w[0, 0, 0:64] = 0.0
+    w[0, 1, 64:128] = -0.0
+    w[0, 2, 0:64] = rng.standard_normal(64).astype(np.float32) * np.float32(1e-3)
+    w[0, 2, 3] = np.float32(-0.0)  # a negative zero inside a live block
+    q = oracle.fp4_codebook()
+    # magnitude midpoints (exact ties where representable) and neighbours
+    blk = [np.float32(1.0)]
+    for j in range(7):
+        m = (np.float64(q[j]) + np.float64(q[j + 1])) / 2
+        m32 = np.float32(m)
+        blk += [m32, np.nextafter(m32, np.float32(-2)), np.nextafter(m32, np.float32(2))]
+    blk = np.array(blk + [0.0] * (64 - len(blk)), dtype=np.float32)
+    w[1, 7, 64:128] = blk
+    w[1, 8, 0:64] = -blk
+    # exact level multiples with a power-of-two absmax
+    codes = rng.integers(0, 16, 64)
+    codes[0] = 7
+    w[2, 9, 128:192] = q[codes] * np.float32(0.5)
+    return w
+
+
+def test_fp4_quantize_bit_exact_edge_cases(gpu_lib):
+    w = _fp4_edge_case_stack()
+    p_ref, a_ref = oracle.quantize_blockwise(w, quant_type="fp4")
+    p, a = gpu_lib.quantize(gpu(w), quant_type="fp4")
+    assert np.array_equal(host(p), p_ref)
+    assert np.array_equal(host(a).view(np.uint32), a_ref.view(np.uint32))
+    # bf16 input and a config-sized slice
+    wb = synth.round_to_bf16(np.random.default_rng(8).standard_normal((2, 32, 256),
+                                                                      dtype=np.float32) * 0.03)
+    p_ref, a_ref = oracle.quantize_blockwise(wb, quant_type="fp4")
+    p, a = gpu_lib.quantize(gpu(wb, torch.bfloat16), quant_type="fp4")
+    assert np.array_equal(host(p), p_ref)
+    assert np.array_equal(host(a), a_ref)
+
+
+@pytest.mark.parametrize("swiglu,lora", [(False, False), (True, True)])
+def test_fp4_grouped_gemm_matches_oracle(gpu_lib, swiglu, lora):
+    rng = np.random.default_rng(200 + 2 * swiglu + lora)
+    E, N, K = 5, 640, 320
+    counts = [130, 1, 0, 77, 260]
+    P = sum(counts)
+    w = rng.standard_normal((E, N, K), dtype=np.float32) * np.float32(0.05)
+    packed, absmax = oracle.quantize_blockwise(w, quant_type="fp4")
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = rng.standard_normal((300, K)).astype(np.float16)
+    gather = rng.integers(0, 300 * 3, size=P).astype(np.int32)
+    lo = lo_ref = None
+    if lora:
+        r = 8
+        A = synth.round_to_bf16(rng.standard_normal((E, r, K), dtype=np.float32) * 0.05)
+        B = synth.round_to_bf16(rng.standard_normal((E, N, r), dtype=np.float32) * 0.05)
+        lo = (gpu(A, torch.bfloat16), gpu(B, torch.bfloat16), 2.0)
+        lo_ref = (A, B, 2.0)
+    out = gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                               gather=gpu(gather), gather_div=3, lora=lo, swiglu=swiglu,
+                               out_dtype=torch.float32, quant_type="fp4")
+    ref = oracle.grouped_gemm(a.astype(np.float64), packed, absmax, offsets, gather=gather,
+                              gather_div=3, lora=lo_ref, swiglu=swiglu, quant_type="fp4")
+    assert_parity(host(out), ref, fro_tol=2e-3, maxabs_tol=2e-2, what="fp4 grouped gemm",
+                  out_dtype="f32")
+
+
+def _fp4_stacks(cfg):
+    gu = synth.stack_weights(cfg, "gu")
+    dn = synth.stack_weights(cfg, "dn")
+    return (oracle.quantize_blockwise(gu, quant_type="fp4")
+            + oracle.quantize_blockwise(dn, quant_type="fp4"))
+
+
+@pytest.mark.parametrize("name,E", [("tiny", None), ("decode", 16)])
+def test_fp4_forward_matches_oracle(gpu_lib, name, E):
+    cfg = synth.config(name, E=E) if E else synth.config(name)
+    gp, ga, dp, da = _fp4_stacks(cfg)
+    x, lg = synth.activations(cfg), synth.router_logits(cfg)
+    y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gp), gpu(ga), gpu(dp),
+                            gpu(da), y_dtype=torch.float32, quant_type="fp4")
+    ref, _ = oracle.moe_forward(x, lg, cfg.k, gp, ga, dp, da, quant_type="fp4")
+    assert_parity(host(y), ref, 2e-3, 2e-2, what=f"fp4 forward {name}", out_dtype="f32")
+
+
+def test_fidelity_ordering_through_the_kernels(gpu_lib):
+    """The pages' ordering nf4 < fp4, end to end: GPU-quantised stacks of the
+    same weights run through the GPU layer; the nf4 output is closer to the
+    layer on the unquantised weights (oracle, fp64) than the fp4 output."""
+    cfg = synth.config("tiny")
+    gu = synth.stack_weights(cfg, "gu")
+    dn = synth.stack_weights(cfg, "dn")
+    x, lg = synth.activations(cfg), synth.router_logits(cfg)
+    # the layer on exact weights: the oracle's per-expert MLP with fp64 weights
+    ids, wts = oracle.route_topk(lg, cfg.k)
+    xs = x.astype(np.float64)
+    exact = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            e = int(ids[t, j])
+            o, _, _ = oracle.expert_mlp(xs[t:t + 1], gu[e].astype(np.float64),
+                                        dn[e].astype(np.float64))
+            exact[t] += wts[t, j] * o[0]
+    errs = {}
+    for qt in ("nf4", "fp4"):
+        gp, ga = gpu_lib.quantize(gpu(gu), quant_type=qt)
+        dp, da = gpu_lib.quantize(gpu(dn), quant_type=qt)
+        y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gp, ga, dp, da,
+                                y_dtype=torch.float32, quant_type=qt)
+        errs[qt] = float(np.linalg.norm(host(y) - exact) / np.linalg.norm(exact))
+    assert errs["nf4"] < errs["fp4"], errs
