@@ -58,3 +58,11 @@ from .moe import (  # noqa: F401
     moe_forward,
     moe_forward_tokens,
 )
+from .backward import (  # noqa: F401
+    silu_grad,
+    swiglu_backward,
+    grouped_dgrad,
+    expert_backward,
+    moe_backward,
+    moe_backward_tokens,
+)
