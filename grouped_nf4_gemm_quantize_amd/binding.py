@@ -17,7 +17,7 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnf4moe.so")
 
 F32, BF16, F16 = 0, 1, 2
-EPI_NONE, EPI_SWIGLU = 0, 1
+EPI_NONE, EPI_SWIGLU, EPI_SWIGLU_BWD = 0, 1, 2
 
 STATUS = {
     0: "NF4MOE_OK", -1: "NF4MOE_EINVAL", -2: "NF4MOE_ESHAPE", -3: "NF4MOE_EBLOCK",
@@ -43,6 +43,13 @@ _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
 _c_vp = ctypes.c_void_p
 _c_size = ctypes.c_size_t
+
+_DGRAD_ARGS = [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_int, _c_i64,
+               _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_int, _c_vp]
+_BACKWARD_ARGS = [_c_vp, _c_int, _c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int,
+                  _c_int, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.POINTER(LoraStruct),
+                  ctypes.POINTER(LoraStruct), _c_vp, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                  _c_vp, _c_size, _c_vp]
 
 _SIGNATURES = {
     "nf4moe_strerror": (ctypes.c_char_p, [_c_int]),
@@ -78,6 +85,11 @@ _SIGNATURES = {
                                          _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                          ctypes.POINTER(LoraStruct), ctypes.POINTER(LoraStruct),
                                          _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
+    "grouped_nf4_gemm_dgrad": (_c_int, _DGRAD_ARGS),
+    "grouped_nbit_gemm_dgrad": (_c_int, [_c_int] + _DGRAD_ARGS),
+    "moe_expert_backward_workspace": (_c_size, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "moe_expert_backward": (_c_int, _BACKWARD_ARGS),
+    "moe_expert_backward_nbit": (_c_int, [_c_int] + _BACKWARD_ARGS),
 }
 
 # storage modes of the nbit entry points (NF4MOE_QT_* in include/nf4moe.h)
@@ -292,3 +304,79 @@ def forward_routing(workspace, T: int, H: int, I: int, E: int, k: int):
                                              ctypes.byref(ids), ctypes.byref(w),
                                              ctypes.byref(sp), ctypes.byref(off)))
     return dict(ids=ids.value, w=w.value, sorted_pair=sp.value, offsets=off.value)
+
+
+def grouped_dgrad(a, packed, absmax, offsets, P: int, gather=None, gather_div: int = 1,
+                  g_pre=None, row_scale=None, scatter=None, out=None, out_dtype=None,
+                  out_rows: Optional[int] = None, quant_type: str = "nf4"):
+    """Grouped dgrad through the packed stack (see grouped_nf4_gemm_dgrad).
+
+    ``g_pre`` (the forward's [gate | up] pre-activation rows) selects the
+    SwiGLU-backward epilogue.  Returns ``out`` ([rows, K] or [rows, 2K]).
+    """
+    torch = _torch()
+    E, N, K2 = packed.shape
+    K = K2 * 2
+    n_out = 2 * K if g_pre is not None else K
+    if out is None:
+        rows = out_rows if out_rows is not None else P
+        out = torch.empty((rows, n_out), dtype=out_dtype or torch.float16, device=a.device)
+    lib = load()
+    args = (_ptr(a), _dtype_code(a.dtype), a.shape[0], _ptr(gather), gather_div, _ptr(packed),
+            _ptr(absmax), _ptr(offsets), E, P, N, K,
+            EPI_SWIGLU_BWD if g_pre is not None else EPI_NONE, _ptr(g_pre),
+            _dtype_code(g_pre.dtype) if g_pre is not None else F16, _ptr(row_scale),
+            _ptr(scatter), _ptr(out), _dtype_code(out.dtype), _stream(a.device))
+    if quant_type == "nf4":
+        _check(lib.grouped_nf4_gemm_dgrad(*args))
+    else:
+        _check(lib.grouped_nbit_gemm_dgrad(_qt(quant_type), *args))
+    return out
+
+
+def backward_workspace_bytes(T: int, H: int, I: int, E: int, k: int, r: int = 0) -> int:
+    return int(load().moe_expert_backward_workspace(T, H, I, E, k, r))
+
+
+def moe_backward(x, logits, dy, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
+                 gu_lora=None, dn_lora=None, renormalize: bool = True, dx=None,
+                 dx_dtype=None, workspace=None, quant_type: str = "nf4"):
+    """Layer backward (see moe_expert_backward in include/nf4moe.h).
+
+    Returns ``(dx, grads)`` where ``grads`` holds ``dA_gu``/``dB_gu`` and
+    ``dA_dn``/``dB_dn`` (fp32) for the adapters given.
+    """
+    torch = _torch()
+    T, H = x.shape
+    E = logits.shape[1]
+    I = dn_packed.shape[2] * 2
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, H), dtype=dx_dtype or torch.bfloat16, device=dev)
+    r = 0
+    grads = {}
+    if gu_lora is not None:
+        r = int(gu_lora[0].shape[1])
+        grads["dA_gu"] = torch.empty((E, r, H), dtype=torch.float32, device=dev)
+        grads["dB_gu"] = torch.empty((E, 2 * I, r), dtype=torch.float32, device=dev)
+    if dn_lora is not None:
+        r = int(dn_lora[0].shape[1])
+        grads["dA_dn"] = torch.empty((E, r, I), dtype=torch.float32, device=dev)
+        grads["dB_dn"] = torch.empty((E, H, r), dtype=torch.float32, device=dev)
+    lib = load()
+    ws_bytes = lib.moe_expert_backward_workspace(T, H, I, E, k, r)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ls_gu = make_lora(*gu_lora) if gu_lora is not None else None
+    ls_dn = make_lora(*dn_lora) if dn_lora is not None else None
+    args = (_ptr(x), _dtype_code(x.dtype), _ptr(logits), _ptr(dy), _dtype_code(dy.dtype), T, H,
+            I, E, k, int(bool(renormalize)), _ptr(gu_packed), _ptr(gu_absmax), _ptr(dn_packed),
+            _ptr(dn_absmax), ctypes.byref(ls_gu) if ls_gu is not None else None,
+            ctypes.byref(ls_dn) if ls_dn is not None else None, _ptr(dx), _dtype_code(dx.dtype),
+            _ptr(grads.get("dA_gu")), _ptr(grads.get("dB_gu")), _ptr(grads.get("dA_dn")),
+            _ptr(grads.get("dB_dn")), _ptr(workspace), workspace.numel(), _stream(dev))
+    if quant_type == "nf4":
+        _check(lib.moe_expert_backward(*args))
+    else:
+        _check(lib.moe_expert_backward_nbit(_qt(quant_type), *args))
+    return dx, grads

@@ -603,4 +603,390 @@ int moe_expert_forward_nbit(int quant_type, const void* x, int x_dtype,
                       y_dtype, workspace, ws_bytes, stream);
 }
 
+// ---- grouped dgrad ------------------------------------------------------
+
+static int dgrad_common(const void* a, int a_dtype, int64_t a_rows, const int32_t* gather,
+                        int gather_div, const uint8_t* packed, const float* absmax,
+                        const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
+                        int epilogue, const void* g_pre, int g_dtype, const float* row_scale,
+                        const int32_t* scatter, const float* lora_v, const nf4moe_lora* lora,
+                        void* out, int out_dtype, int qt, hipStream_t stream) {
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != NF4MOE_OK) return st;
+  DgradArgs d{};
+  d.a = a;
+  d.a_rows = a_rows;
+  d.a_bf16 = a_dtype == NF4MOE_BF16;
+  d.gather = gather;
+  d.gather_div = gather ? gather_div : 1;
+  d.packed = packed;
+  d.absmax = absmax;
+  d.offsets = expert_offsets;
+  d.E = E;
+  d.P = P;
+  d.N = (int)N;
+  d.K = (int)K;
+  d.row_scale = row_scale;
+  d.scatter = scatter;
+  d.epilogue = epilogue == NF4MOE_EPI_SWIGLU_BWD ? kDgradEpiSwigluBwd : kDgradEpiNone;
+  d.g = g_pre;
+  d.g_bf16 = g_dtype == NF4MOE_BF16;
+  if (lora_v != nullptr && lora != nullptr) {
+    d.lora_v = lora_v;
+    d.lora_a = lora->A;
+    d.lora_r = lora->r;
+    d.lora_scale = lora->scale;
+    d.lora_bf16 = lora->dtype == NF4MOE_BF16;
+  }
+  d.out = out;
+  d.out_dtype = out_dtype;
+  d.qtype = qt;
+  hipError_t err = launch_grouped_dgrad(d, cus, stream);
+  if (err != hipSuccess) return hip_fail(err, "grouped dgrad launch");
+  return NF4MOE_OK;
+}
+
+static int dgrad_impl(int qt, const void* a, int a_dtype, int64_t a_rows,
+                      const int32_t* gather, int gather_div, const uint8_t* packed,
+                      const float* absmax, const int32_t* expert_offsets, int E, int64_t P,
+                      int64_t N, int64_t K, int epilogue, const void* g_pre, int g_dtype,
+                      const float* row_scale, const int32_t* scatter, void* out,
+                      int out_dtype, void* stream) {
+  if (a == nullptr || packed == nullptr || absmax == nullptr || expert_offsets == nullptr ||
+      out == nullptr)
+    return fail(NF4MOE_EINVAL, "a, packed, absmax, expert_offsets and out must be non-null");
+  if (E < 1 || E > NF4MOE_MAX_EXPERTS)
+    return fail(E < 1 ? NF4MOE_EINVAL : NF4MOE_ESHAPE, "E=%d outside [1, %d]", E,
+                NF4MOE_MAX_EXPERTS);
+  if (P < 0 || a_rows < 0) return fail(NF4MOE_EINVAL, "P and a_rows must be >= 0");
+  if (N < 64 || K < 64) return fail(NF4MOE_EINVAL, "N >= 64 and K >= 64 required");
+  if (N % 64 || K % 64)
+    return fail(NF4MOE_ESHAPE, "N=%lld and K=%lld must be multiples of 64", (long long)N,
+                (long long)K);
+  if (epilogue != NF4MOE_EPI_NONE && epilogue != NF4MOE_EPI_SWIGLU_BWD)
+    return fail(NF4MOE_EINVAL, "unknown dgrad epilogue %d", epilogue);
+  if (epilogue == NF4MOE_EPI_SWIGLU_BWD) {
+    if (g_pre == nullptr) return fail(NF4MOE_EINVAL, "the SwiGLU backward needs g_pre");
+    if (g_dtype != NF4MOE_F16 && g_dtype != NF4MOE_BF16)
+      return fail(NF4MOE_EDTYPE, "g_dtype=%d: the pre-activation must be F16 or BF16", g_dtype);
+    if (!aligned(g_pre, 16)) return fail(NF4MOE_EINVAL, "g_pre must be 16-byte aligned");
+  }
+  if (a_dtype != NF4MOE_F16 && a_dtype != NF4MOE_BF16)
+    return fail(NF4MOE_EDTYPE, "a_dtype=%d: gradient rows must be F16 or BF16", a_dtype);
+  if (out_dtype != NF4MOE_F16 && out_dtype != NF4MOE_BF16 && out_dtype != NF4MOE_F32)
+    return fail(NF4MOE_EDTYPE, "out_dtype=%d unsupported", out_dtype);
+  if (gather != nullptr && gather_div < 1) return fail(NF4MOE_EINVAL, "gather_div must be >= 1");
+  if (P >= INT32_MAX || N > INT32_MAX / 2 || K > INT32_MAX / 4)
+    return fail(NF4MOE_EOVERFLOW, "P, N or K too large for 32-bit row indexing");
+  if (a_rows * N * 2 > (int64_t)UINT32_MAX || N * K / 2 > (int64_t)UINT32_MAX)
+    return fail(NF4MOE_EOVERFLOW, "gradient rows or one expert's stack exceed 4 GiB");
+  if (!aligned(a, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(out, 16))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (a, packed and out need 16 bytes)");
+  if (P == 0) return ok();
+  int st = dgrad_common(a, a_dtype, a_rows, gather, gather_div, packed, absmax,
+                        expert_offsets, E, P, N, K, epilogue, g_pre, g_dtype, row_scale,
+                        scatter, nullptr, nullptr, out, out_dtype, qt, (hipStream_t)stream);
+  if (st != NF4MOE_OK) return st;
+  return ok();
+}
+
+int grouped_nf4_gemm_dgrad(const void* a, int a_dtype, int64_t a_rows, const int32_t* gather,
+                           int gather_div, const uint8_t* packed, const float* absmax,
+                           const int32_t* expert_offsets, int E, int64_t P, int64_t N,
+                           int64_t K, int epilogue, const void* g_pre, int g_dtype,
+                           const float* row_scale, const int32_t* scatter, void* out,
+                           int out_dtype, void* stream) {
+  return dgrad_impl(kQtNF4, a, a_dtype, a_rows, gather, gather_div, packed, absmax,
+                    expert_offsets, E, P, N, K, epilogue, g_pre, g_dtype, row_scale, scatter,
+                    out, out_dtype, stream);
+}
+
+int grouped_nbit_gemm_dgrad(int quant_type, const void* a, int a_dtype, int64_t a_rows,
+                            const int32_t* gather, int gather_div, const uint8_t* packed,
+                            const float* absmax, const int32_t* expert_offsets, int E,
+                            int64_t P, int64_t N, int64_t K, int epilogue, const void* g_pre,
+                            int g_dtype, const float* row_scale, const int32_t* scatter,
+                            void* out, int out_dtype, void* stream) {
+  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  return dgrad_impl(quant_type, a, a_dtype, a_rows, gather, gather_div, packed, absmax,
+                    expert_offsets, E, P, N, K, epilogue, g_pre, g_dtype, row_scale, scatter,
+                    out, out_dtype, stream);
+}
+
+// ---- layer backward -----------------------------------------------------
+
+struct BwdLayout {
+  FwdLayout f;  // routing regions and x16 (h and o unused)
+  size_t g, dg, dxp, h, u_gu, v_gu, u_dn, v_dn, bt_gu, bt_dn, part, total;
+};
+
+static BwdLayout bwd_layout(int64_t T, int H, int I, int E, int k, int r) {
+  BwdLayout L;
+  L.f = fwd_layout(T, H, I, E, k);
+  const size_t P = (size_t)T * k;
+  size_t o = L.f.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.g = take(P * 2 * (size_t)I * 2);
+  L.dg = take(P * 2 * (size_t)I * 2);
+  L.dxp = take(P * (size_t)H * 2);
+  const size_t rr = (size_t)(r > 0 ? r : 0);
+  L.h = take(rr ? P * (size_t)I * 2 : 0);
+  L.u_gu = take(P * rr * 4);
+  L.v_gu = take(P * rr * 4);
+  L.u_dn = take(P * rr * 4);
+  L.v_dn = take(P * rr * 4);
+  L.bt_gu = take((size_t)E * rr * 2 * I * 2);
+  L.bt_dn = take((size_t)E * rr * H * 2);
+  const size_t cmax = (size_t)(H > 2 * I ? H : 2 * I);
+  L.part = take(rr ? ((P + 127) / 128 + (size_t)E) * rr * cmax * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+size_t moe_expert_backward_workspace(int64_t T, int H, int I, int E, int k, int r) {
+  if (T < 1 || H < 1 || I < 1 || E < 1 || E > NF4MOE_MAX_EXPERTS || k < 1 || r < 0 ||
+      r > NF4MOE_MAX_LORA_R)
+    return 0;
+  return bwd_layout(T, H, I, E, k, r).total;
+}
+
+static int lora_wgrad(const void* m, int m_bf16, const int32_t* gather, int gather_div,
+                      const float* rs, const int32_t* rs_idx, const float* q, int r,
+                      const int32_t* offsets, int E, int64_t P, int C, float* part, float* z,
+                      float scale, int rank_major, int cus, hipStream_t s) {
+  LoraGradArgs a{};
+  a.m = m;
+  a.m_bf16 = m_bf16;
+  a.gather = gather;
+  a.gather_div = gather ? gather_div : 1;
+  a.rs = rs;
+  a.rs_idx = rs_idx;
+  a.q = q;
+  a.r = r;
+  a.offsets = offsets;
+  a.E = E;
+  a.P = P;
+  a.C = C;
+  a.part = part;
+  a.z = z;
+  a.scale = scale;
+  hipError_t err = launch_lora_wgrad(a, rank_major, cus, s);
+  if (err != hipSuccess) return hip_fail(err, "LoRA weight-gradient launch");
+  return NF4MOE_OK;
+}
+
+static int lora_proj(const void* m, int m_bf16, const int32_t* gather, int gather_div,
+                     const int32_t* offsets, int E, int64_t P, int C, const void* w,
+                     int w_bf16, int r, float* out, hipStream_t s) {
+  LoraProjArgs a{};
+  a.m = m;
+  a.m_bf16 = m_bf16;
+  a.gather = gather;
+  a.gather_div = gather ? gather_div : 1;
+  a.offsets = offsets;
+  a.E = E;
+  a.P = P;
+  a.C = C;
+  a.w = w;
+  a.w_bf16 = w_bf16;
+  a.r = r;
+  a.out = out;
+  hipError_t err = launch_lora_rowproj(a, s);
+  if (err != hipSuccess) return hip_fail(err, "LoRA projection launch");
+  return NF4MOE_OK;
+}
+
+static int backward_impl(int qt, const void* x, int x_dtype, const float* router_logits,
+                         const void* dy, int dy_dtype, int64_t T, int H, int I, int E, int k,
+                         int renormalize, const uint8_t* gu_packed, const float* gu_absmax,
+                         const uint8_t* dn_packed, const float* dn_absmax,
+                         const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora, void* dx,
+                         int dx_dtype, float* d_gu_A, float* d_gu_B, float* d_dn_A,
+                         float* d_dn_B, void* workspace, size_t ws_bytes, void* stream) {
+  if (x == nullptr || router_logits == nullptr || dy == nullptr || gu_packed == nullptr ||
+      gu_absmax == nullptr || dn_packed == nullptr || dn_absmax == nullptr || dx == nullptr)
+    return fail(NF4MOE_EINVAL, "x, router_logits, dy, the four stack buffers and dx must be non-null");
+  int st = check_route_shape(T, E, k);
+  if (st != NF4MOE_OK) return st;
+  if (H < 64 || I < 64) return fail(NF4MOE_EINVAL, "H and I must be >= 64");
+  if (H % 64 || I % 64)
+    return fail(NF4MOE_ESHAPE, "H=%d and I=%d must be multiples of 64", H, I);
+  if (renormalize != 0 && renormalize != 1)
+    return fail(NF4MOE_EINVAL, "renormalize must be 0 or 1");
+  if (x_dtype != NF4MOE_BF16 && x_dtype != NF4MOE_F16)
+    return fail(NF4MOE_EDTYPE, "x_dtype=%d: activations must be BF16 or F16", x_dtype);
+  if (dy_dtype != NF4MOE_BF16 && dy_dtype != NF4MOE_F16)
+    return fail(NF4MOE_EDTYPE, "dy_dtype=%d: the output gradient must be BF16 or F16", dy_dtype);
+  if (dx_dtype != NF4MOE_BF16 && dx_dtype != NF4MOE_F16 && dx_dtype != NF4MOE_F32)
+    return fail(NF4MOE_EDTYPE, "dx_dtype=%d unsupported", dx_dtype);
+  st = check_lora(gu_lora, "gu_lora");
+  if (st != NF4MOE_OK) return st;
+  st = check_lora(dn_lora, "dn_lora");
+  if (st != NF4MOE_OK) return st;
+  if (gu_lora && (d_gu_A == nullptr || d_gu_B == nullptr))
+    return fail(NF4MOE_EINVAL, "gu_lora given: d_gu_A and d_gu_B must be non-null");
+  if (dn_lora && (d_dn_A == nullptr || d_dn_B == nullptr))
+    return fail(NF4MOE_EINVAL, "dn_lora given: d_dn_A and d_dn_B must be non-null");
+  if (gu_lora && dn_lora && gu_lora->r != dn_lora->r)
+    return fail(NF4MOE_EINVAL, "gu_lora and dn_lora must have the same rank");
+  const int r = gu_lora ? gu_lora->r : (dn_lora ? dn_lora->r : 0);
+  const int64_t P = T * k;
+  if (T * H * 2 > (int64_t)UINT32_MAX || P * 2 * (int64_t)I * 2 > (int64_t)UINT32_MAX ||
+      2 * (int64_t)I * H / 2 > (int64_t)UINT32_MAX)
+    return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(gu_packed, 16) ||
+      !aligned(dn_packed, 16) || !aligned(gu_absmax, 4) || !aligned(dn_absmax, 4) ||
+      !aligned(dx, 16))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (x, dy, dx and packed stacks need 16 bytes)");
+  const BwdLayout L = bwd_layout(T, H, I, E, k, r);
+  if (workspace == nullptr || ws_bytes < L.total)
+    return fail(NF4MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? ws_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(NF4MOE_EINVAL, "workspace must be 256-byte aligned");
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != NF4MOE_OK) return st;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+
+  // 1. routing (recomputed from the same logits), x in fp16
+  RouteArgs ra{};
+  ra.logits = router_logits;
+  ra.T = T;
+  ra.E = E;
+  ra.k = k;
+  ra.renormalize = renormalize;
+  ra.topk_ids = (int32_t*)(ws + L.f.ids);
+  ra.topk_w = (float*)(ws + L.f.w);
+  ra.sorted_pair = (int32_t*)(ws + L.f.sorted);
+  ra.pair_pos = (int32_t*)(ws + L.f.pos);
+  ra.expert_offsets = (int32_t*)(ws + L.f.offsets);
+  ra.chunk_masks = (uint32_t*)(ws + L.f.route + L.f.r.masks);
+  ra.chunk_base = (int32_t*)(ws + L.f.route + L.f.r.base);
+  const bool conv = x_dtype == NF4MOE_BF16;
+  ra.x_in = x;
+  ra.x_bf16 = conv ? 1 : 0;
+  ra.x16 = conv ? (_Float16*)(ws + L.f.x16) : nullptr;
+  ra.H = H;
+  ra.num_cus = cus;
+  hipError_t err = launch_route(ra, s);
+  if (err != hipSuccess) return hip_fail(err, "route launch");
+  const void* xa = conv ? (const void*)(ws + L.f.x16) : x;
+  const int32_t* sorted = ra.sorted_pair;
+  const int32_t* offs = ra.expert_offsets;
+  const float* wts = ra.topk_w;
+  _Float16* G = (_Float16*)(ws + L.g);
+  _Float16* dG = (_Float16*)(ws + L.dg);
+  _Float16* dXp = (_Float16*)(ws + L.dxp);
+  _Float16* hbuf = (_Float16*)(ws + L.h);
+  float* u_gu = (float*)(ws + L.u_gu);
+  float* v_gu = (float*)(ws + L.v_gu);
+  float* u_dn = (float*)(ws + L.u_dn);
+  float* v_dn = (float*)(ws + L.v_dn);
+  _Float16* bt_gu = (_Float16*)(ws + L.bt_gu);
+  _Float16* bt_dn = (_Float16*)(ws + L.bt_dn);
+  float* part = (float*)(ws + L.part);
+  const int dy_bf16 = dy_dtype == NF4MOE_BF16;
+
+  // 2. recompute the gate_up pre-activation G = x W_gu^T (+ LoRA), fp16
+  st = gemm_common(xa, NF4MOE_F16, T, sorted, k, gu_packed, gu_absmax, offs, E, P,
+                   2 * (int64_t)I, H, gu_lora, NF4MOE_EPI_NONE, nullptr, nullptr, G,
+                   NF4MOE_F16, qt, s);
+  if (st != NF4MOE_OK) return st;
+
+  // 3. down adapter: h, v' = dy B_dn (without the routing weight), u = h A_dn^T
+  if (dn_lora) {
+    err = launch_swiglu_rows(G, P, I, hbuf, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "SwiGLU launch");
+    err = launch_lora_transpose(dn_lora->B, dn_lora->dtype == NF4MOE_BF16, E, H, r, bt_dn, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "LoRA transpose launch");
+    st = lora_proj(dy, dy_bf16, sorted, k, offs, E, P, H, bt_dn, 0, r, v_dn, s);
+    if (st != NF4MOE_OK) return st;
+    st = lora_proj(hbuf, 0, nullptr, 1, offs, E, P, I, dn_lora->A,
+                   dn_lora->dtype == NF4MOE_BF16, r, u_dn, s);
+    if (st != NF4MOE_OK) return st;
+  }
+
+  // 4. dG = SwiGLU backward of (w * dy_t) W_dn (+ LoRA), fp16
+  st = dgrad_common(dy, dy_dtype, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
+                    NF4MOE_EPI_SWIGLU_BWD, G, NF4MOE_F16, wts, nullptr,
+                    dn_lora ? v_dn : nullptr, dn_lora, dG, NF4MOE_F16, qt, s);
+  if (st != NF4MOE_OK) return st;
+
+  // 5. down adapter gradients
+  if (dn_lora) {
+    st = lora_wgrad(dy, dy_bf16, sorted, k, wts, sorted, u_dn, r, offs, E, P, H, part, d_dn_B,
+                    dn_lora->scale, 0, cus, s);
+    if (st != NF4MOE_OK) return st;
+    st = lora_wgrad(hbuf, 0, nullptr, 1, wts, sorted, v_dn, r, offs, E, P, I, part, d_dn_A,
+                    dn_lora->scale, 1, cus, s);
+    if (st != NF4MOE_OK) return st;
+  }
+
+  // 6. gate_up adapter projections: u = x A_gu^T, v = dG B_gu
+  if (gu_lora) {
+    err = launch_lora_transpose(gu_lora->B, gu_lora->dtype == NF4MOE_BF16, E, 2 * I, r, bt_gu,
+                                cus, s);
+    if (err != hipSuccess) return hip_fail(err, "LoRA transpose launch");
+    st = lora_proj(xa, 0, sorted, k, offs, E, P, H, gu_lora->A, gu_lora->dtype == NF4MOE_BF16,
+                   r, u_gu, s);
+    if (st != NF4MOE_OK) return st;
+    st = lora_proj(dG, 0, nullptr, 1, offs, E, P, 2 * I, bt_gu, 0, r, v_gu, s);
+    if (st != NF4MOE_OK) return st;
+  }
+
+  // 7. per-pair input gradients dG W_gu (+ LoRA) in pair order, then the sum
+  //    over each token's k pairs
+  st = dgrad_common(dG, NF4MOE_F16, P, nullptr, 1, gu_packed, gu_absmax, offs, E, P,
+                    2 * (int64_t)I, H, NF4MOE_EPI_NONE, nullptr, 0, nullptr, sorted,
+                    gu_lora ? v_gu : nullptr, gu_lora, dXp, NF4MOE_F16, qt, s);
+  if (st != NF4MOE_OK) return st;
+  err = launch_combine(dXp, nullptr, T, k, H, dx, dx_dtype, cus, s);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+
+  // 8. gate_up adapter gradients
+  if (gu_lora) {
+    st = lora_wgrad(dG, 0, nullptr, 1, nullptr, nullptr, u_gu, r, offs, E, P, 2 * I, part,
+                    d_gu_B, gu_lora->scale, 0, cus, s);
+    if (st != NF4MOE_OK) return st;
+    st = lora_wgrad(xa, 0, sorted, k, nullptr, nullptr, v_gu, r, offs, E, P, H, part, d_gu_A,
+                    gu_lora->scale, 1, cus, s);
+    if (st != NF4MOE_OK) return st;
+  }
+  return ok();
+}
+
+int moe_expert_backward(const void* x, int x_dtype, const float* router_logits, const void* dy,
+                        int dy_dtype, int64_t T, int H, int I, int E, int k, int renormalize,
+                        const uint8_t* gu_packed, const float* gu_absmax,
+                        const uint8_t* dn_packed, const float* dn_absmax,
+                        const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora, void* dx,
+                        int dx_dtype, float* d_gu_A, float* d_gu_B, float* d_dn_A,
+                        float* d_dn_B, void* workspace, size_t ws_bytes, void* stream) {
+  return backward_impl(kQtNF4, x, x_dtype, router_logits, dy, dy_dtype, T, H, I, E, k,
+                       renormalize, gu_packed, gu_absmax, dn_packed, dn_absmax, gu_lora,
+                       dn_lora, dx, dx_dtype, d_gu_A, d_gu_B, d_dn_A, d_dn_B, workspace,
+                       ws_bytes, stream);
+}
+
+int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
+                             const float* router_logits, const void* dy, int dy_dtype,
+                             int64_t T, int H, int I, int E, int k, int renormalize,
+                             const uint8_t* gu_packed, const float* gu_absmax,
+                             const uint8_t* dn_packed, const float* dn_absmax,
+                             const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora, void* dx,
+                             int dx_dtype, float* d_gu_A, float* d_gu_B, float* d_dn_A,
+                             float* d_dn_B, void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  return backward_impl(quant_type, x, x_dtype, router_logits, dy, dy_dtype, T, H, I, E, k,
+                       renormalize, gu_packed, gu_absmax, dn_packed, dn_absmax, gu_lora,
+                       dn_lora, dx, dx_dtype, d_gu_A, d_gu_B, d_dn_A, d_dn_B, workspace,
+                       ws_bytes, stream);
+}
+
 }  // extern "C"

@@ -61,6 +61,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mfma_common.h"
 
 namespace nf4moe {
 
@@ -87,9 +88,6 @@ constexpr int BPAIR = BN * BK;                       // 512 rows x 64 B = 32768 
 constexpr int RING = OFF_BR + 2 * BPAIR;             // 102400 B
 constexpr int kAbsGroup = 4;                   // steps of absmax per copy (16 B per row)
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 }  // namespace
 
 __shared__ __attribute__((aligned(16))) char g_ring[RING];
@@ -110,89 +108,6 @@ namespace {
 constexpr int OFF_U = RING - BM * kMaxLoraR * 2;
 __device__ __forceinline__ _Float16* u_buf() {
   return reinterpret_cast<_Float16*>(g_ring + OFF_U);
-}
-
-// ---- buffer resources and the direct-to-LDS copies -------------------------
-
-// Raw buffer resource over [base, base + bytes): stride 0, offset-addressed.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)p);
-}
-
-// Lane i copies 16 (resp. 4) bytes from rsrc + voff + soff to LDS address
-// lds + 16 i (resp. 4 i).  M0 carries the LDS base; one wait state separates
-// its write from the load.  The kernel uses M0 for nothing else.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory operations are pending
-// and its LDS operations are done, then meet the other waves.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// ---- small helpers ---------------------------------------------------------
-
-template <int kOut>
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
-  if constexpr (kOut == kF32) {
-    reinterpret_cast<float*>(out)[idx] = v;
-  } else if constexpr (kOut == kBF16) {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(v);
-  } else {
-    reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
-  }
-}
-
-// Four consecutive output values -> one 8-byte (16-byte for fp32) LDS write.
-template <int kOut>
-__device__ __forceinline__ void stage_out4(char* p, const float (&v)[4]) {
-  if constexpr (kOut == kF32) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-  } else if constexpr (kOut == kBF16) {
-    *reinterpret_cast<u32x2*>(p) =
-        u32x2{(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
-              (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
-  } else {
-    *reinterpret_cast<u32x2*>(p) = u32x2{pack_half2((_Float16)v[0], (_Float16)v[1]),
-                                         pack_half2((_Float16)v[2], (_Float16)v[3])};
-  }
-}
-
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
-  u32x4 o;
-  o.x = pack_half2((_Float16)bf16_bits_to_f32(v.x & 0xffffu), (_Float16)bf16_bits_to_f32(v.x >> 16));
-  o.y = pack_half2((_Float16)bf16_bits_to_f32(v.y & 0xffffu), (_Float16)bf16_bits_to_f32(v.y >> 16));
-  o.z = pack_half2((_Float16)bf16_bits_to_f32(v.z & 0xffffu), (_Float16)bf16_bits_to_f32(v.z >> 16));
-  o.w = pack_half2((_Float16)bf16_bits_to_f32(v.w & 0xffffu), (_Float16)bf16_bits_to_f32(v.w >> 16));
-  return o;
-}
-
-__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
-
-__device__ __forceinline__ float silu_f(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 __device__ __forceinline__ uint32_t lut_read(uint32_t addr) {
@@ -447,37 +362,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
 
   lut_fill<kCopies>(g_lut, g_lstage, g.qtype == kQtFP4 ? c_levels_gemm_fp4 : c_levels_gemm, tid, NTHREADS);
 
-  // M-tile table from the offsets: thread t owns experts 2t, 2t + 1
-  {
-    constexpr int kPer = kMaxExperts / NTHREADS;
-    int32_t cnt[kPer];
-    int32_t local = 0;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int ex = tid * kPer + u;
-      cnt[u] = 0;
-      if (ex < g.E) cnt[u] = (g.offsets[ex + 1] - g.offsets[ex] + BM - 1) / BM;
-      local += cnt[u];
-    }
-    int32_t incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) g_wsum[wave] = incl;
-    __syncthreads();
-    int32_t run = incl - local;
-    for (int w = 0; w < wave; ++w) run += g_wsum[w];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int ex = tid * kPer + u;
-      if (ex < g.E) g_tiles[ex] = run;
-      run += cnt[u];
-    }
-    if (tid == NTHREADS - 1) g_tiles[g.E] = run;
-  }
-  __syncthreads();
+  build_tile_table<NTHREADS, BM>(g.offsets, g.E, g_tiles, g_wsum, tid);
 
   const int N = g.N;
   const int K = g.K;

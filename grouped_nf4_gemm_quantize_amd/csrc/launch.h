@@ -103,4 +103,81 @@ struct GemvArgs {
 
 hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream);
 
+// Grouped dgrad: out[i, :K] = row_scale * (a[src(i), :N] . W_e [N, K]
+// (+ lora_scale * v[i, :r] . A_e[:r, :K])), contracting over the stack rows.
+constexpr int kDgradEpiNone = 0;
+constexpr int kDgradEpiSwigluBwd = 1;  // out = [dh*up*silu'(gate) | dh*silu(gate)], 2K cols
+
+struct DgradArgs {
+  const void* a;           // [a_rows, N] f16/bf16
+  int64_t a_rows;
+  int a_bf16;
+  const int32_t* gather;   // nullable: src(i) = gather[i] / gather_div
+  int gather_div;
+  const uint8_t* packed;   // [E, N, K/2]
+  const float* absmax;     // [E, N, K/64]
+  const int32_t* offsets;  // [E+1]
+  int E;
+  int64_t P;
+  int N;                   // stack rows = contraction
+  int K;                   // output columns
+  const float* row_scale;  // nullable, row i scaled by row_scale[gather ? gather[i] : i]
+  const int32_t* scatter;  // nullable: output row of row i
+  int epilogue;
+  const void* g;           // SwiGLU backward: pre-activation rows [P, 2K] (row i)
+  int g_bf16;
+  const float* lora_v;     // nullable [P, r] fp32 (row i)
+  const void* lora_a;      // [E, r, K]
+  int lora_r;
+  float lora_scale;
+  int lora_bf16;
+  void* out;
+  int out_dtype;
+  int qtype;
+};
+
+hipError_t launch_grouped_dgrad(const DgradArgs& g, int num_cus, hipStream_t stream);
+
+// Rank-r row projections: out[i, j] = sum_c m[src(i), c] * w[e(i), j, c].
+struct LoraProjArgs {
+  const void* m;           // [rows, C] f16/bf16
+  int m_bf16;
+  const int32_t* gather;   // nullable: src(i) = gather[i] / gather_div
+  int gather_div;
+  const int32_t* offsets;  // [E+1]
+  int E;
+  int64_t P;
+  int C;
+  const void* w;           // [E, r, C] f16/bf16
+  int w_bf16;
+  int r;
+  float* out;              // [P, r]
+};
+
+// Adapter weight gradient: z[e] = scale * sum_i rs(i) q[i, :] (x) m[src(i), :].
+struct LoraGradArgs {
+  const void* m;           // [rows, C] f16/bf16
+  int m_bf16;
+  const int32_t* gather;
+  int gather_div;
+  const float* rs;         // nullable row scale, rs[rs_idx ? rs_idx[i] : i]
+  const int32_t* rs_idx;
+  const float* q;          // [P, r]
+  int r;
+  const int32_t* offsets;
+  int E;
+  int64_t P;
+  int C;
+  float* part;             // [(P / 128 + E), r, C] partials
+  float* z;                // [E, r, C] or [E, C, r]
+  float scale;
+};
+
+hipError_t launch_swiglu_rows(const _Float16* g, int64_t P, int I, _Float16* h, int num_cus,
+                              hipStream_t s);
+hipError_t launch_lora_transpose(const void* b, int b_bf16, int E, int C, int r, _Float16* bt,
+                                 int num_cus, hipStream_t s);
+hipError_t launch_lora_rowproj(const LoraProjArgs& a, hipStream_t s);
+hipError_t launch_lora_wgrad(const LoraGradArgs& a, int rank_major, int num_cus, hipStream_t s);
+
 }  // namespace nf4moe

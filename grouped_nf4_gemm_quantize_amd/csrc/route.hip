@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int64_t c = (i - t * h8) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
-      const float wj = w[t * k + j];
+      const float wj = w ? w[t * k + j] : 1.0f;  // no weights: a plain sum
       const u32x4 v = *reinterpret_cast<const u32x4*>(o + (t * k + j) * H + c);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -30,7 +30,7 @@ from typing import Optional
 
 import numpy as np
 
-_STREAMS = ("w_gu", "w_dn", "x", "logits", "a_gu", "b_gu", "a_dn", "b_dn")
+_STREAMS = ("w_gu", "w_dn", "x", "logits", "a_gu", "b_gu", "a_dn", "b_dn", "dy")
 
 
 @dataclass(frozen=True)
@@ -124,6 +124,12 @@ def stack_weights(cfg: LayerConfig, which: str, seed: int = 0,
 def activations(cfg: LayerConfig, seed: int = 0) -> np.ndarray:
     """x [T, H]: bf16 values held in fp32."""
     rng = np.random.default_rng(_streams(seed)["x"])
+    return round_to_bf16(rng.standard_normal((cfg.T, cfg.H), dtype=np.float32))
+
+
+def output_grad(cfg: LayerConfig, seed: int = 0) -> np.ndarray:
+    """dL/dy [T, H] for the backward: bf16 values (N(0,1)) held in fp32."""
+    rng = np.random.default_rng(_streams(seed)["dy"])
     return round_to_bf16(rng.standard_normal((cfg.T, cfg.H), dtype=np.float32))
 
 

@@ -76,6 +76,7 @@ typedef enum {
 /* Epilogues of grouped_nf4_gemm. */
 #define NF4MOE_EPI_NONE   0
 #define NF4MOE_EPI_SWIGLU 1 /* N = 2I outputs -> I outputs: silu(first I) * next I */
+#define NF4MOE_EPI_SWIGLU_BWD 2 /* dgrad only: see grouped_nf4_gemm_dgrad */
 
 /* Static description of the status code (never NULL). */
 const char* nf4moe_strerror(int status);
@@ -220,6 +221,75 @@ int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
                        void* y, int y_dtype, void* workspace, size_t ws_bytes,
                        void* stream);
 
+/* ---- grouped NF4 dgrad (backward through the frozen stack) ---------------
+ * out_row(i) = row_scale(i) * a[src(i)] . W_e  for rows
+ * expert_offsets[e] <= i < expert_offsets[e+1], W_e = dequant(packed[e],
+ * absmax[e]) [N, K]: the input gradient of the grouped GEMM above, which
+ * contracts over the N stack rows (across the absmax blocks).  Nibbles are
+ * decoded in registers, nothing dequantised is written, fp32 accumulation:
+ * the single-launch dgrad kernel of the fused training path (0.22.0 README
+ * "Which training path?", dgrad=True; the frozen projections re-dequantise
+ * from the packed bytes inside backward, README "Training + expert
+ * offload").
+ *   a [a_rows, N]   gradient rows, F16 or BF16 (else EDTYPE);
+ *   gather          nullable int32 [P]: src(i) = gather[i] / gather_div, else
+ *                   i (not checked on the device: src(i) < a_rows);
+ *   packed, absmax  the stack [E, N, K]; N and K multiples of 64 (ESHAPE);
+ *   expert_offsets  device int32 [E+1] as for grouped_nf4_gemm;
+ *   epilogue        NF4MOE_EPI_NONE: out has K columns;
+ *                   NF4MOE_EPI_SWIGLU_BWD: the backward of the SwiGLU that
+ *                   followed the forward GEMM whose pre-activation row i is
+ *                   g_pre[i] = [gate | up] (2K columns, F16 or BF16): with
+ *                   dh = the dgrad row, out row i = [dh * up * silu'(gate) |
+ *                   dh * silu(gate)] (2K columns);
+ *   row_scale       nullable fp32; row i is scaled by row_scale[gather[i]]
+ *                   when gather is given (a per-pair weight), else
+ *                   row_scale[i]; applied before the SwiGLU backward;
+ *   scatter         nullable int32 [P]: output row i goes to row scatter[i];
+ *   out             F32, F16 or BF16, 16-byte aligned.
+ * One kernel launch, no workspace.  Errors as for grouped_nf4_gemm. */
+int grouped_nf4_gemm_dgrad(const void* a, int a_dtype, int64_t a_rows,
+                           const int32_t* gather, int gather_div,
+                           const uint8_t* packed, const float* absmax,
+                           const int32_t* expert_offsets, int E, int64_t P,
+                           int64_t N, int64_t K, int epilogue, const void* g_pre,
+                           int g_dtype, const float* row_scale,
+                           const int32_t* scatter, void* out, int out_dtype,
+                           void* stream);
+
+/* ---- routed-expert layer backward (QLoRA) --------------------------------
+ * Given dL/dy for y = moe_expert_forward(x, ...), returns dL/dx through the
+ * frozen stacks and, per adapter, dL/dA and dL/dB; the stacks get no
+ * gradient (only the adapters train: solutions entry "How do I QLoRA-train
+ * the fused experts").  Nothing from the forward is kept: routing and the
+ * gate_up pre-activation are recomputed from x and the logits, and both
+ * projections are decoded again from the packed bytes (README "Training +
+ * expert offload").  The router logits are an input, so no gradient flows
+ * through the routing.  Steps: route; G = gate_up(x) (+LoRA); for the down
+ * adapter h = SwiGLU(G) and its rank-r projections; dG = SwiGLU backward of
+ * (w * dy) . W_dn (+ LoRA), one dgrad launch; per-pair dX = dG . W_gu (+
+ * LoRA), one dgrad launch; dx_t = sum of its k pairs; the adapters'
+ * gradients as per-128-row partial sums reduced per expert in a fixed order
+ * (deterministic).
+ *   x [T, H]        BF16 or F16; dy [T, H] BF16 or F16 (dy_dtype);
+ *   dx [T, H]       BF16, F16 or F32 (dx_dtype);
+ *   d_gu_A [E, r, H], d_gu_B [E, 2I, r], d_dn_A [E, r, I], d_dn_B [E, H, r]
+ *                   fp32, required when the matching adapter is given
+ *                   (experts that no token picked get zeros); both adapters
+ *                   must share r;
+ *   workspace       moe_expert_backward_workspace(T, H, I, E, k, r) bytes,
+ *                   256-byte aligned (r = 0 without adapters).
+ * Other arguments and errors as for moe_expert_forward. */
+size_t moe_expert_backward_workspace(int64_t T, int H, int I, int E, int k, int r);
+int moe_expert_backward(const void* x, int x_dtype, const float* router_logits,
+                        const void* dy, int dy_dtype, int64_t T, int H, int I,
+                        int E, int k, int renormalize, const uint8_t* gu_packed,
+                        const float* gu_absmax, const uint8_t* dn_packed,
+                        const float* dn_absmax, const nf4moe_lora* gu_lora,
+                        const nf4moe_lora* dn_lora, void* dx, int dx_dtype,
+                        float* d_gu_A, float* d_gu_B, float* d_dn_A, float* d_dn_B,
+                        void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- other 4-bit storage modes ---------------------------------------------
  * ExpertsNbit stores the same fused stack at selectable precision; nf4 and
  * fp4 are its two 4-bit packed modes, and nf4 reconstructs with less error
@@ -255,6 +325,24 @@ int moe_expert_forward_nbit(int quant_type, const void* x, int x_dtype,
                             const float* dn_absmax, const nf4moe_lora* gu_lora,
                             const nf4moe_lora* dn_lora, void* y, int y_dtype,
                             void* workspace, size_t ws_bytes, void* stream);
+int grouped_nbit_gemm_dgrad(int quant_type, const void* a, int a_dtype,
+                            int64_t a_rows, const int32_t* gather, int gather_div,
+                            const uint8_t* packed, const float* absmax,
+                            const int32_t* expert_offsets, int E, int64_t P,
+                            int64_t N, int64_t K, int epilogue, const void* g_pre,
+                            int g_dtype, const float* row_scale,
+                            const int32_t* scatter, void* out, int out_dtype,
+                            void* stream);
+int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
+                             const float* router_logits, const void* dy,
+                             int dy_dtype, int64_t T, int H, int I, int E, int k,
+                             int renormalize, const uint8_t* gu_packed,
+                             const float* gu_absmax, const uint8_t* dn_packed,
+                             const float* dn_absmax, const nf4moe_lora* gu_lora,
+                             const nf4moe_lora* dn_lora, void* dx, int dx_dtype,
+                             float* d_gu_A, float* d_gu_B, float* d_dn_A,
+                             float* d_dn_B, void* workspace, size_t ws_bytes,
+                             void* stream);
 
 /* Device-pointer views into a moe_expert_forward workspace (for inspection of
  * the routing a forward used; valid after the forward completes on its

@@ -197,3 +197,52 @@ def test_status_strings(lib):
     for s in range(0, -9, -1):
         assert lib.nf4moe_strerror(s).decode() != "unknown status"
     assert lib.nf4moe_version().decode().count(".") == 2
+
+
+def test_dgrad_rejects_bad_arguments_on_the_host(lib):
+    ok_args = dict(a=FAKE, a_dtype=2, a_rows=8, gather=None, gather_div=1, packed=FAKE,
+                   absmax=FAKE, offsets=FAKE, E=1, P=8, N=128, K=64, epi=0, g=None,
+                   g_dtype=2, rs=None, scatter=None, out=FAKE, out_dtype=2, stream=None)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.grouped_nf4_gemm_dgrad(*a.values())
+
+    assert call(a=None) == -1
+    assert call(N=96) == -2            # the contraction runs in 64-row steps
+    assert call(K=96) == -2
+    assert call(epi=1) == -1           # NF4MOE_EPI_SWIGLU is a forward epilogue
+    assert call(epi=2) == -1           # the SwiGLU backward needs g_pre
+    assert "g_pre" in _last(lib)
+    assert call(epi=2, g=FAKE, g_dtype=0) == -5
+    assert call(a_dtype=0) == -5
+    assert call(out_dtype=7) == -5
+    assert call(E=0) == -1
+    assert call(P=0) == 0              # nothing to do: no launch
+    assert lib.grouped_nbit_gemm_dgrad(5, *ok_args.values()) == -1
+
+
+def test_backward_rejects_bad_arguments_on_the_host(lib):
+    lora = binding.LoraStruct(FAKE, FAKE, 8, 2.0, 1)
+    base = dict(x=FAKE, x_dtype=1, logits=FAKE, dy=FAKE, dy_dtype=1, T=4, H=64, I=64, E=4,
+                k=2, renorm=1, gup=FAKE, gua=FAKE, dnp=FAKE, dna=FAKE, gul=None, dnl=None,
+                dx=FAKE, dx_dtype=1, dAg=None, dBg=None, dAd=None, dBd=None, ws=FAKE,
+                ws_bytes=1 << 30, stream=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.moe_expert_backward(*a.values())
+
+    assert call(dy=None) == -1
+    assert call(dy_dtype=0) == -5
+    assert call(dx_dtype=9) == -5
+    assert call(H=96) == -2
+    assert call(k=5) == -4
+    assert call(gul=ctypes.pointer(lora)) == -1        # dA_gu / dB_gu missing
+    assert "d_gu_A" in _last(lib)
+    small = lib.moe_expert_backward_workspace(4, 64, 64, 4, 2, 0)
+    assert small > 0
+    assert lib.moe_expert_backward_workspace(4, 64, 64, 4, 2, 8) > small
+    assert lib.moe_expert_backward_workspace(4, 64, 64, 4, 2, 17) == 0
+    assert call(ws_bytes=small - 1) == -6
+    assert lib.moe_expert_backward_nbit(9, *base.values()) == -1
