@@ -1,7 +1,8 @@
 """Benchmark of the grouped NF4 MoE expert layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload olmoe]
-                    [--no-cpu-baseline] [--no-decode] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-decode] [--no-backward]
+                    [--no-control] [--copy-calibration]
     python bench.py --summarize-trace DIR
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
 
@@ -17,6 +18,9 @@ I=1024, top-8, T=4096 tokens); the value is its algorithmic TFLOP/s
   decode        the batch-1 decode layer (Qwen3-30B-A3B shape, 8 routed
                 experts) as packed-weight GB/s over 48 distinct layer stacks
                 replayed from a HIP graph;
+  backward      the QLoRA training backward of a layer (olmoe without
+                adapters, qlora with r=8 adapters): time per backward and
+                its two dgrad kernels timed alone;
   cpu_baseline  the CPU oracle timed on this host on the same layer shape.
 
 Prints exactly one JSON line.
@@ -302,6 +306,99 @@ def bench_decode(dev, steps: int):
     return out
 
 
+def bench_backward(name: str, dev, steps: int):
+    """The QLoRA training backward of one layer (route, recomputed gate_up,
+    down dgrad with the SwiGLU backward, gate_up dgrad, combine, adapter
+    gradients) and its two dgrad kernels timed alone on the same routing."""
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    cfg = synth.config(name)
+    st = gpu_stacks(cfg, dev)
+    gp, ga = st["gu"]
+    dp, da = st["dn"]
+    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
+    lg = torch.from_numpy(synth.router_logits(cfg)).to(dev)
+    dy = torch.from_numpy(synth.output_grad(cfg)).to(dev).to(torch.bfloat16)
+    glo = dlo = None
+    lw = synth.lora_weights(cfg)
+    if lw is not None:
+        t = {k_: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k_, v in lw.items()}
+        glo = (t["a_gu"], t["b_gu"], cfg.lora_scale)
+        dlo = (t["a_dn"], t["b_dn"], cfg.lora_scale)
+    r = cfg.lora_r
+    dx = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, r),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.moe_backward(x, lg, dy, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
+                             dx=dx, workspace=ws)
+
+    for _ in range(3):
+        step()
+    bwd_ms = time_events(step, max(steps, 5), stream)
+
+    # the dgrad kernels alone, on this layer's routing and recomputed G
+    fws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+                      dtype=torch.uint8, device=dev)
+    binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
+                        workspace=fws)
+    ptr = binding.forward_routing(fws, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    base = fws.data_ptr()
+    P = cfg.P
+    sp = fws[ptr["sorted_pair"] - base: ptr["sorted_pair"] - base + 4 * P].view(torch.int32)
+    off = fws[ptr["offsets"] - base: ptr["offsets"] - base + 4 * (cfg.E + 1)].view(torch.int32)
+    wts = fws[ptr["w"] - base: ptr["w"] - base + 4 * P].view(torch.float32)
+    x16 = x.to(torch.float16)
+    G = torch.empty((P, 2 * cfg.I), dtype=torch.float16, device=dev)
+    binding.grouped_gemm(x16, gp, ga, off, P, gather=sp, gather_div=cfg.k, out=G)
+    dG = torch.empty_like(G)
+    dXp = torch.empty((P, cfg.H), dtype=torch.float16, device=dev)
+
+    dy16 = dy.to(torch.float16)  # the layer backward converts dy once, as here
+
+    def down_dgrad():
+        binding.grouped_dgrad(dy16, dp, da, off, P, gather=sp, gather_div=cfg.k, g_pre=G,
+                              row_scale=wts, out=dG)
+
+    def gate_up_dgrad():
+        binding.grouped_dgrad(dG, gp, ga, off, P, scatter=sp, out=dXp)
+
+    for _ in range(2):
+        down_dgrad()
+        gate_up_dgrad()
+    dn_ms = time_events(down_dgrad, max(steps, 10), stream)
+    gu_ms = time_events(gate_up_dgrad, max(steps, 10), stream)
+    phi = float(P) * cfg.H * cfg.I
+    grad_flops = 6.0 * phi           # the two dgrads
+    exec_flops = 10.0 * phi          # + the recomputed gate_up forward
+    if r:
+        # adapter work: gate_up (in H, out 2I) recomputed u and delta, u again,
+        # v, the input-gradient term, dA, dB: 4 rank-r products over H and 3
+        # over 2I; down (in I, out H): u, v, the input-gradient term, dA, dB:
+        # 3 over I and 2 over H
+        exec_flops += 2.0 * P * r * (6 * cfg.H + 9 * cfg.I)
+    out = {
+        "workload": (f"{cfg.name} layer backward: E={cfg.E} H={cfg.H} I={cfg.I} top-{cfg.k} "
+                     f"T={cfg.T}" + (f" LoRA r={r} on gate_up and down" if r else "")
+                     + ", routing and gate_up recomputed"),
+        "us_per_backward": round(bwd_ms * 1e3, 2),
+        "tflops_gradient": round(grad_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "tflops_executed": round(exec_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "down_dgrad_swiglu_bwd_us": round(dn_ms * 1e3, 2),
+        "down_dgrad_tflops": round(2.0 * phi / (dn_ms * 1e-3) / 1e12, 2),
+        "gate_up_dgrad_us": round(gu_ms * 1e3, 2),
+        "gate_up_dgrad_tflops": round(4.0 * phi / (gu_ms * 1e-3) / 1e12, 2),
+        "gate_up_dgrad_frac_peak": round(4.0 * phi / (gu_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+    }
+    del st, gp, ga, dp, da, G, dG, dXp, ws, fws
+    torch.cuda.empty_cache()
+    return out
+
+
 def control_lane(cfg, st, x16, off, sp, stream, iters: int):
     """Dequantise-then-GEMM control (a benchmark control, never a product
     path): the whole stack is dequantised to fp16 with plain torch ops, then
@@ -380,6 +477,8 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-control", action="store_true",
                     help="skip the dequantise-then-GEMM control lane")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training-backward section")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -533,6 +632,10 @@ def main() -> int:
     if not args.no_decode:
         result["decode"] = bench_decode(dev, args.steps)
         log(f"[bench] decode {result['decode']}")
+    if not args.no_backward:
+        result["backward"] = {n_: bench_backward(n_, dev, args.steps)
+                              for n_ in ("olmoe", "qlora")}
+        log(f"[bench] backward {result['backward']}")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)
         log(f"[bench] cpu baseline {result['cpu_baseline']}")

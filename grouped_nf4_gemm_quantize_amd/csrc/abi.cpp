@@ -718,7 +718,7 @@ int grouped_nbit_gemm_dgrad(int quant_type, const void* a, int a_dtype, int64_t 
 
 struct BwdLayout {
   FwdLayout f;  // routing regions and x16 (h and o unused)
-  size_t g, dg, dxp, h, u_gu, v_gu, u_dn, v_dn, bt_gu, bt_dn, part, total;
+  size_t dy16, g, dg, dxp, h, u_gu, v_gu, u_dn, v_dn, a16_gu, bt_gu, a16_dn, bt_dn, part, total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int H, int I, int E, int k, int r) {
@@ -731,6 +731,7 @@ static BwdLayout bwd_layout(int64_t T, int H, int I, int E, int k, int r) {
     o = align_up(o + bytes, 256);
     return at;
   };
+  L.dy16 = take((size_t)T * H * 2);
   L.g = take(P * 2 * (size_t)I * 2);
   L.dg = take(P * 2 * (size_t)I * 2);
   L.dxp = take(P * (size_t)H * 2);
@@ -740,10 +741,12 @@ static BwdLayout bwd_layout(int64_t T, int H, int I, int E, int k, int r) {
   L.v_gu = take(P * rr * 4);
   L.u_dn = take(P * rr * 4);
   L.v_dn = take(P * rr * 4);
+  L.a16_gu = take((size_t)E * rr * H * 2);
   L.bt_gu = take((size_t)E * rr * 2 * I * 2);
+  L.a16_dn = take((size_t)E * rr * I * 2);
   L.bt_dn = take((size_t)E * rr * H * 2);
   const size_t cmax = (size_t)(H > 2 * I ? H : 2 * I);
-  L.part = take(rr ? ((P + 127) / 128 + (size_t)E) * rr * cmax * 4 : 0);
+  L.part = take(rr ? ((P + 63) / 64 + (size_t)E) * rr * cmax * 4 : 0);
   L.total = o;
   return L;
 }
@@ -755,49 +758,34 @@ size_t moe_expert_backward_workspace(int64_t T, int H, int I, int E, int k, int 
   return bwd_layout(T, H, I, E, k, r).total;
 }
 
-static int lora_wgrad(const void* m, int m_bf16, const int32_t* gather, int gather_div,
-                      const float* rs, const int32_t* rs_idx, const float* q, int r,
-                      const int32_t* offsets, int E, int64_t P, int C, float* part, float* z,
-                      float scale, int rank_major, int cus, hipStream_t s) {
-  LoraGradArgs a{};
+// One LoRA pass over the rows of m: the projection onto w (out non-null)
+// and/or the weight gradient from q (z non-null; part is scratch).
+static int lora_pass(const void* m, int m_bf16, const int32_t* gather, int gather_div,
+                     const int32_t* offsets, int E, int64_t P, int C, int r,
+                     const _Float16* w, float* out, const float* rs, const int32_t* rs_idx,
+                     const float* q, float* part, float* z, float scale, int rank_major,
+                     int cus, hipStream_t s) {
+  LoraPassArgs a{};
   a.m = m;
   a.m_bf16 = m_bf16;
   a.gather = gather;
   a.gather_div = gather ? gather_div : 1;
+  a.offsets = offsets;
+  a.E = E;
+  a.P = P;
+  a.C = C;
+  a.r = r;
+  a.w = w;
+  a.out = out;
   a.rs = rs;
   a.rs_idx = rs_idx;
   a.q = q;
-  a.r = r;
-  a.offsets = offsets;
-  a.E = E;
-  a.P = P;
-  a.C = C;
-  a.part = part;
+  a.part = z ? part : nullptr;
   a.z = z;
   a.scale = scale;
-  hipError_t err = launch_lora_wgrad(a, rank_major, cus, s);
-  if (err != hipSuccess) return hip_fail(err, "LoRA weight-gradient launch");
-  return NF4MOE_OK;
-}
-
-static int lora_proj(const void* m, int m_bf16, const int32_t* gather, int gather_div,
-                     const int32_t* offsets, int E, int64_t P, int C, const void* w,
-                     int w_bf16, int r, float* out, hipStream_t s) {
-  LoraProjArgs a{};
-  a.m = m;
-  a.m_bf16 = m_bf16;
-  a.gather = gather;
-  a.gather_div = gather ? gather_div : 1;
-  a.offsets = offsets;
-  a.E = E;
-  a.P = P;
-  a.C = C;
-  a.w = w;
-  a.w_bf16 = w_bf16;
-  a.r = r;
-  a.out = out;
-  hipError_t err = launch_lora_rowproj(a, s);
-  if (err != hipSuccess) return hip_fail(err, "LoRA projection launch");
+  a.rank_major = rank_major;
+  hipError_t err = launch_lora_pass(a, cus, s);
+  if (err != hipSuccess) return hip_fail(err, "LoRA pass launch");
   return NF4MOE_OK;
 }
 
@@ -888,10 +876,18 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
   float* v_gu = (float*)(ws + L.v_gu);
   float* u_dn = (float*)(ws + L.u_dn);
   float* v_dn = (float*)(ws + L.v_dn);
+  _Float16* a16_gu = (_Float16*)(ws + L.a16_gu);
   _Float16* bt_gu = (_Float16*)(ws + L.bt_gu);
+  _Float16* a16_dn = (_Float16*)(ws + L.a16_dn);
   _Float16* bt_dn = (_Float16*)(ws + L.bt_dn);
   float* part = (float*)(ws + L.part);
-  const int dy_bf16 = dy_dtype == NF4MOE_BF16;
+  // the output gradient in fp16 (the dgrad and LoRA passes read fp16 rows)
+  const void* dyh = dy;
+  if (dy_dtype == NF4MOE_BF16) {
+    err = launch_bf16_to_f16(dy, T * H, (_Float16*)(ws + L.dy16), cus, s);
+    if (err != hipSuccess) return hip_fail(err, "conversion launch");
+    dyh = ws + L.dy16;
+  }
 
   // 2. recompute the gate_up pre-activation G = x W_gu^T (+ LoRA), fp16
   st = gemm_common(xa, NF4MOE_F16, T, sorted, k, gu_packed, gu_absmax, offs, E, P,
@@ -899,44 +895,49 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
                    NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
 
-  // 3. down adapter: h, v' = dy B_dn (without the routing weight), u = h A_dn^T
+  // 3. down adapter: h, u = h A_dn^T, then one pass over dy for
+  //    v' = dy B_dn (without the routing weight) and dB_dn = s sum w dy u^T
   if (dn_lora) {
+    const int bf = dn_lora->dtype == NF4MOE_BF16;
     err = launch_swiglu_rows(G, P, I, hbuf, cus, s);
     if (err != hipSuccess) return hip_fail(err, "SwiGLU launch");
-    err = launch_lora_transpose(dn_lora->B, dn_lora->dtype == NF4MOE_BF16, E, H, r, bt_dn, cus, s);
-    if (err != hipSuccess) return hip_fail(err, "LoRA transpose launch");
-    st = lora_proj(dy, dy_bf16, sorted, k, offs, E, P, H, bt_dn, 0, r, v_dn, s);
+    err = launch_lora_to_f16(dn_lora->A, bf, 0, E, I, r, a16_dn, cus, s);
+    if (err == hipSuccess) err = launch_lora_to_f16(dn_lora->B, bf, 1, E, H, r, bt_dn, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
+    st = lora_pass(hbuf, 0, nullptr, 1, offs, E, P, I, r, a16_dn, u_dn, nullptr, nullptr,
+                   nullptr, nullptr, nullptr, 0.f, 0, cus, s);
     if (st != NF4MOE_OK) return st;
-    st = lora_proj(hbuf, 0, nullptr, 1, offs, E, P, I, dn_lora->A,
-                   dn_lora->dtype == NF4MOE_BF16, r, u_dn, s);
+    st = lora_pass(dyh, 0, sorted, k, offs, E, P, H, r, bt_dn, v_dn, wts, sorted, u_dn,
+                   part, d_dn_B, dn_lora->scale, 0, cus, s);
     if (st != NF4MOE_OK) return st;
   }
 
   // 4. dG = SwiGLU backward of (w * dy_t) W_dn (+ LoRA), fp16
-  st = dgrad_common(dy, dy_dtype, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
+  st = dgrad_common(dyh, NF4MOE_F16, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
                     NF4MOE_EPI_SWIGLU_BWD, G, NF4MOE_F16, wts, nullptr,
                     dn_lora ? v_dn : nullptr, dn_lora, dG, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
 
-  // 5. down adapter gradients
+  // 5. dA_dn = s sum w v' h^T
   if (dn_lora) {
-    st = lora_wgrad(dy, dy_bf16, sorted, k, wts, sorted, u_dn, r, offs, E, P, H, part, d_dn_B,
-                    dn_lora->scale, 0, cus, s);
-    if (st != NF4MOE_OK) return st;
-    st = lora_wgrad(hbuf, 0, nullptr, 1, wts, sorted, v_dn, r, offs, E, P, I, part, d_dn_A,
-                    dn_lora->scale, 1, cus, s);
+    st = lora_pass(hbuf, 0, nullptr, 1, offs, E, P, I, r, nullptr, nullptr, wts, sorted, v_dn,
+                   part, d_dn_A, dn_lora->scale, 1, cus, s);
     if (st != NF4MOE_OK) return st;
   }
 
-  // 6. gate_up adapter projections: u = x A_gu^T, v = dG B_gu
+  // 6. gate_up adapter: u = x A_gu^T, then one pass over dG for v = dG B_gu
+  //    and dB_gu = s sum dG u^T
   if (gu_lora) {
-    err = launch_lora_transpose(gu_lora->B, gu_lora->dtype == NF4MOE_BF16, E, 2 * I, r, bt_gu,
-                                cus, s);
-    if (err != hipSuccess) return hip_fail(err, "LoRA transpose launch");
-    st = lora_proj(xa, 0, sorted, k, offs, E, P, H, gu_lora->A, gu_lora->dtype == NF4MOE_BF16,
-                   r, u_gu, s);
+    const int bf = gu_lora->dtype == NF4MOE_BF16;
+    err = launch_lora_to_f16(gu_lora->A, bf, 0, E, H, r, a16_gu, cus, s);
+    if (err == hipSuccess)
+      err = launch_lora_to_f16(gu_lora->B, bf, 1, E, 2 * I, r, bt_gu, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
+    st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, a16_gu, u_gu, nullptr, nullptr, nullptr,
+                   nullptr, nullptr, 0.f, 0, cus, s);
     if (st != NF4MOE_OK) return st;
-    st = lora_proj(dG, 0, nullptr, 1, offs, E, P, 2 * I, bt_gu, 0, r, v_gu, s);
+    st = lora_pass(dG, 0, nullptr, 1, offs, E, P, 2 * I, r, bt_gu, v_gu, nullptr, nullptr, u_gu,
+                   part, d_gu_B, gu_lora->scale, 0, cus, s);
     if (st != NF4MOE_OK) return st;
   }
 
@@ -949,13 +950,10 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
   err = launch_combine(dXp, nullptr, T, k, H, dx, dx_dtype, cus, s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
 
-  // 8. gate_up adapter gradients
+  // 8. dA_gu = s sum v x^T
   if (gu_lora) {
-    st = lora_wgrad(dG, 0, nullptr, 1, nullptr, nullptr, u_gu, r, offs, E, P, 2 * I, part,
-                    d_gu_B, gu_lora->scale, 0, cus, s);
-    if (st != NF4MOE_OK) return st;
-    st = lora_wgrad(xa, 0, sorted, k, nullptr, nullptr, v_gu, r, offs, E, P, H, part, d_gu_A,
-                    gu_lora->scale, 1, cus, s);
+    st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, nullptr, nullptr, nullptr, nullptr, v_gu,
+                   part, d_gu_A, gu_lora->scale, 1, cus, s);
     if (st != NF4MOE_OK) return st;
   }
   return ok();

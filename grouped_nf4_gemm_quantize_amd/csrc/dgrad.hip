@@ -282,8 +282,7 @@ __device__ __forceinline__ float sigmoid_f(float z) {
 }
 
 template <bool kBf16>
-__device__ __forceinline__ void load8_f32(const void* base, int64_t idx, float (&v)[8]) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+__device__ __forceinline__ void unpack8(const u32x4 w, float (&v)[8]) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -496,9 +495,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
       constexpr int PITCH = BNW * 4 + 16;
       static_assert(NWAVES * 32 * PITCH <= RING, "staging fits the ring");
       char* ws = d_ring + wave * 32 * PITCH;
+      // lane item `it` of an m-tile: tile row mt*32 + (it*64 + lane)/8, 8
+      // columns at col_w + 8*(lane % 8); the gate and up chunks of g (16 B
+      // each) of all four items are loaded before the m-tile is staged, so
+      // their latency overlaps the staging and is paid once per m-tile
+      u32x4 gq[4][2];
+      auto load_g = [&](int mt, u32x4 (&dst)[4][2]) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int row = mt * 32 + ((it * 64 + lane) >> 3);
+          const int col = col_w + (lane & 7) * 8;
+          dst[it][0] = u32x4{0u, 0u, 0u, 0u};
+          dst[it][1] = u32x4{0u, 0u, 0u, 0u};
+          if (wave_live && row < rows_valid) {
+            const uint16_t* gp = reinterpret_cast<const uint16_t*>(g.g) +
+                                 (int64_t)(row0 + row) * 2 * K + col;
+            dst[it][0] = *reinterpret_cast<const u32x4*>(gp);
+            dst[it][1] = *reinterpret_cast<const u32x4*>(gp + K);
+          }
+        }
+      };
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt >= mtv) continue;
+        load_g(mt, gq);
         const float rs = d_rscale[par][mt * 32 + n32];
         char* prow = ws + n32 * PITCH;
 #pragma unroll
@@ -520,14 +540,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
             const f32x4 d0 = *reinterpret_cast<const f32x4*>(ws + rr * PITCH + c8 * 32);
             const f32x4 d1 = *reinterpret_cast<const f32x4*>(ws + rr * PITCH + c8 * 32 + 16);
             const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            const int64_t grow = row0 + row;
             float gate[8], up[8];
             if (g.g_bf16) {
-              load8_f32<true>(g.g, grow * 2 * K + col, gate);
-              load8_f32<true>(g.g, grow * 2 * K + K + col, up);
+              unpack8<true>(gq[it][0], gate);
+              unpack8<true>(gq[it][1], up);
             } else {
-              load8_f32<false>(g.g, grow * 2 * K + col, gate);
-              load8_f32<false>(g.g, grow * 2 * K + K + col, up);
+              unpack8<false>(gq[it][0], gate);
+              unpack8<false>(gq[it][1], up);
             }
             float dg[8], du[8];
 #pragma unroll

@@ -138,8 +138,11 @@ struct DgradArgs {
 
 hipError_t launch_grouped_dgrad(const DgradArgs& g, int num_cus, hipStream_t stream);
 
-// Rank-r row projections: out[i, j] = sum_c m[src(i), c] * w[e(i), j, c].
-struct LoraProjArgs {
+// One pass of the QLoRA backward over the rows of m (64-row tiles of one
+// expert): a rank-r projection out[i, j] = sum_c m[src(i), c] w[e, j, c]
+// and/or an adapter weight gradient z[e] = scale * sum_i rs(i) q[i, :] (x)
+// m[src(i), :] (per-tile partials, then a fixed-order reduction per expert).
+struct LoraPassArgs {
   const void* m;           // [rows, C] f16/bf16
   int m_bf16;
   const int32_t* gather;   // nullable: src(i) = gather[i] / gather_div
@@ -147,37 +150,25 @@ struct LoraProjArgs {
   const int32_t* offsets;  // [E+1]
   int E;
   int64_t P;
-  int C;
-  const void* w;           // [E, r, C] f16/bf16
-  int w_bf16;
+  int C;                   // a multiple of 64
   int r;
-  float* out;              // [P, r]
-};
-
-// Adapter weight gradient: z[e] = scale * sum_i rs(i) q[i, :] (x) m[src(i), :].
-struct LoraGradArgs {
-  const void* m;           // [rows, C] f16/bf16
-  int m_bf16;
-  const int32_t* gather;
-  int gather_div;
-  const float* rs;         // nullable row scale, rs[rs_idx ? rs_idx[i] : i]
+  const _Float16* w;       // projection weights [E, r, C]
+  float* out;              // nullable: projection [P, r]
+  const float* rs;         // nullable row scale rs[rs_idx ? rs_idx[i] : i]
   const int32_t* rs_idx;
   const float* q;          // [P, r]
-  int r;
-  const int32_t* offsets;
-  int E;
-  int64_t P;
-  int C;
-  float* part;             // [(P / 128 + E), r, C] partials
-  float* z;                // [E, r, C] or [E, C, r]
+  float* part;             // nullable: gradient partials [(P / 64 + E), r, C]
+  float* z;                // gradient [E, r, C] (rank_major) or [E, C, r]
   float scale;
+  int rank_major;
 };
 
 hipError_t launch_swiglu_rows(const _Float16* g, int64_t P, int I, _Float16* h, int num_cus,
                               hipStream_t s);
-hipError_t launch_lora_transpose(const void* b, int b_bf16, int E, int C, int r, _Float16* bt,
-                                 int num_cus, hipStream_t s);
-hipError_t launch_lora_rowproj(const LoraProjArgs& a, hipStream_t s);
-hipError_t launch_lora_wgrad(const LoraGradArgs& a, int rank_major, int num_cus, hipStream_t s);
+hipError_t launch_bf16_to_f16(const void* src, int64_t n, _Float16* dst, int num_cus,
+                              hipStream_t s);
+hipError_t launch_lora_to_f16(const void* src, int src_bf16, int transpose, int E, int C,
+                              int r, _Float16* dst, int num_cus, hipStream_t s);
+hipError_t launch_lora_pass(const LoraPassArgs& a, int num_cus, hipStream_t s);
 
 }  // namespace nf4moe

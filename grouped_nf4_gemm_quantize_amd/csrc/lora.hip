@@ -10,8 +10,8 @@
 //   dB_e = s * sum_i d_i u_i^T,  dA_e = s * sum_i v_i x_i^T
 // and the input gradient gains s * A_e^T v_i (added inside the dgrad
 // kernel's epilogue).  The sums over an expert's rows are taken in a fixed
-// order: per 128-row tile (the tile table of the GEMMs) into a partial, then
-// the partials of each expert in tile order, so results are deterministic.
+// order: per 64-row tile into a partial, then the partials of each expert in
+// tile order, so results are deterministic.
 
 #include "common.h"
 #include "launch.h"
@@ -21,7 +21,7 @@ namespace nf4moe {
 
 namespace {
 
-constexpr int kLoraTile = 128;  // rows per partial (the GEMM M-tile)
+constexpr int kLoraTile = 64;  // rows per tile (one expert's rows only)
 
 template <bool kBf16>
 __device__ __forceinline__ void ld8(const void* base, int64_t idx, float (&v)[8]) {
@@ -38,18 +38,6 @@ __device__ __forceinline__ void ld8(const void* base, int64_t idx, float (&v)[8]
       v[2 * i + 1] = (float)h.y;
     }
   }
-}
-
-// Expert of row i: the e with offsets[e] <= i < offsets[e + 1] (rows at or
-// beyond offsets[E] return -1).
-__device__ __forceinline__ int expert_of(const int32_t* __restrict__ offsets, int E, int64_t i) {
-  if (i >= offsets[E]) return -1;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= i) lo = mid; else hi = mid;
-  }
-  return lo;
 }
 
 }  // namespace
@@ -80,74 +68,60 @@ __global__ __launch_bounds__(256) void swiglu_rows_kernel(const _Float16* __rest
   }
 }
 
-// bt[e, j, c] = b[e, c, j] (fp16), the adapter B stored rank-major.
-__global__ __launch_bounds__(256) void lora_transpose_kernel(const uint16_t* __restrict__ b,
-                                                             int b_bf16, int E, int C, int r,
-                                                             _Float16* __restrict__ bt) {
+// bf16 -> fp16 rows (the output gradient, converted once so the dgrad's
+// contraction loop reads fp16 operands); 8 elements per thread and step.
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ src,
+                                                          int64_t n8, _Float16* __restrict__ dst) {
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n8;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + q * 8);
+    *reinterpret_cast<u32x4*>(dst + q * 8) = bf16x8_to_f16x8(v);
+  }
+}
+
+// An adapter matrix as fp16 [E, r, C]: src is [E, r, C] (transpose = 0,
+// the A factor) or [E, C, r] (transpose = 1, the B factor), bf16 or fp16.
+__global__ __launch_bounds__(256) void lora_to_f16_kernel(const uint16_t* __restrict__ src,
+                                                          int src_bf16, int transpose, int E,
+                                                          int C, int r,
+                                                          _Float16* __restrict__ dst) {
   const int64_t n = (int64_t)E * C * r;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n;
        q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = q / ((int64_t)C * r);
     const int64_t rem = q - e * C * r;
     const int j = (int)(rem / C), c = (int)(rem - (int64_t)j * C);
-    const uint16_t raw = b[(e * C + c) * r + j];
-    bt[q] = b_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
+    const uint16_t raw = transpose ? src[(e * C + c) * r + j] : src[q];
+    dst[q] = src_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
   }
 }
 
-// out[i, j] = sum_c m[src(i), c] * w[e(i), j, c] for the P rows that belong
-// to an expert (src(i) = gather[i] / gather_div, else i; w [E, r, C]).  One
-// wave per row; lane l covers columns 8 l + 512 t.
-template <bool kMBf16, bool kWBf16>
-__global__ __launch_bounds__(256) void lora_rowproj_kernel(LoraProjArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= a.P) return;
-  const int e = expert_of(a.offsets, a.E, i);
-  if (e < 0) return;
-  const int64_t src = a.gather ? (int64_t)(a.gather[i] / a.gather_div) : i;
-  float acc[kMaxLoraR];
-#pragma unroll
-  for (int j = 0; j < kMaxLoraR; ++j) acc[j] = 0.f;
-  for (int c = lane * 8; c < a.C; c += 512) {
-    float m[8];
-    ld8<kMBf16>(a.m, src * a.C + c, m);
-#pragma unroll
-    for (int j = 0; j < kMaxLoraR; ++j) {
-      if (j < a.r) {
-        float w[8];
-        ld8<kWBf16>(a.w, ((int64_t)e * a.r + j) * a.C + c, w);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[j] = fmaf(m[t], w[t], acc[j]);
-      }
-    }
-  }
-  float mine = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxLoraR; ++j) {
-    if (j < a.r) {
-      const float s = wave_sum(acc[j]);
-      if (lane == j) mine = s;
-    }
-  }
-  if (lane < a.r) a.out[i * a.r + lane] = mine;
-}
+// One pass over the rows of a matrix m (rows of one expert per 64-row tile;
+// src(i) = gather[i] / gather_div, else i), 64 columns at a time, on
+// v_mfma_f32_16x16x32_f16:
+//   kProj: out[i, j] = sum_c m[src(i), c] * w[e, j, c]      (w [E, r, C] fp16)
+//   kGrad: part[tile, j, c] = sum_{i in tile} rs(i) q[i, j] m[src(i), c]
+// Each 64x64 chunk of m is staged in LDS twice: row-major for the
+// projection's A operand (8 columns of a row per lane) and column-major for
+// the gradient's B operand (8 rows of a column per lane, the contraction of
+// the sum over rows).  Wave w projects rows 16w..16w+15 and sums columns
+// 16w..16w+15 of each chunk; ranks beyond r are zero.
+constexpr int kPitch = 64 * 2 + 16;  // LDS row pitch of a staged chunk (bytes)
 
-// Partial weight gradient of one 128-row tile and 512 columns:
-//   part[tile, j, c] = sum_{rows i of the tile} rs(i) q[i, j] m[src(i), c]
-// with rs(i) = rs[rs_idx ? rs_idx[i] : i] (1 when rs is null).  Four waves of
-// 32 rows each; lane l holds columns 8 l .. 8 l + 7 for all r ranks; the
-// waves' sums meet in LDS, four ranks at a time.
-template <int kR, bool kMBf16>
-__global__ __launch_bounds__(256) void lora_wgrad_partial_kernel(LoraGradArgs a, int n_chunks) {
+template <bool kProj, bool kGrad, bool kMBf16>
+__global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
   __shared__ int32_t tiles[kMaxExperts + 1];
   __shared__ int32_t wsum[4];
-  __shared__ __attribute__((aligned(16))) float red[4][4][64 * 8];
+  __shared__ int32_t srcs[kLoraTile];
+  __shared__ __attribute__((aligned(16))) char nat[kLoraTile * kPitch];  // [row][col]
+  __shared__ __attribute__((aligned(16))) char tr[64 * kPitch];         // [col][row]
+  __shared__ __attribute__((aligned(16))) _Float16 qt[16][kLoraTile + 8];  // [rank][row]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
   build_tile_table<256, kLoraTile>(a.offsets, a.E, tiles, wsum, tid);
   const int total = tiles[a.E];
-  for (int u = blockIdx.x; u < total * n_chunks; u += gridDim.x) {
-    const int tix = u / n_chunks, cc = u - tix * n_chunks;
+  const int nchunk = a.C / 64;
+  for (int tix = blockIdx.x; tix < total; tix += gridDim.x) {
     int lo = 0, hi = a.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -156,44 +130,95 @@ __global__ __launch_bounds__(256) void lora_wgrad_partial_kernel(LoraGradArgs a,
     const int e = lo;
     const int row0 = a.offsets[e] + (tix - tiles[e]) * kLoraTile;
     const int rows = min(kLoraTile, a.offsets[e + 1] - row0);
-    const int c = cc * 512 + lane * 8;
-    const bool live = c < a.C;
-    float acc[kR][8];
-#pragma unroll
-    for (int j = 0; j < kR; ++j)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[j][t] = 0.f;
-    const int rb = wave * 32, re = min(rows, rb + 32);
-    for (int rr = rb; rr < re; ++rr) {
-      const int64_t i = row0 + rr;
-      const float rs = a.rs ? a.rs[a.rs_idx ? a.rs_idx[i] : i] : 1.0f;
-      const int64_t src = a.gather ? (int64_t)(a.gather[i] / a.gather_div) : i;
-      float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (live) ld8<kMBf16>(a.m, src * a.C + c, m);
-#pragma unroll
-      for (int j = 0; j < kR; ++j) {
-        const float qj = j < a.r ? a.q[i * a.r + j] * rs : 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[j][t] = fmaf(qj, m[t], acc[j][t]);
+    __syncthreads();  // the previous tile is done with srcs / qt
+    if (tid < kLoraTile) {
+      const int i = row0 + (tid < rows ? tid : 0);
+      srcs[tid] = a.gather ? a.gather[i] / a.gather_div : i;
+    }
+    if constexpr (kGrad) {
+      // q^T of the tile with the row scale folded in, fp16
+      for (int u = tid; u < 16 * kLoraTile; u += 256) {
+        const int j = u / kLoraTile, rr = u % kLoraTile;
+        float v = 0.f;
+        if (j < a.r && rr < rows) {
+          const int64_t i = row0 + rr;
+          const float rs = a.rs ? a.rs[a.rs_idx ? a.rs_idx[i] : i] : 1.0f;
+          v = a.q[i * a.r + j] * rs;
+        }
+        qt[j][rr] = (_Float16)v;
       }
     }
-    float* part = a.part + (int64_t)tix * a.r * a.C;
+    __syncthreads();
+    f32x4 accp = {0.f, 0.f, 0.f, 0.f};
+    // this thread's two 16-byte pieces of a chunk: rows tid/8 and tid/8 + 32,
+    // columns 8 * (tid % 8)
+    const int lr = tid >> 3, lc = (tid & 7) * 8;
+    u32x4 pre[2];
+    auto load_chunk = [&](int ch) {
 #pragma unroll
-    for (int j0 = 0; j0 < kR; j0 += 4) {
-      __syncthreads();
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) red[wave][jj][lane * 8 + t] = acc[j0 + jj][t];
-      __syncthreads();
-      const int j = j0 + wave;  // wave w sums rank j0 + w over the four waves
-      if (j < a.r && live) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float s = (red[0][wave][lane * 8 + t] + red[1][wave][lane * 8 + t]) +
-                          (red[2][wave][lane * 8 + t] + red[3][wave][lane * 8 + t]);
-          part[(int64_t)j * a.C + c + t] = s;
+      for (int h = 0; h < 2; ++h) {
+        const int rr = lr + 32 * h;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (rr < rows) {
+          v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.m) +
+                                              (int64_t)srcs[rr] * a.C + ch * 64 + lc);
+          if constexpr (kMBf16) v = bf16x8_to_f16x8(v);
         }
+        pre[h] = v;
+      }
+    };
+    load_chunk(0);
+    for (int ch = 0; ch < nchunk; ++ch) {
+      __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rr = lr + 32 * h;
+        *reinterpret_cast<u32x4*>(nat + rr * kPitch + lc * 2) = pre[h];
+        const uint32_t w4[4] = {pre[h].x, pre[h].y, pre[h].z, pre[h].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          *reinterpret_cast<uint16_t*>(tr + (lc + 2 * t) * kPitch + rr * 2) = (uint16_t)(w4[t] & 0xffffu);
+          *reinterpret_cast<uint16_t*>(tr + (lc + 2 * t + 1) * kPitch + rr * 2) = (uint16_t)(w4[t] >> 16);
+        }
+      }
+      __syncthreads();
+      if (ch + 1 < nchunk) load_chunk(ch + 1);
+      if constexpr (kProj) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(nat + (16 * wave + l16) * kPitch +
+                                                           (32 * u + 8 * g4) * 2);
+          u32x4 bv = {0u, 0u, 0u, 0u};
+          if (l16 < a.r)
+            bv = *reinterpret_cast<const u32x4*>(a.w + ((int64_t)e * a.r + l16) * a.C +
+                                                 ch * 64 + 32 * u + 8 * g4);
+          accp = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(bv), accp, 0, 0, 0);
+        }
+      }
+      if constexpr (kGrad) {
+        f32x4 accg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f16x8 qa = *reinterpret_cast<const f16x8*>(&qt[l16][32 * u + 8 * g4]);
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(tr + (16 * wave + l16) * kPitch +
+                                                           (32 * u + 8 * g4) * 2);
+          accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_f16x8(bv), accg, 0, 0, 0);
+        }
+        // lane holds ranks 4 g4 + t of column 16 wave + l16
+        float* part = a.part + (int64_t)tix * a.r * a.C + ch * 64 + 16 * wave + l16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = 4 * g4 + t;
+          if (j < a.r) part[(int64_t)j * a.C] = accg[t];
+        }
+      }
+    }
+    if constexpr (kProj) {
+      // lane holds rows 16 wave + 4 g4 + t, rank l16
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int rr = 16 * wave + 4 * g4 + t;
+        if (rr < rows && l16 < a.r) a.out[(int64_t)(row0 + rr) * a.r + l16] = accp[t];
       }
     }
   }
@@ -201,7 +226,7 @@ __global__ __launch_bounds__(256) void lora_wgrad_partial_kernel(LoraGradArgs a,
 
 // z[e] = scale * sum over expert e's tiles (in tile order) of part; stored
 // [E, r, C] (kRankMajor) or [E, C, r].  Experts without rows get zeros.
-__global__ __launch_bounds__(256) void lora_wgrad_reduce_kernel(LoraGradArgs a, int rank_major) {
+__global__ __launch_bounds__(256) void lora_wgrad_reduce_kernel(LoraPassArgs a) {
   __shared__ int32_t tiles[kMaxExperts + 1];
   __shared__ int32_t wsum[4];
   build_tile_table<256, kLoraTile>(a.offsets, a.E, tiles, wsum, threadIdx.x);
@@ -214,7 +239,7 @@ __global__ __launch_bounds__(256) void lora_wgrad_reduce_kernel(LoraGradArgs a, 
     float s = 0.f;
     for (int t = tiles[e]; t < tiles[e + 1]; ++t) s += a.part[((int64_t)t * a.r + j) * a.C + c];
     s *= a.scale;
-    if (rank_major) a.z[q] = s;
+    if (a.rank_major) a.z[q] = s;
     else a.z[((int64_t)e * a.C + c) * a.r + j] = s;
   }
 }
@@ -229,51 +254,50 @@ hipError_t launch_swiglu_rows(const _Float16* g, int64_t P, int I, _Float16* h, 
   return hipGetLastError();
 }
 
-hipError_t launch_lora_transpose(const void* b, int b_bf16, int E, int C, int r, _Float16* bt,
-                                 int num_cus, hipStream_t s) {
+hipError_t launch_bf16_to_f16(const void* src, int64_t n, _Float16* dst, int num_cus,
+                              hipStream_t s) {
+  const int64_t n8 = n / 8;
+  int64_t grid = (n8 + 255) / 256;
+  if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(src), n8, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_to_f16(const void* src, int src_bf16, int transpose, int E, int C,
+                              int r, _Float16* dst, int num_cus, hipStream_t s) {
   const int64_t n = (int64_t)E * C * r;
   int64_t grid = (n + 255) / 256;
   if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(lora_transpose_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t*>(b), b_bf16, E, C, r, bt);
+  hipLaunchKernelGGL(lora_to_f16_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(src), src_bf16, transpose, E, C, r, dst);
   return hipGetLastError();
 }
 
-hipError_t launch_lora_rowproj(const LoraProjArgs& a, hipStream_t s) {
+template <bool kProj, bool kGrad>
+static void pass_m(const LoraPassArgs& a, dim3 g, hipStream_t s) {
+  if (a.m_bf16) hipLaunchKernelGGL((lora_pass_kernel<kProj, kGrad, true>), g, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((lora_pass_kernel<kProj, kGrad, false>), g, dim3(256), 0, s, a);
+}
+
+hipError_t launch_lora_pass(const LoraPassArgs& a, int num_cus, hipStream_t s) {
   if (a.P == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.P + 3) / 4));
-  if (a.m_bf16) {
-    if (a.w_bf16) hipLaunchKernelGGL((lora_rowproj_kernel<true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((lora_rowproj_kernel<true, false>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.w_bf16) hipLaunchKernelGGL((lora_rowproj_kernel<false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((lora_rowproj_kernel<false, false>), grid, dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_lora_wgrad(const LoraGradArgs& a, int rank_major, int num_cus, hipStream_t s) {
-  const int n_chunks = (a.C + 511) / 512;
-  const int64_t max_units = ((a.P + kLoraTile - 1) / kLoraTile + a.E) * n_chunks;
-  int64_t grid = max_units;
-  if (grid > (int64_t)num_cus * 4) grid = (int64_t)num_cus * 4;
-  if (grid < 1) grid = 1;
+  int64_t grid = (a.P + kLoraTile - 1) / kLoraTile + a.E;
+  if (grid > (int64_t)num_cus * 8) grid = (int64_t)num_cus * 8;
   const dim3 g((unsigned)grid);
-  if (a.r <= 8) {
-    if (a.m_bf16) hipLaunchKernelGGL((lora_wgrad_partial_kernel<8, true>), g, dim3(256), 0, s, a, n_chunks);
-    else hipLaunchKernelGGL((lora_wgrad_partial_kernel<8, false>), g, dim3(256), 0, s, a, n_chunks);
-  } else {
-    if (a.m_bf16) hipLaunchKernelGGL((lora_wgrad_partial_kernel<16, true>), g, dim3(256), 0, s, a, n_chunks);
-    else hipLaunchKernelGGL((lora_wgrad_partial_kernel<16, false>), g, dim3(256), 0, s, a, n_chunks);
-  }
+  const bool proj = a.out != nullptr, grad = a.part != nullptr;
+  if (proj && grad) pass_m<true, true>(a, g, s);
+  else if (proj) pass_m<true, false>(a, g, s);
+  else pass_m<false, true>(a, g, s);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || !grad) return err;
   const int64_t n = (int64_t)a.E * a.r * a.C;
   int64_t rg = (n + 255) / 256;
   if (rg > (int64_t)num_cus * 16) rg = (int64_t)num_cus * 16;
   if (rg < 1) rg = 1;
-  hipLaunchKernelGGL(lora_wgrad_reduce_kernel, dim3((unsigned)rg), dim3(256), 0, s, a, rank_major);
+  hipLaunchKernelGGL(lora_wgrad_reduce_kernel, dim3((unsigned)rg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
