@@ -479,6 +479,8 @@ def main() -> int:
                     help="skip the dequantise-then-GEMM control lane")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training-backward section")
+    ap.add_argument("--backward-workloads", default="olmoe,qlora",
+                    help="comma-separated workloads of the backward section")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -632,9 +634,9 @@ def main() -> int:
     if not args.no_decode:
         result["decode"] = bench_decode(dev, args.steps)
         log(f"[bench] decode {result['decode']}")
-    if not args.no_backward:
-        result["backward"] = {n_: bench_backward(n_, dev, args.steps)
-                              for n_ in ("olmoe", "qlora")}
+    bwd_names = [n_ for n_ in args.backward_workloads.split(",") if n_]
+    if not args.no_backward and bwd_names:
+        result["backward"] = {n_: bench_backward(n_, dev, args.steps) for n_ in bwd_names}
         log(f"[bench] backward {result['backward']}")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)
