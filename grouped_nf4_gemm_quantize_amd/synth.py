@@ -30,7 +30,7 @@ from typing import Optional
 
 import numpy as np
 
-_STREAMS = ("w_gu", "w_dn", "x", "logits", "a_gu", "b_gu", "a_dn", "b_dn", "dy")
+_STREAMS = ("w_gu", "w_dn", "x", "logits", "a_gu", "b_gu", "a_dn", "b_dn", "dy", "mx")
 
 
 @dataclass(frozen=True)
@@ -168,3 +168,24 @@ def lora_weights(cfg: LayerConfig, seed: int = 0):
         out[name] = round_to_bf16(
             rng.standard_normal(shape, dtype=np.float32) * np.float32(0.01))
     return out
+
+
+# magnitude index frequencies (0, 0.5, 1, 1.5, 2, 3, 4, 6) of the synthetic
+# MXFP4 elements, shaped like a block-quantised bell curve
+_MX_MAG_P = (0.10, 0.20, 0.19, 0.15, 0.14, 0.11, 0.07, 0.04)
+
+
+def mxfp4_stack(cfg: LayerConfig, which: str, seed: int = 0):
+    """Synthetic released-MXFP4 stack bytes: (blocks [E, N, K/2] uint8,
+    scales [E, N, K/32] uint8).  Element codes are sign | magnitude index
+    drawn from _MX_MAG_P; scale bytes 127 + {-8, -7, -6} (2^-8 .. 2^-6, the
+    range a 0.02-scale weight's blocks take).  Random bytes only."""
+    child = _streams(seed)["mx"].spawn(2)[0 if which == "gu" else 1]
+    rng = np.random.default_rng(child)
+    N, K = (2 * cfg.I, cfg.H) if which == "gu" else (cfg.H, cfg.I)
+    mag = rng.choice(8, size=(cfg.E, N, K), p=_MX_MAG_P).astype(np.uint8)
+    sign = rng.integers(0, 2, size=(cfg.E, N, K), dtype=np.uint8) << 3
+    codes = mag | sign
+    blocks = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    scales = (127 + rng.integers(-8, -5, size=(cfg.E, N, K // 32))).astype(np.uint8)
+    return blocks, scales

@@ -66,3 +66,13 @@ from .backward import (  # noqa: F401
     moe_backward,
     moe_backward_tokens,
 )
+from .mxfp4 import (  # noqa: F401
+    MX_BLOCK,
+    e2m1_value,
+    e8m0_value,
+    unpack_mx,
+    pack_mx,
+    dequantize_mxfp4,
+    grouped_gemm_mxfp4,
+    moe_forward_mxfp4,
+)
