@@ -90,6 +90,12 @@ _SIGNATURES = {
     "moe_expert_backward_workspace": (_c_size, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_expert_backward": (_c_int, _BACKWARD_ARGS),
     "moe_expert_backward_nbit": (_c_int, [_c_int] + _BACKWARD_ARGS),
+    "grouped_mxfp4_gemm": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_int, _c_vp, _c_vp, _c_vp,
+                                    _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp,
+                                    _c_int, _c_vp]),
+    "moe_expert_forward_mxfp4": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                          _c_int, _c_vp, _c_size, _c_vp]),
 }
 
 # storage modes of the nbit entry points (NF4MOE_QT_* in include/nf4moe.h)
@@ -380,3 +386,41 @@ def moe_backward(x, logits, dy, k: int, gu_packed, gu_absmax, dn_packed, dn_absm
     else:
         _check(lib.moe_expert_backward_nbit(_qt(quant_type), *args))
     return dx, grads
+
+
+def grouped_gemm_mxfp4(a, blocks, scales, offsets, P: int, gather=None, gather_div: int = 1,
+                       swiglu: bool = False, row_scale=None, scatter=None, out=None,
+                       out_dtype=None, out_rows: Optional[int] = None):
+    """Grouped GEMM on MXFP4 stacks (see grouped_mxfp4_gemm in include/nf4moe.h)."""
+    torch = _torch()
+    E, N, K2 = blocks.shape
+    K = K2 * 2
+    n_out = N // 2 if swiglu else N
+    if out is None:
+        rows = out_rows if out_rows is not None else P
+        out = torch.empty((rows, n_out), dtype=out_dtype or torch.float16, device=a.device)
+    _check(load().grouped_mxfp4_gemm(
+        _ptr(a), _dtype_code(a.dtype), a.shape[0], _ptr(gather), gather_div, _ptr(blocks),
+        _ptr(scales), _ptr(offsets), E, P, N, K, EPI_SWIGLU if swiglu else EPI_NONE,
+        _ptr(row_scale), _ptr(scatter), _ptr(out), _dtype_code(out.dtype), _stream(a.device)))
+    return out
+
+
+def moe_forward_mxfp4(x, logits, k: int, gu_blocks, gu_scales, dn_blocks, dn_scales,
+                      renormalize: bool = True, y=None, y_dtype=None, workspace=None):
+    """Routed-expert layer on MXFP4 stacks (see moe_expert_forward_mxfp4)."""
+    torch = _torch()
+    T, H = x.shape
+    E = logits.shape[1]
+    I = dn_blocks.shape[2] * 2
+    if y is None:
+        y = torch.empty((T, H), dtype=y_dtype or torch.bfloat16, device=x.device)
+    lib = load()
+    ws_bytes = lib.moe_expert_forward_workspace(T, H, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_expert_forward_mxfp4(
+        _ptr(x), _dtype_code(x.dtype), _ptr(logits), T, H, I, E, k, int(bool(renormalize)),
+        _ptr(gu_blocks), _ptr(gu_scales), _ptr(dn_blocks), _ptr(dn_scales), _ptr(y),
+        _dtype_code(y.dtype), _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return y

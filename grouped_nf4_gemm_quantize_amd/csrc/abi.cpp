@@ -515,7 +515,7 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   int32_t* ids = (int32_t*)(ws + L.ids);
   float* wts = (float*)(ws + L.w);
 
-  if (use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
+  if (qt != kQtMXFP4 && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
     GemvArgs g{};
     g.x = x;
     g.x_bf16 = x_dtype == NF4MOE_BF16;
@@ -985,6 +985,41 @@ int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
                        renormalize, gu_packed, gu_absmax, dn_packed, dn_absmax, gu_lora,
                        dn_lora, dx, dx_dtype, d_gu_A, d_gu_B, d_dn_A, d_dn_B, workspace,
                        ws_bytes, stream);
+}
+
+// ---- MXFP4 stacks (e2m1 + e8m0 per 32) ----------------------------------
+
+static int mx_shape_check(int64_t N, int64_t K) {
+  if (K % 128)
+    return fail(NF4MOE_ESHAPE, "MXFP4: K=%lld must be a multiple of 128", (long long)K);
+  (void)N;
+  return NF4MOE_OK;
+}
+
+int grouped_mxfp4_gemm(const void* a, int a_dtype, int64_t a_rows, const int32_t* gather,
+                       int gather_div, const uint8_t* blocks, const uint8_t* scales,
+                       const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
+                       int epilogue, const float* row_scale, const int32_t* scatter,
+                       void* out, int out_dtype, void* stream) {
+  int st = mx_shape_check(N, K);
+  if (st != NF4MOE_OK) return st;
+  return gemm_impl(kQtMXFP4, a, a_dtype, a_rows, gather, gather_div, blocks,
+                   reinterpret_cast<const float*>(scales), expert_offsets, E, P, N, K, nullptr,
+                   epilogue, row_scale, scatter, out, out_dtype, stream);
+}
+
+int moe_expert_forward_mxfp4(const void* x, int x_dtype, const float* router_logits, int64_t T,
+                             int H, int I, int E, int k, int renormalize,
+                             const uint8_t* gu_blocks, const uint8_t* gu_scales,
+                             const uint8_t* dn_blocks, const uint8_t* dn_scales, void* y,
+                             int y_dtype, void* workspace, size_t ws_bytes, void* stream) {
+  int st = mx_shape_check(2 * (int64_t)I, H);
+  if (st == NF4MOE_OK) st = mx_shape_check(H, I);
+  if (st != NF4MOE_OK) return st;
+  return forward_impl(kQtMXFP4, x, x_dtype, router_logits, T, H, I, E, k, renormalize,
+                      gu_blocks, reinterpret_cast<const float*>(gu_scales), dn_blocks,
+                      reinterpret_cast<const float*>(dn_scales), nullptr, nullptr, y, y_dtype,
+                      workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

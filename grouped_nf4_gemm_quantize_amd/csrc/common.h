@@ -29,9 +29,16 @@
    -0.0f,        -0.5f / 6.0f, -1.0f / 6.0f, -1.5f / 6.0f,                    \
    -2.0f / 6.0f, -3.0f / 6.0f, -4.0f / 6.0f, -1.0f}
 
+// MXFP4 elements: the e2m1 values by code (sign bit 3), not normalised; the
+// block's e8m0 byte carries the scale.
+#define NF4MOE_E2M1_VALUES_INIT                                               \
+  {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,                            \
+   -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f}
+
 namespace nf4moe {
 constexpr int kQtNF4 = 0;
 constexpr int kQtFP4 = 1;
+constexpr int kQtMXFP4 = 2;  // e2m1 + e8m0 per 32, low nibble first (own entry points)
 }  // namespace nf4moe
 
 namespace nf4moe {
@@ -95,17 +102,33 @@ struct Lut {
 // Fill the LDS table from the fp32 levels (each half rounded to nearest-even
 // fp16).  `stage` is a 16-entry LDS scratch array.  The fill ends with a
 // barrier, so the table is ready to use on return.
+// With low_first the byte holds the first element in its LOW nibble (the
+// MXFP4 packing): the pair is (level[b & 15], level[b >> 4]).
 template <int kLutCopies>
 __device__ __forceinline__ void lut_fill(uint32_t* lut, uint16_t* stage,
                                          const float* levels, int tid,
-                                         int nthreads) {
+                                         int nthreads, bool low_first = false) {
   if (tid < 16) stage[tid] = __builtin_bit_cast(uint16_t, (_Float16)levels[tid]);
   __syncthreads();
   for (int i = tid; i < 256 * kLutCopies; i += nthreads) {
     const int b = i / kLutCopies;
-    lut[i] = (uint32_t)stage[b >> 4] | ((uint32_t)stage[b & 15] << 16);
+    const int first = low_first ? (b & 15) : (b >> 4);
+    const int second = low_first ? (b >> 4) : (b & 15);
+    lut[i] = (uint32_t)stage[first] | ((uint32_t)stage[second] << 16);
   }
   __syncthreads();
+}
+
+// e8m0 scale byte -> fp16 2^(s - 127): normal for s in [113, 142],
+// subnormal down to s = 103, zero below, inf above, NaN for 255.
+__device__ __forceinline__ _Float16 e8m0_to_half(uint32_t s) {
+  uint32_t bits;
+  if (s == 255u) bits = 0x7e00u;
+  else if (s >= 143u) bits = 0x7c00u;
+  else if (s >= 113u) bits = (s - 112u) << 10;
+  else if (s >= 103u) bits = 1u << (s - 103u);
+  else bits = 0u;
+  return __builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 // Per-lane constant of the lookup address: 4 * (lane % copies).

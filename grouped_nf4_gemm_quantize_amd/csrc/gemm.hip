@@ -67,6 +67,7 @@ namespace nf4moe {
 
 __constant__ float c_levels_gemm[16] = NF4MOE_LEVELS_INIT;
 __constant__ float c_levels_gemm_fp4[16] = NF4MOE_FP4_LEVELS_INIT;
+__constant__ float c_levels_gemm_mx[16] = NF4MOE_E2M1_VALUES_INIT;
 
 namespace {
 
@@ -87,6 +88,7 @@ constexpr int OFF_BR = 2 * ASTAGE;                   // packed-code ring
 constexpr int BPAIR = BN * BK;                       // 512 rows x 64 B = 32768 B
 constexpr int RING = OFF_BR + 2 * BPAIR;             // 102400 B
 constexpr int kAbsGroup = 4;                   // steps of absmax per copy (16 B per row)
+constexpr int kMxGroup = 8;                    // MXFP4: steps of scale bytes per copy (2 per step)
 
 }  // namespace
 
@@ -184,14 +186,21 @@ struct StepRegs {
   f16x2 sc[NT];
 };
 
+template <bool kMx>
 __device__ __forceinline__ void load_step_regs(const char* bst, int step, const Rd& rd,
                                                StepRegs& r) {
-  const float* sab = &g_sabs[(step / kAbsGroup) & 1][step % kAbsGroup];
   const uint32_t bo = (step & 1) ? rd.b[1] : rd.b[0];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     r.bq[nt] = *reinterpret_cast<const u32x4*>(bst + bo + nt * 2048);
-    const _Float16 sh = (_Float16)sab[rd.s + nt * 32 * kAbsGroup];
+    _Float16 sh;
+    if constexpr (kMx) {
+      // the e8m0 byte of this lane's 32-element block (k half g2 of the step)
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(&g_sabs[(step / kMxGroup) & 1][0]);
+      sh = e8m0_to_half(sb[rd.s + nt * 32 * 16 + (step % kMxGroup) * 2]);
+    } else {
+      sh = (_Float16)g_sabs[(step / kAbsGroup) & 1][rd.s + nt * 32 * kAbsGroup + step % kAbsGroup];
+    }
     r.sc[nt] = f16x2{sh, sh};
   }
 }
@@ -240,7 +249,7 @@ __device__ __forceinline__ void scale_b(const StepRegs& r, const uint32_t (&d)[N
 // ahead of use), while the A fragments and table words of the next substep
 // are read -- for S = 3 those of substep 0 of the next step, from the next
 // stage `nst` (valid once the barrier before substep 3 has passed).
-template <int S, int MTV, bool kLora, bool kABf16>
+template <int S, int MTV, bool kLora, bool kABf16, bool kMx>
 __device__ __forceinline__ void substep(const char* st, const char* nst, const char* nbst,
                                         int next_step, const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
@@ -252,7 +261,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
     load_a<MTV, kABf16>(st, rd, S + 1, af_n);
     lut_lookups(cur, S + 1, rd.lane_off, dn);
   } else {
-    load_step_regs(nbst, next_step, rd, nxt);
+    load_step_regs<kMx>(nbst, next_step, rd, nxt);
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
     lut_lookups(nxt, 0, rd.lane_off, dn);
   }
@@ -297,7 +306,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
 // complete in order.  Pairs and activations are issued at least one full
 // step before use, codes and absmax two.  Past the last step the copies of
 // the last step / pair / group are repeated, so the counts hold throughout.
-template <int MTV, bool kLora, bool kABf16>
+template <int MTV, bool kLora, bool kABf16, bool kMx>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
                                       int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
                                       f32x4& acc_u) {
@@ -319,7 +328,7 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
   StepRegs cur, nxt;
   f16x8 af[MT];
   uint32_t d[NT][4];
-  load_step_regs(g_ring + OFF_BR, 0, rd, cur);
+  load_step_regs<kMx>(g_ring + OFF_BR, 0, rd, cur);
   load_a<MTV, kABf16>(g_ring, rd, 0, af);
   lut_lookups(cur, 0, rd.lane_off, d);
   for (int kb = 0; kb < nk; ++kb) {
@@ -327,31 +336,44 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
     const char* sp = g_ring + a * ASTAGE;              // step kb's activations
     const char* np = g_ring + (a ^ 1) * ASTAGE;        // step kb + 1's
     const char* nbp = g_ring + OFF_BR + (((kb + 1) >> 1) & 1) * BPAIR;  // kb + 1's codes
-    substep<0, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<1, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<2, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    switch (kb & 3) {
-      case 0: wait_vm_barrier<kDmaB>(); break;             // batch kb - 1 = 3 mod 4
-      case 2: wait_vm_barrier<kDmaB + kDmaAbs>(); break;   // batch kb - 1 = 1 mod 4
-      default: wait_vm_barrier<0>(); break;                // batch kb - 1 even
+    substep<0, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<1, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<2, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    if constexpr (kMx) {
+      // MXFP4 scale groups cover 8 steps: batch kb - 1 carried one when it
+      // was 5 mod 8
+      if (kb & 1) wait_vm_barrier<0>();
+      else if ((kb & 7) == 6) wait_vm_barrier<kDmaB + kDmaAbs>();
+      else wait_vm_barrier<kDmaB>();
+    } else {
+      switch (kb & 3) {
+        case 0: wait_vm_barrier<kDmaB>(); break;             // batch kb - 1 = 3 mod 4
+        case 2: wait_vm_barrier<kDmaB + kDmaAbs>(); break;   // batch kb - 1 = 1 mod 4
+        default: wait_vm_barrier<0>(); break;                // batch kb - 1 even
+      }
     }
     issue_a<kLora>(src, min(kb + 2, last), ring + a * ASTAGE, wave);
     if (kb & 1) {
       const int pn = (kb + 3) >> 1;
       issue_b(src, min(pn, last_pair), ring + OFF_BR + (pn & 1) * BPAIR, wave);
-      if ((kb & 3) == 1) {
+      if constexpr (kMx) {
+        if ((kb & 7) == 5) {
+          const int grp = (kb + 3) >> 3;
+          issue_abs(src, min(grp, last >> 3), grp & 1, wave);
+        }
+      } else if ((kb & 3) == 1) {
         const int grp = (kb + 3) >> 2;
         issue_abs(src, min(grp, last >> 2), grp & 1, wave);
       }
     }
-    substep<3, MTV, kLora, kABf16>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<3, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
     cur = nxt;
   }
 }
 
 }  // namespace
 
-template <bool kSwiglu, bool kLora, bool kABf16, int kOut>
+template <bool kSwiglu, bool kLora, bool kABf16, int kOut, bool kMx>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -360,7 +382,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   const int g2 = lane >> 5;   // k half of the operands
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16x32 operand coordinates
 
-  lut_fill<kCopies>(g_lut, g_lstage, g.qtype == kQtFP4 ? c_levels_gemm_fp4 : c_levels_gemm, tid, NTHREADS);
+  if constexpr (kMx)
+    lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm_mx, tid, NTHREADS, /*low_first=*/true);
+  else
+    lut_fill<kCopies>(g_lut, g_lstage, g.qtype == kQtFP4 ? c_levels_gemm_fp4 : c_levels_gemm,
+                      tid, NTHREADS);
 
   build_tile_table<NTHREADS, BM>(g.offsets, g.E, g_tiles, g_wsum, tid);
 
@@ -378,7 +404,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
 #pragma unroll
   for (int sp2 = 0; sp2 < 2; ++sp2)
     rd.b[sp2] = (wave * BNW + n32) * 64 + (((sp2 * 2 + g2) ^ ((n32 >> 2) & 3)) << 4);
-  rd.s = (wave * BNW + n32) * kAbsGroup;
+  // absmax element (fp32 index) of n-tile 0's row; MXFP4: its scale byte of
+  // k half g2 (16 bytes per row: 8 steps x 2 halves)
+  rd.s = kMx ? (wave * BNW + n32) * 16 + g2 : (wave * BNW + n32) * kAbsGroup;
   // LoRA operands of 16x16x32: A row c16 of this wave's 16 rows and k chunk
   // 4*s2 + g4 (swizzled like the main fragments); A_e row c16, same k
 #pragma unroll
@@ -446,7 +474,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     Src src;
     src.a_rsrc = a_rsrc;
     const uint32_t b_bytes = (uint32_t)N * (uint32_t)(K / 2);
-    const uint32_t s_bytes = (uint32_t)N * (uint32_t)nk * 4u;
+    const uint32_t s_bytes = kMx ? (uint32_t)N * (uint32_t)(K / 32) : (uint32_t)N * (uint32_t)nk * 4u;
     src.b_rsrc = make_rsrc(reinterpret_cast<const char*>(g.packed) + (int64_t)e * b_bytes, b_bytes);
     src.s_rsrc = make_rsrc(reinterpret_cast<const char*>(g.absmax) + (int64_t)e * s_bytes, s_bytes);
     // A: wave instruction i covers LDS chunks [64 j, 64 j + 64) = rows
@@ -473,7 +501,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     }
     // absmax groups: the wave's instruction covers rows [64 wave, 64 wave +
     // 64), 16 bytes (kAbsGroup steps) per row
-    src.s_off = (uint32_t)weight_row(wave * 64 + lane, n_idx) * (uint32_t)nk * 4u;
+    src.s_off = (uint32_t)weight_row(wave * 64 + lane, n_idx) *
+                (kMx ? (uint32_t)(K / 32) : (uint32_t)nk * 4u);
     if constexpr (kLora) {
       const uint32_t l_bytes = (uint32_t)g.lora_r * (uint32_t)K * 2u;
       src.l_rsrc = make_rsrc(reinterpret_cast<const char*>(g.lora_a) + (int64_t)e * l_bytes, l_bytes);
@@ -507,10 +536,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     // every wave is done with the previous tile's stages (and LoRA exchange)
     lds_barrier();
     switch (mtv) {
-      case 1: kloop<1, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      case 2: kloop<2, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      case 3: kloop<3, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      default: kloop<4, kLora, kABf16>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 1: kloop<1, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 2: kloop<2, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 3: kloop<3, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      default: kloop<4, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
     }
     // every copy has landed and every wave is done with the ring: the
     // epilogue stages its output there
@@ -610,28 +639,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kSwiglu, bool kLora, bool kABf16>
+template <bool kSwiglu, bool kLora, bool kABf16, bool kMx>
 static void launch_out(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
   switch (g.out_dtype) {
     case kF32:
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF32>), grid,
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF32, kMx>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     case kBF16:
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kBF16>), grid,
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kBF16, kMx>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF16>), grid,
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF16, kMx>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
   }
 }
 
-template <bool kSwiglu, bool kLora>
+template <bool kSwiglu, bool kLora, bool kMx = false>
 static void launch_a(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
-  if (g.a_bf16) launch_out<kSwiglu, kLora, true>(g, grid, n_tiles, s);
-  else launch_out<kSwiglu, kLora, false>(g, grid, n_tiles, s);
+  if (g.a_bf16) launch_out<kSwiglu, kLora, true, kMx>(g, grid, n_tiles, s);
+  else launch_out<kSwiglu, kLora, false, kMx>(g, grid, n_tiles, s);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t stream) {
@@ -643,6 +672,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t strea
   if (grid < 8) grid = 8;
   const dim3 dg((unsigned)grid);
   const bool lora = g.lora_a != nullptr;
+  if (g.qtype == kQtMXFP4) {  // no adapters on MXFP4 stacks (checked by the caller)
+    if (g.swiglu) launch_a<true, false, true>(g, dg, n_tiles, stream);
+    else launch_a<false, false, true>(g, dg, n_tiles, stream);
+    return hipGetLastError();
+  }
   if (g.swiglu) {
     if (lora) launch_a<true, true>(g, dg, n_tiles, stream);
     else launch_a<true, false>(g, dg, n_tiles, stream);

@@ -344,6 +344,34 @@ int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
                              float* d_dn_B, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/* ---- MXFP4 stacks (released e2m1 blocks + e8m0 scales) --------------------
+ * The grouped GEMM and the layer forward on expert stacks released in MXFP4,
+ * multiplied on their own bytes with no requantisation to NF4 and no bf16
+ * copy (grouped-nf4-gemm solutions entry "How do I run MoE expert inference
+ * natively on MXFP4 (e2m1 + e8m0) weights, straight from the released
+ * checkpoint bytes?").  Format (OCP microscaling):
+ *   blocks [E, N, K/2] uint8: two e2m1 codes per byte, element 2i in the LOW
+ *          nibble (the released packing; the NF4 stacks put it high);
+ *   scales [E, N, K/32] uint8: e8m0, weight = e2m1 value * 2^(s - 127).
+ * The elements are decoded in registers to fp16 (value x scale, exact while
+ * 2^(s-127) is within fp16's range, 2^-24 .. 2^15; s = 255 decodes as NaN);
+ * fp32 accumulation.  K must be a multiple of 128 (ESHAPE).  No adapters.
+ * Other arguments, layouts and errors as for grouped_nf4_gemm and
+ * moe_expert_forward (the T == 1 case runs the grouped kernels). */
+int grouped_mxfp4_gemm(const void* a, int a_dtype, int64_t a_rows,
+                       const int32_t* gather, int gather_div,
+                       const uint8_t* blocks, const uint8_t* scales,
+                       const int32_t* expert_offsets, int E, int64_t P,
+                       int64_t N, int64_t K, int epilogue, const float* row_scale,
+                       const int32_t* scatter, void* out, int out_dtype,
+                       void* stream);
+int moe_expert_forward_mxfp4(const void* x, int x_dtype, const float* router_logits,
+                             int64_t T, int H, int I, int E, int k,
+                             int renormalize, const uint8_t* gu_blocks,
+                             const uint8_t* gu_scales, const uint8_t* dn_blocks,
+                             const uint8_t* dn_scales, void* y, int y_dtype,
+                             void* workspace, size_t ws_bytes, void* stream);
+
 /* Device-pointer views into a moe_expert_forward workspace (for inspection of
  * the routing a forward used; valid after the forward completes on its
  * stream).  Any out-pointer may be NULL.  Returns a negative status on bad

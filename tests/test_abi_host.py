@@ -246,3 +246,14 @@ def test_backward_rejects_bad_arguments_on_the_host(lib):
     assert lib.moe_expert_backward_workspace(4, 64, 64, 4, 2, 17) == 0
     assert call(ws_bytes=small - 1) == -6
     assert lib.moe_expert_backward_nbit(9, *base.values()) == -1
+
+
+def test_mxfp4_entry_points_check_shapes_on_the_host(lib):
+    # K must be a multiple of 128 (whole dwords of scale bytes per row)
+    assert lib.grouped_mxfp4_gemm(FAKE, 2, 8, None, 1, FAKE, FAKE, FAKE, 1, 8, 64, 192, 0,
+                                  None, None, FAKE, 2, None) == -2
+    assert "128" in _last(lib)
+    assert lib.grouped_mxfp4_gemm(None, 2, 8, None, 1, FAKE, FAKE, FAKE, 1, 8, 64, 256, 0,
+                                  None, None, FAKE, 2, None) == -1
+    assert lib.moe_expert_forward_mxfp4(FAKE, 1, FAKE, 4, 192, 128, 4, 2, 1, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, 1, FAKE, 1 << 30, None) == -2
