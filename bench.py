@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload olmoe]
                     [--no-cpu-baseline] [--no-decode] [--no-backward]
-                    [--no-control] [--copy-calibration]
+                    [--no-control] [--no-mxfp4] [--copy-calibration]
     python bench.py --summarize-trace DIR
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
 
@@ -18,6 +18,8 @@ I=1024, top-8, T=4096 tokens); the value is its algorithmic TFLOP/s
   decode        the batch-1 decode layer (Qwen3-30B-A3B shape, 8 routed
                 experts) as packed-weight GB/s over 48 distinct layer stacks
                 replayed from a HIP graph;
+  mxfp4         the same prefill layer on released-MXFP4-format stacks
+                (e2m1 + e8m0 bytes multiplied in place);
   backward      the QLoRA training backward of a layer (olmoe without
                 adapters, qlora with r=8 adapters): time per backward and
                 its two dgrad kernels timed alone;
@@ -399,6 +401,57 @@ def bench_backward(name: str, dev, steps: int):
     return out
 
 
+def bench_mxfp4(dev, steps: int):
+    """The olmoe-shaped prefill layer on synthetic released-MXFP4 stacks
+    (e2m1 + e8m0 bytes multiplied in place) and its gate_up GEMM alone."""
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    cfg = synth.config("olmoe")
+    gb, gs = (torch.from_numpy(t).to(dev) for t in synth.mxfp4_stack(cfg, "gu"))
+    db, ds = (torch.from_numpy(t).to(dev) for t in synth.mxfp4_stack(cfg, "dn"))
+    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
+    lg = torch.from_numpy(synth.router_logits(cfg)).to(dev)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.moe_forward_mxfp4(x, lg, cfg.k, gb, gs, db, ds, y=y, workspace=ws)
+
+    for _ in range(3):
+        step()
+    ms = time_events(step, max(steps, 5), stream)
+    ptr = binding.forward_routing(ws, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    base = ws.data_ptr()
+    P = cfg.P
+    sp = ws[ptr["sorted_pair"] - base: ptr["sorted_pair"] - base + 4 * P].view(torch.int32)
+    off = ws[ptr["offsets"] - base: ptr["offsets"] - base + 4 * (cfg.E + 1)].view(torch.int32)
+    x16 = x.to(torch.float16)
+    h = torch.empty((P, cfg.I), dtype=torch.float16, device=dev)
+
+    def gate_up():
+        binding.grouped_gemm_mxfp4(x16, gb, gs, off, P, gather=sp, gather_div=cfg.k,
+                                   swiglu=True, out=h)
+
+    for _ in range(2):
+        gate_up()
+    gu_ms = time_events(gate_up, max(steps, 10), stream)
+    out = {
+        "workload": (f"olmoe layer prefill on MXFP4 stacks (e2m1 + e8m0 per 32): E={cfg.E} "
+                     f"H={cfg.H} I={cfg.I} top-{cfg.k} T={cfg.T}"),
+        "us_per_forward": round(ms * 1e3, 2),
+        "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
+        "gate_up_us": round(gu_ms * 1e3, 2),
+        "gate_up_tflops": round(4.0 * P * cfg.H * cfg.I / (gu_ms * 1e-3) / 1e12, 2),
+    }
+    del gb, gs, db, ds, ws, h
+    torch.cuda.empty_cache()
+    return out
+
+
 def control_lane(cfg, st, x16, off, sp, stream, iters: int):
     """Dequantise-then-GEMM control (a benchmark control, never a product
     path): the whole stack is dequantised to fp16 with plain torch ops, then
@@ -481,6 +534,7 @@ def main() -> int:
                     help="skip the training-backward section")
     ap.add_argument("--backward-workloads", default="olmoe,qlora",
                     help="comma-separated workloads of the backward section")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 section")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -634,6 +688,9 @@ def main() -> int:
     if not args.no_decode:
         result["decode"] = bench_decode(dev, args.steps)
         log(f"[bench] decode {result['decode']}")
+    if not args.no_mxfp4:
+        result["mxfp4"] = bench_mxfp4(dev, args.steps)
+        log(f"[bench] mxfp4 {result['mxfp4']}")
     bwd_names = [n_ for n_ in args.backward_workloads.split(",") if n_]
     if not args.no_backward and bwd_names:
         result["backward"] = {n_: bench_backward(n_, dev, args.steps) for n_ in bwd_names}
