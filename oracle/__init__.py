@@ -76,3 +76,10 @@ from .mxfp4 import (  # noqa: F401
     grouped_gemm_mxfp4,
     moe_forward_mxfp4,
 )
+from .nbit8 import (  # noqa: F401
+    e4m3_value,
+    int8_code,
+    fp8_code,
+    quantize_blockwise8,
+    dequantize_blockwise8,
+)

@@ -201,7 +201,14 @@ def quantize_blockwise(w: np.ndarray, blocksize: int = BLOCKSIZE, quant_type: st
 
 def dequantize_blockwise(packed: np.ndarray, absmax: np.ndarray,
                          blocksize: int = BLOCKSIZE, quant_type: str = "nf4") -> np.ndarray:
-    """fp32 weights: level[code] * absmax, one fp32 multiply per element."""
+    """fp32 weights: level[code] * absmax, one fp32 multiply per element.
+
+    The 8-bit modes ("int8", "fp8"; one code byte per element) are the
+    exact fp64 values of ``oracle.nbit8``."""
+    if quant_type in ("int8", "fp8"):
+        from .nbit8 import dequantize_blockwise8
+
+        return dequantize_blockwise8(packed, absmax, quant_type, blocksize)
     levels = codebook(quant_type)
     codes = unpack_codes(packed)
     vals = levels[codes]
