@@ -99,12 +99,13 @@ _SIGNATURES = {
 }
 
 # storage modes of the nbit entry points (NF4MOE_QT_* in include/nf4moe.h)
-QUANT_TYPES = {"nf4": 0, "fp4": 1}
+QUANT_TYPES = {"nf4": 0, "fp4": 1, "int8": 3, "fp8": 4}
+EIGHT_BIT = ("int8", "fp8")  # one byte per element: packed stacks are [E, N, K]
 
 
 def _qt(quant_type: str) -> int:
     if quant_type not in QUANT_TYPES:
-        raise ValueError(f"unknown quant_type {quant_type!r} (nf4 or fp4)")
+        raise ValueError(f"unknown quant_type {quant_type!r} (one of {sorted(QUANT_TYPES)})")
     return QUANT_TYPES[quant_type]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -192,7 +193,8 @@ def quantize(w, nonfinite_flag=None, quant_type: str = "nf4"):
     if w.dim() != 3:
         raise ValueError("w must be [E, N, K]")
     E, N, K = w.shape
-    packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    per_byte = 1 if quant_type in EIGHT_BIT else 2
+    packed = torch.empty((E, N, K // per_byte), dtype=torch.uint8, device=w.device)
     absmax = torch.empty((E, N, max(K // 64, 1)), dtype=torch.float32, device=w.device)
     args = (_ptr(w), _dtype_code(w.dtype), E, N, K, 64, _ptr(packed), _ptr(absmax),
             _ptr(nonfinite_flag), _stream(w.device))
@@ -247,7 +249,7 @@ def grouped_gemm(a, packed, absmax, offsets, P: int, gather=None, gather_div: in
     """
     torch = _torch()
     E, N, K2 = packed.shape
-    K = K2 * 2
+    K = K2 if quant_type in EIGHT_BIT else K2 * 2
     n_out = N // 2 if swiglu else N
     if out is None:
         rows = out_rows if out_rows is not None else P
@@ -281,7 +283,7 @@ def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
     torch = _torch()
     T, H = x.shape
     E = logits.shape[1]
-    I = dn_packed.shape[2] * 2
+    I = dn_packed.shape[2] * (1 if quant_type in EIGHT_BIT else 2)
     if y is None:
         y = torch.empty((T, H), dtype=y_dtype or torch.bfloat16, device=x.device)
     lib = load()

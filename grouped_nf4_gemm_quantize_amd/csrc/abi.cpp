@@ -86,10 +86,25 @@ const QuantThresholds& thresholds(int qt) {
     return t;
   }();
   static const QuantThresholds fp4 = make_thresholds_fp4();
+  static const QuantThresholds int8 = [] {
+    QuantThresholds t{};
+    t.qtype = kQtINT8;
+    return t;
+  }();
+  static const QuantThresholds fp8 = [] {
+    QuantThresholds t{};
+    t.qtype = kQtFP8;
+    return t;
+  }();
+  if (qt == kQtINT8) return int8;
+  if (qt == kQtFP8) return fp8;
   return qt == kQtFP4 ? fp4 : nf4;
 }
 
-bool valid_qtype(int qt) { return qt == kQtNF4 || qt == kQtFP4; }
+bool valid_qtype(int qt) {
+  return qt == kQtNF4 || qt == kQtFP4 || qt == kQtINT8 || qt == kQtFP8;
+}
+bool is_8bit(int qt) { return qt == kQtINT8 || qt == kQtFP8; }
 
 std::atomic<int> g_cu_cache[64];
 
@@ -231,7 +246,8 @@ int nf4moe_codebook(float* out16) {
 
 int nbit_codebook(int quant_type, float* out16) {
   if (out16 == nullptr) return fail(NF4MOE_EINVAL, "out16 is NULL");
-  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  if (!valid_qtype(quant_type) || is_8bit(quant_type))
+    return fail(NF4MOE_EINVAL, "storage mode %d has no 16-level codebook", quant_type);
   std::memcpy(out16, quant_type == kQtFP4 ? kLevelsFP4 : kLevels, sizeof(kLevels));
   return ok();
 }
@@ -404,8 +420,11 @@ static int gemm_impl(int qt, const void* a, int a_dtype, int64_t a_rows,
     return fail(NF4MOE_EOVERFLOW, "P, N or K too large for 32-bit row indexing");
   // the kernel addresses activations and one expert's weights with 32-bit
   // byte offsets
-  if (a_rows * K * 2 > (int64_t)UINT32_MAX || N * K / 2 > (int64_t)UINT32_MAX)
+  if (a_rows * K * 2 > (int64_t)UINT32_MAX ||
+      N * K / (is_8bit(qt) ? 1 : 2) > (int64_t)UINT32_MAX)
     return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
+  if (lora != nullptr && (is_8bit(qt) || qt == kQtMXFP4))
+    return fail(NF4MOE_EINVAL, "adapters are supported on nf4 and fp4 stacks only");
   int st = check_lora(lora, "lora");
   if (st != NF4MOE_OK) return st;
   if (!aligned(a, 16) || !aligned(packed, 16) || !aligned(absmax, 4) ||
@@ -497,7 +516,7 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   // the GEMMs address activations and one expert's weights with 32-bit byte
   // offsets
   if (T * H * 2 > (int64_t)UINT32_MAX || P * I * 2 > (int64_t)UINT32_MAX ||
-      2 * (int64_t)I * H / 2 > (int64_t)UINT32_MAX)
+      2 * (int64_t)I * H / (is_8bit(qt) ? 1 : 2) > (int64_t)UINT32_MAX)
     return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
   if (!aligned(x, 16) || !aligned(gu_packed, 16) || !aligned(dn_packed, 16) ||
       !aligned(gu_absmax, 4) || !aligned(dn_absmax, 4) || !aligned(y, 16))
@@ -515,7 +534,9 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   int32_t* ids = (int32_t*)(ws + L.ids);
   float* wts = (float*)(ws + L.w);
 
-  if (qt != kQtMXFP4 && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
+  if ((gu_lora != nullptr || dn_lora != nullptr) && (is_8bit(qt) || qt == kQtMXFP4))
+    return fail(NF4MOE_EINVAL, "adapters are supported on nf4 and fp4 stacks only");
+  if (qt != kQtMXFP4 && !is_8bit(qt) && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
     GemvArgs g{};
     g.x = x;
     g.x_bf16 = x_dtype == NF4MOE_BF16;
@@ -708,7 +729,8 @@ int grouped_nbit_gemm_dgrad(int quant_type, const void* a, int a_dtype, int64_t 
                             int64_t P, int64_t N, int64_t K, int epilogue, const void* g_pre,
                             int g_dtype, const float* row_scale, const int32_t* scatter,
                             void* out, int out_dtype, void* stream) {
-  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  if (quant_type != kQtNF4 && quant_type != kQtFP4)
+    return fail(NF4MOE_EINVAL, "storage mode %d: the dgrad takes nf4 or fp4 stacks", quant_type);
   return dgrad_impl(quant_type, a, a_dtype, a_rows, gather, gather_div, packed, absmax,
                     expert_offsets, E, P, N, K, epilogue, g_pre, g_dtype, row_scale, scatter,
                     out, out_dtype, stream);
@@ -980,7 +1002,8 @@ int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
                              const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora, void* dx,
                              int dx_dtype, float* d_gu_A, float* d_gu_B, float* d_dn_A,
                              float* d_dn_B, void* workspace, size_t ws_bytes, void* stream) {
-  if (!valid_qtype(quant_type)) return fail(NF4MOE_EINVAL, "unknown storage mode %d", quant_type);
+  if (quant_type != kQtNF4 && quant_type != kQtFP4)
+    return fail(NF4MOE_EINVAL, "storage mode %d: the backward takes nf4 or fp4 stacks", quant_type);
   return backward_impl(quant_type, x, x_dtype, router_logits, dy, dy_dtype, T, H, I, E, k,
                        renormalize, gu_packed, gu_absmax, dn_packed, dn_absmax, gu_lora,
                        dn_lora, dx, dx_dtype, d_gu_A, d_gu_B, d_dn_A, d_dn_B, workspace,

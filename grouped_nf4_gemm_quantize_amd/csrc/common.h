@@ -39,6 +39,8 @@ namespace nf4moe {
 constexpr int kQtNF4 = 0;
 constexpr int kQtFP4 = 1;
 constexpr int kQtMXFP4 = 2;  // e2m1 + e8m0 per 32, low nibble first (own entry points)
+constexpr int kQtINT8 = 3;   // 8-bit codes: int8, value = code / 127 * absmax
+constexpr int kQtFP8 = 4;    // 8-bit codes: fp8 e4m3, value = e4m3(code) / 448 * absmax
 }  // namespace nf4moe
 
 namespace nf4moe {

@@ -89,6 +89,11 @@ constexpr int BPAIR = BN * BK;                       // 512 rows x 64 B = 32768 
 constexpr int RING = OFF_BR + 2 * BPAIR;             // 102400 B
 constexpr int kAbsGroup = 4;                   // steps of absmax per copy (16 B per row)
 constexpr int kMxGroup = 8;                    // MXFP4: steps of scale bytes per copy (2 per step)
+// weight formats (a template parameter of the kernel)
+constexpr int kW4 = 0;   // 4-bit codes through the decode table, fp32 absmax per 64 (nf4, fp4)
+constexpr int kWMx = 1;  // MXFP4: e2m1 codes through the table, e8m0 scale per 32
+constexpr int kWI8 = 2;  // 8-bit int8 codes, fp32 absmax per 64
+constexpr int kWF8 = 3;  // 8-bit fp8 e4m3 codes, fp32 absmax per 64
 
 }  // namespace
 
@@ -173,6 +178,7 @@ __device__ __forceinline__ void issue_abs(const Src& s, int grp, int buf, int wa
 struct Rd {
   uint32_t a[4];   // A fragment of substep s (m-tile 0; + 4096 per m-tile)
   uint32_t b[2];   // packed codes of n-tile 0 in a pair stage, by step parity (+ 2048 per n-tile)
+  uint32_t b8[2];  // 8-bit codes: chunks 2 g2 and 2 g2 + 1 of a one-step stage (+ 2048 per n-tile)
   uint32_t s;      // absmax element of n-tile 0's row (+ 32 rows per n-tile)
   uint32_t ua[2];  // LoRA: A fragment (16x16x32) of this wave's 16 rows, [k half]
   uint32_t ul;     // LoRA: A_e fragment of this lane (k half 0; + 64 B for half 1)
@@ -183,18 +189,28 @@ struct Rd {
 // weights (4 n-tiles x 16 B) and their absmax as an fp16 pair.
 struct StepRegs {
   u32x4 bq[NT];
+  u32x4 bq2[NT];  // 8-bit codes: the second 16 bytes of the lane's 32
   f16x2 sc[NT];
 };
 
-template <bool kMx>
+template <int kW>
 __device__ __forceinline__ void load_step_regs(const char* bst, int step, const Rd& rd,
                                                StepRegs& r) {
   const uint32_t bo = (step & 1) ? rd.b[1] : rd.b[0];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    r.bq[nt] = *reinterpret_cast<const u32x4*>(bst + bo + nt * 2048);
     _Float16 sh;
-    if constexpr (kMx) {
+    if constexpr (kW >= kWI8) {
+      // 32 codes of the lane's k half; scale = absmax / 127 (int8) or / 448 (fp8)
+      r.bq[nt] = *reinterpret_cast<const u32x4*>(bst + rd.b8[0] + nt * 2048);
+      r.bq2[nt] = *reinterpret_cast<const u32x4*>(bst + rd.b8[1] + nt * 2048);
+      const float a = g_sabs[(step / kAbsGroup) & 1][rd.s + nt * 32 * kAbsGroup + step % kAbsGroup];
+      sh = (_Float16)(a / (kW == kWI8 ? 127.0f : 448.0f));
+      r.sc[nt] = f16x2{sh, sh};
+      continue;
+    }
+    r.bq[nt] = *reinterpret_cast<const u32x4*>(bst + bo + nt * 2048);
+    if constexpr (kW == kWMx) {
       // the e8m0 byte of this lane's 32-element block (k half g2 of the step)
       const uint8_t* sb = reinterpret_cast<const uint8_t*>(&g_sabs[(step / kMxGroup) & 1][0]);
       sh = e8m0_to_half(sb[rd.s + nt * 32 * 16 + (step % kMxGroup) * 2]);
@@ -244,12 +260,43 @@ __device__ __forceinline__ void scale_b(const StepRegs& r, const uint32_t (&d)[N
   }
 }
 
+// 8-bit codes of substep S (k = 32 g2 + 8 S .. + 8) -> scaled fp16 operands.
+// int8: each byte b becomes the fp16 1024 + (b ^ 0x80) by placing it under
+// the exponent byte 0x64 (one v_perm per two bytes), minus 1152 = b, exact;
+// fp8 e4m3: the hardware fp8 -> fp16 conversion (exact at scale 1).
+template <int kW, int S>
+__device__ __forceinline__ void decode_b8(const StepRegs& r, f16x8 (&bf)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const u32x4 q = (S >> 1) ? r.bq2[nt] : r.bq[nt];
+    const uint32_t w0 = (S & 1) ? q.z : q.x;
+    const uint32_t w1 = (S & 1) ? q.w : q.y;
+    f16x2 h[4];
+    if constexpr (kW == kWI8) {
+      const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+      const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+      h[0] = u32_as_half2(__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - off;
+      h[1] = u32_as_half2(__builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - off;
+      h[2] = u32_as_half2(__builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - off;
+      h[3] = u32_as_half2(__builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - off;
+    } else {
+      h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+      h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+      h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+      h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    }
+    const u32x4 v = {half2_as_u32(h[0] * r.sc[nt]), half2_as_u32(h[1] * r.sc[nt]),
+                     half2_as_u32(h[2] * r.sc[nt]), half2_as_u32(h[3] * r.sc[nt])};
+    bf[nt] = as_f16x8(v);
+  }
+}
+
 // Substep S of a step: its MFMAs, with A fragments `af` and the raw table
 // words `d` of its weights already in registers (scaled here, one n-tile
 // ahead of use), while the A fragments and table words of the next substep
 // are read -- for S = 3 those of substep 0 of the next step, from the next
 // stage `nst` (valid once the barrier before substep 3 has passed).
-template <int S, int MTV, bool kLora, bool kABf16, bool kMx>
+template <int S, int MTV, bool kLora, bool kABf16, int kW>
 __device__ __forceinline__ void substep(const char* st, const char* nst, const char* nbst,
                                         int next_step, const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
@@ -259,11 +306,11 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
   uint32_t dn[NT][4];
   if constexpr (S < 3) {
     load_a<MTV, kABf16>(st, rd, S + 1, af_n);
-    lut_lookups(cur, S + 1, rd.lane_off, dn);
+    if constexpr (kW < kWI8) lut_lookups(cur, S + 1, rd.lane_off, dn);
   } else {
-    load_step_regs<kMx>(nbst, next_step, rd, nxt);
+    load_step_regs<kW>(nbst, next_step, rd, nxt);
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
-    lut_lookups(nxt, 0, rd.lane_off, dn);
+    if constexpr (kW < kWI8) lut_lookups(nxt, 0, rd.lane_off, dn);
   }
   // LoRA: u[this wave's 16 rows][16 ranks] += X A_e^T, k half S - 1
   if constexpr (kLora && (S == 1 || S == 2)) {
@@ -276,7 +323,8 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
     acc_u = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_u, 0, 0, 0);
   }
   f16x8 bf[NT];
-  scale_b(cur, d, bf);
+  if constexpr (kW >= kWI8) decode_b8<kW, S>(cur, bf);
+  else scale_b(cur, d, bf);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -284,11 +332,12 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
       acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nt], af[mt], acc[mt][nt], 0, 0, 0);
 #pragma unroll
   for (int mt = 0; mt < MTV; ++mt) af[mt] = af_n[mt];
+  if constexpr (kW < kWI8) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[nt][j] = dn[nt][j];
-
+      for (int j = 0; j < 4; ++j) d[nt][j] = dn[nt][j];
+  }
 }
 
 // The k-loop of one tile.  After the barrier of step kb (every wave is done
@@ -306,7 +355,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
 // complete in order.  Pairs and activations are issued at least one full
 // step before use, codes and absmax two.  Past the last step the copies of
 // the last step / pair / group are repeated, so the counts hold throughout.
-template <int MTV, bool kLora, bool kABf16, bool kMx>
+template <int MTV, bool kLora, bool kABf16, int kW>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
                                       int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
                                       f32x4& acc_u) {
@@ -320,7 +369,8 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
   issue_b(src, 0, ring + OFF_BR, wave);
   issue_a<kLora>(src, 0, ring, wave);
   issue_a<kLora>(src, min(1, last), ring + ASTAGE, wave);
-  issue_b(src, min(1, last_pair), ring + OFF_BR + BPAIR, wave);
+  // 8-bit codes: one step per stage (64 bytes of a row), not a step pair
+  issue_b(src, kW >= kWI8 ? min(1, last) : min(1, last_pair), ring + OFF_BR + BPAIR, wave);
   const int lora_live = (lane & 15) < lora_r;
 
   // absmax group 0, pair 0 and step 0's activations complete
@@ -328,18 +378,23 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
   StepRegs cur, nxt;
   f16x8 af[MT];
   uint32_t d[NT][4];
-  load_step_regs<kMx>(g_ring + OFF_BR, 0, rd, cur);
+  load_step_regs<kW>(g_ring + OFF_BR, 0, rd, cur);
   load_a<MTV, kABf16>(g_ring, rd, 0, af);
-  lut_lookups(cur, 0, rd.lane_off, d);
+  if constexpr (kW < kWI8) lut_lookups(cur, 0, rd.lane_off, d);
   for (int kb = 0; kb < nk; ++kb) {
     const int a = kb & 1;
     const char* sp = g_ring + a * ASTAGE;              // step kb's activations
     const char* np = g_ring + (a ^ 1) * ASTAGE;        // step kb + 1's
-    const char* nbp = g_ring + OFF_BR + (((kb + 1) >> 1) & 1) * BPAIR;  // kb + 1's codes
-    substep<0, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<1, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<2, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    if constexpr (kMx) {
+    const char* nbp = g_ring + OFF_BR +
+                      ((kW >= kWI8 ? (kb + 1) : ((kb + 1) >> 1)) & 1) * BPAIR;  // kb + 1's codes
+    substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    if constexpr (kW >= kWI8) {
+      // 8-bit codes: every batch carries the next step's codes and
+      // activations, both needed now
+      wait_vm_barrier<0>();
+    } else if constexpr (kW == kWMx) {
       // MXFP4 scale groups cover 8 steps: batch kb - 1 carried one when it
       // was 5 mod 8
       if (kb & 1) wait_vm_barrier<0>();
@@ -353,10 +408,16 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
       }
     }
     issue_a<kLora>(src, min(kb + 2, last), ring + a * ASTAGE, wave);
-    if (kb & 1) {
+    if constexpr (kW >= kWI8) {
+      issue_b(src, min(kb + 2, last), ring + OFF_BR + a * BPAIR, wave);
+      if ((kb & 3) == 1) {
+        const int grp = (kb + 3) >> 2;
+        issue_abs(src, min(grp, last >> 2), grp & 1, wave);
+      }
+    } else if (kb & 1) {
       const int pn = (kb + 3) >> 1;
       issue_b(src, min(pn, last_pair), ring + OFF_BR + (pn & 1) * BPAIR, wave);
-      if constexpr (kMx) {
+      if constexpr (kW == kWMx) {
         if ((kb & 7) == 5) {
           const int grp = (kb + 3) >> 3;
           issue_abs(src, min(grp, last >> 3), grp & 1, wave);
@@ -366,15 +427,16 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
         issue_abs(src, min(grp, last >> 2), grp & 1, wave);
       }
     }
-    substep<3, MTV, kLora, kABf16, kMx>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
     cur = nxt;
   }
 }
 
 }  // namespace
 
-template <bool kSwiglu, bool kLora, bool kABf16, int kOut, bool kMx>
+template <bool kSwiglu, bool kLora, bool kABf16, int kOut, int kW>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
+  constexpr bool kMx = kW == kWMx;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,6 +446,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
 
   if constexpr (kMx)
     lut_fill<kCopies>(g_lut, g_lstage, c_levels_gemm_mx, tid, NTHREADS, /*low_first=*/true);
+  else if constexpr (kW >= kWI8)
+    __syncthreads();  // 8-bit codes decode without the table
   else
     lut_fill<kCopies>(g_lut, g_lstage, g.qtype == kQtFP4 ? c_levels_gemm_fp4 : c_levels_gemm,
                       tid, NTHREADS);
@@ -404,6 +468,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
 #pragma unroll
   for (int sp2 = 0; sp2 < 2; ++sp2)
     rd.b[sp2] = (wave * BNW + n32) * 64 + (((sp2 * 2 + g2) ^ ((n32 >> 2) & 3)) << 4);
+  // 8-bit stage: weight row l's 64 bytes of one step, chunk c at c ^ ((l >> 2) & 3)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    rd.b8[i] = (wave * BNW + n32) * 64 + (((2 * g2 + i) ^ ((n32 >> 2) & 3)) << 4);
   // absmax element (fp32 index) of n-tile 0's row; MXFP4: its scale byte of
   // k half g2 (16 bytes per row: 8 steps x 2 halves)
   rd.s = kMx ? (wave * BNW + n32) * 16 + g2 : (wave * BNW + n32) * kAbsGroup;
@@ -473,7 +541,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
 
     Src src;
     src.a_rsrc = a_rsrc;
-    const uint32_t b_bytes = (uint32_t)N * (uint32_t)(K / 2);
+    const uint32_t brow = kW >= kWI8 ? (uint32_t)K : (uint32_t)(K / 2);  // code bytes per row
+    const uint32_t b_bytes = (uint32_t)N * brow;
     const uint32_t s_bytes = kMx ? (uint32_t)N * (uint32_t)(K / 32) : (uint32_t)N * (uint32_t)nk * 4u;
     src.b_rsrc = make_rsrc(reinterpret_cast<const char*>(g.packed) + (int64_t)e * b_bytes, b_bytes);
     src.s_rsrc = make_rsrc(reinterpret_cast<const char*>(g.absmax) + (int64_t)e * s_bytes, s_bytes);
@@ -497,7 +566,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     for (int i = 0; i < 4; ++i) {
       const int l = (wave * 4 + i) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((l >> 2) & 3);
-      src.b_off[i] = (uint32_t)weight_row(l, n_idx) * (uint32_t)(K / 2) + c * 16;
+      src.b_off[i] = (uint32_t)weight_row(l, n_idx) * brow + c * 16;
     }
     // absmax groups: the wave's instruction covers rows [64 wave, 64 wave +
     // 64), 16 bytes (kAbsGroup steps) per row
@@ -536,10 +605,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     // every wave is done with the previous tile's stages (and LoRA exchange)
     lds_barrier();
     switch (mtv) {
-      case 1: kloop<1, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      case 2: kloop<2, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      case 3: kloop<3, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      default: kloop<4, kLora, kABf16, kMx>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 1: kloop<1, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 2: kloop<2, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 3: kloop<3, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      default: kloop<4, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
     }
     // every copy has landed and every wave is done with the ring: the
     // epilogue stages its output there
@@ -639,28 +708,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kSwiglu, bool kLora, bool kABf16, bool kMx>
+template <bool kSwiglu, bool kLora, bool kABf16, int kW>
 static void launch_out(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
   switch (g.out_dtype) {
     case kF32:
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF32, kMx>), grid,
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF32, kW>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     case kBF16:
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kBF16, kMx>), grid,
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kBF16, kW>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF16, kMx>), grid,
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiglu, kLora, kABf16, kF16, kW>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
   }
 }
 
-template <bool kSwiglu, bool kLora, bool kMx = false>
+template <bool kSwiglu, bool kLora, int kW = kW4>
 static void launch_a(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
-  if (g.a_bf16) launch_out<kSwiglu, kLora, true, kMx>(g, grid, n_tiles, s);
-  else launch_out<kSwiglu, kLora, false, kMx>(g, grid, n_tiles, s);
+  if (g.a_bf16) launch_out<kSwiglu, kLora, true, kW>(g, grid, n_tiles, s);
+  else launch_out<kSwiglu, kLora, false, kW>(g, grid, n_tiles, s);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t stream) {
@@ -672,9 +741,20 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t strea
   if (grid < 8) grid = 8;
   const dim3 dg((unsigned)grid);
   const bool lora = g.lora_a != nullptr;
-  if (g.qtype == kQtMXFP4) {  // no adapters on MXFP4 stacks (checked by the caller)
-    if (g.swiglu) launch_a<true, false, true>(g, dg, n_tiles, stream);
-    else launch_a<false, false, true>(g, dg, n_tiles, stream);
+  // no adapters on MXFP4 or 8-bit stacks (checked by the caller)
+  if (g.qtype == kQtMXFP4) {
+    if (g.swiglu) launch_a<true, false, kWMx>(g, dg, n_tiles, stream);
+    else launch_a<false, false, kWMx>(g, dg, n_tiles, stream);
+    return hipGetLastError();
+  }
+  if (g.qtype == kQtINT8 || g.qtype == kQtFP8) {
+    if (g.qtype == kQtINT8) {
+      if (g.swiglu) launch_a<true, false, kWI8>(g, dg, n_tiles, stream);
+      else launch_a<false, false, kWI8>(g, dg, n_tiles, stream);
+    } else {
+      if (g.swiglu) launch_a<true, false, kWF8>(g, dg, n_tiles, stream);
+      else launch_a<false, false, kWF8>(g, dg, n_tiles, stream);
+    }
     return hipGetLastError();
   }
   if (g.swiglu) {

@@ -1,4 +1,5 @@
-// NF4 (and fp4) blockwise quantiser for fused expert stacks.
+// Blockwise quantiser for fused expert stacks: NF4, and the fp4, int8 and
+// fp8 storage modes.
 //
 // Experts4bit.from_float quantises the fused gate_up / down stacks to NF4
 // with one absmax per 64 elements (experts4bit-qlora 0.22.0 README,
@@ -16,7 +17,28 @@
 
 namespace nf4moe {
 
-template <bool kBF16, bool kFP4>
+// fp32 y with |y| <= 448 -> its nearest fp8 e4m3 code, ties to the even
+// mantissa: below 2^-6 the subnormal steps of 2^-9 (a rint of y * 512, whose
+// result 8 is the smallest normal), else the fp32 mantissa rounded to 3 bits
+// (a carry moves into the exponent).  Zero of either sign gives code 0.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float ay = fabsf(y);
+  uint32_t c;
+  if (ay < 0.015625f) {
+    c = (uint32_t)__builtin_rintf(ay * 512.0f);
+  } else {
+    const uint32_t u = __float_as_uint(ay);
+    const uint32_t e = (u >> 23) - 120u;  // fp32 bias 127 -> e4m3 bias 7
+    const uint32_t m = u & 0x7fffffu;
+    c = (e << 3) + ((m + 0x7ffffu + ((m >> 20) & 1u)) >> 20);
+  }
+  return c == 0u ? 0u : (sign | c);
+}
+
+// kQ: 0 nf4, 1 fp4 (4-bit codes, two per byte), 2 int8, 3 fp8 e4m3 (one
+// byte per element).
+template <bool kBF16, int kQ>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const void* __restrict__ w, int64_t nblocks, uint8_t* __restrict__ packed,
     float* __restrict__ absmax, int32_t* __restrict__ nonfinite_flag,
@@ -64,11 +86,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     uint32_t codes[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t c = kFP4 ? 0u : 7u;  // all-zero block: the zero level (+0 for fp4)
+      uint32_t c = kQ == 0 ? 7u : 0u;  // all-zero block: the zero level / code 0
       if (a != 0.f) {
         const float xn = x[i] / a;  // IEEE fp32 division (no fast-math)
         c = 0u;
-        if constexpr (kFP4) {
+        if constexpr (kQ == 2) {
+          c = (uint32_t)(int)__builtin_rintf(xn * 127.0f) & 0xffu;
+        } else if constexpr (kQ == 3) {
+          c = e4m3_code(xn * 448.0f);
+        } else if constexpr (kQ == 1) {
           const float ax = fabsf(xn);
 #pragma unroll
           for (int j = 0; j < 7; ++j) c += (ax > t[j]) ? 1u : 0u;
@@ -81,9 +107,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       codes[i] = c;
     }
     if (live) {
-      const uint32_t b01 = (codes[0] << 4) | codes[1];
-      const uint32_t b23 = (codes[2] << 4) | codes[3];
-      *reinterpret_cast<uint16_t*>(packed + e0 / 2) = (uint16_t)(b01 | (b23 << 8));
+      if constexpr (kQ >= 2) {
+        *reinterpret_cast<uint32_t*>(packed + e0) =
+            codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
+      } else {
+        const uint32_t b01 = (codes[0] << 4) | codes[1];
+        const uint32_t b23 = (codes[2] << 4) | codes[3];
+        *reinterpret_cast<uint16_t*>(packed + e0 / 2) = (uint16_t)(b01 | (b23 << 8));
+      }
       if (sub == 0) absmax[blk] = a;
     }
   }
@@ -100,22 +131,18 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t nelem,
   const int64_t cap = (int64_t)num_cus * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  const bool fp4 = thr.qtype == kQtFP4;
-  if (w_dtype == kBF16) {
-    if (fp4)
-      hipLaunchKernelGGL((quantize_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, w, nblocks, packed, absmax, flag, thr);
-    else
-      hipLaunchKernelGGL((quantize_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, w, nblocks, packed, absmax, flag, thr);
-  } else {
-    if (fp4)
-      hipLaunchKernelGGL((quantize_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, w, nblocks, packed, absmax, flag, thr);
-    else
-      hipLaunchKernelGGL((quantize_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, w, nblocks, packed, absmax, flag, thr);
+  const dim3 g((unsigned)grid);
+  const bool bf = w_dtype == kBF16;
+#define NF4MOE_QLAUNCH(B, Q) \
+  hipLaunchKernelGGL((quantize_kernel<B, Q>), g, dim3(256), 0, stream, w, nblocks, packed, \
+                     absmax, flag, thr)
+  switch (thr.qtype) {
+    case kQtFP4: if (bf) NF4MOE_QLAUNCH(true, 1); else NF4MOE_QLAUNCH(false, 1); break;
+    case kQtINT8: if (bf) NF4MOE_QLAUNCH(true, 2); else NF4MOE_QLAUNCH(false, 2); break;
+    case kQtFP8: if (bf) NF4MOE_QLAUNCH(true, 3); else NF4MOE_QLAUNCH(false, 3); break;
+    default: if (bf) NF4MOE_QLAUNCH(true, 0); else NF4MOE_QLAUNCH(false, 0); break;
   }
+#undef NF4MOE_QLAUNCH
   return hipGetLastError();
 }
 

@@ -303,9 +303,22 @@ int moe_expert_backward(const void* x, int x_dtype, const float* router_logits,
  *                  x/absmax, nearest magnitude level (an exact tie goes to
  *                  the even index), an all-zero block stores code 0.  The
  *                  pages print no fp4 values; this is the OCP e2m1 format.
- * An unknown mode returns NF4MOE_EINVAL. */
+ *   NF4MOE_QT_INT8 8-bit blockwise: one byte per element (packed is
+ *                  [E, N, K]), code = round-half-even(x/absmax * 127) as
+ *                  int8, value = code / 127 * absmax;
+ *   NF4MOE_QT_FP8  8-bit blockwise: one byte per element, code = the
+ *                  nearest OCP fp8 e4m3 value of x/absmax * 448 (ties to the
+ *                  even mantissa; zero of either sign is code 0), value =
+ *                  e4m3(code) / 448 * absmax.
+ * The 8-bit modes have no 16-level codebook (nbit_codebook returns
+ * NF4MOE_EINVAL), run the grouped kernels for every T, and take no adapters;
+ * the dgrad and the backward take nf4 and fp4 only.  The pages name int8 and
+ * fp8 blockwise modes of ExpertsNbit but not their maps; these are the plain
+ * absmax-scaled readings.  An unknown mode returns NF4MOE_EINVAL. */
 #define NF4MOE_QT_NF4 0
 #define NF4MOE_QT_FP4 1
+#define NF4MOE_QT_INT8 3
+#define NF4MOE_QT_FP8 4
 int nbit_codebook(int quant_type, float* out16);  /* [host] levels by code */
 int nbit_quantize_experts(int quant_type, const void* w, int w_dtype, int64_t E,
                           int64_t N, int64_t K, int blocksize, uint8_t* packed,

@@ -74,7 +74,7 @@ def test_nbit_entry_points_reject_unknown_modes(lib):
     assert "storage mode" in _last(lib)
     assert lib.grouped_nbit_gemm(-1, FAKE, 2, 8, None, 1, FAKE, FAKE, FAKE, 1, 8, 64, 64,
                                  None, 0, None, None, FAKE, 2, None) == -1
-    assert lib.moe_expert_forward_nbit(3, FAKE, 1, FAKE, 1, 64, 64, 8, 2, 1, FAKE, FAKE,
+    assert lib.moe_expert_forward_nbit(9, FAKE, 1, FAKE, 1, 64, 64, 8, 2, 1, FAKE, FAKE,
                                        FAKE, FAKE, None, None, FAKE, 1, FAKE, 1 << 20,
                                        None) == -1
     # a known mode reaches the usual validation (blocksize)
