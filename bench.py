@@ -20,6 +20,7 @@ I=1024, top-8, T=4096 tokens); the value is its algorithmic TFLOP/s
                 replayed from a HIP graph;
   mxfp4         the same prefill layer on released-MXFP4-format stacks
                 (e2m1 + e8m0 bytes multiplied in place);
+  storage_modes the same layer with the stacks stored as fp4, int8, fp8;
   backward      the QLoRA training backward of a layer (olmoe without
                 adapters, qlora with r=8 adapters): time per backward and
                 its two dgrad kernels timed alone;
@@ -452,6 +453,53 @@ def bench_mxfp4(dev, steps: int):
     return out
 
 
+def bench_storage_modes(dev, steps: int):
+    """The olmoe-shaped prefill layer with its stacks stored in each of the
+    other modes (quantised on the GPU from the same fp32 weights)."""
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    cfg = synth.config("olmoe")
+    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
+    lg = torch.from_numpy(synth.router_logits(cfg)).to(dev)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for qt in ("fp4", "int8", "fp8"):
+        st = {}
+        for which, (n, kk) in (("gu", (2 * cfg.I, cfg.H)), ("dn", (cfg.H, cfg.I))):
+            per = 1 if qt in binding.EIGHT_BIT else 2
+            p = torch.empty((cfg.E, n, kk // per), dtype=torch.uint8, device=dev)
+            a = torch.empty((cfg.E, n, kk // 64), dtype=torch.float32, device=dev)
+            for e0 in range(0, cfg.E, 16):
+                ex = range(e0, min(e0 + 16, cfg.E))
+                w = torch.from_numpy(synth.stack_weights(cfg, which, 0, ex)).to(dev)
+                pp, aa = binding.quantize(w, quant_type=qt)
+                p[e0:e0 + len(ex)] = pp
+                a[e0:e0 + len(ex)] = aa
+                del w
+            st[which] = (p, a)
+        gp, ga = st["gu"]
+        dp, da = st["dn"]
+
+        def step():
+            binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, y=y, workspace=ws,
+                                quant_type=qt)
+
+        for _ in range(3):
+            step()
+        ms = time_events(step, max(steps, 5), stream)
+        out[qt] = {"us_per_forward": round(ms * 1e3, 2),
+                   "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
+                   "stack_bytes": int(sum(t.numel() * t.element_size() for t in (gp, ga, dp, da)))}
+        del st, gp, ga, dp, da
+        torch.cuda.empty_cache()
+    return out
+
+
 def control_lane(cfg, st, x16, off, sp, stream, iters: int):
     """Dequantise-then-GEMM control (a benchmark control, never a product
     path): the whole stack is dequantised to fp16 with plain torch ops, then
@@ -534,7 +582,8 @@ def main() -> int:
                     help="skip the training-backward section")
     ap.add_argument("--backward-workloads", default="olmoe,qlora",
                     help="comma-separated workloads of the backward section")
-    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 section")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the MXFP4 and storage-mode sections")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -691,6 +740,8 @@ def main() -> int:
     if not args.no_mxfp4:
         result["mxfp4"] = bench_mxfp4(dev, args.steps)
         log(f"[bench] mxfp4 {result['mxfp4']}")
+        result["storage_modes"] = bench_storage_modes(dev, args.steps)
+        log(f"[bench] storage modes {result['storage_modes']}")
     bwd_names = [n_ for n_ in args.backward_workloads.split(",") if n_]
     if not args.no_backward and bwd_names:
         result["backward"] = {n_: bench_backward(n_, dev, args.steps) for n_ in bwd_names}
