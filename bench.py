@@ -150,7 +150,7 @@ def _counter_means(directory: str, counter: str):
             continue
         name = r["Kernel_Name"]
         v = float(r["Counter_Value"])
-        if "grouped_gemm_kernel<true" in name:
+        if "grouped_gemm_kernel<true, false, false, 2, 0>" in name:  # the NF4 gate_up
             gemm.append(v)
         elif "copyBuffer" in name:
             copy.append(v)

@@ -630,8 +630,9 @@ static int dgrad_common(const void* a, int a_dtype, int64_t a_rows, const int32_
                         int gather_div, const uint8_t* packed, const float* absmax,
                         const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
                         int epilogue, const void* g_pre, int g_dtype, const float* row_scale,
-                        const int32_t* scatter, const float* lora_v, const nf4moe_lora* lora,
-                        void* out, int out_dtype, int qt, hipStream_t stream) {
+                        const int32_t* rs_idx, const int32_t* scatter, const float* lora_v,
+                        const nf4moe_lora* lora, void* out, int out_dtype, int qt,
+                        hipStream_t stream) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
@@ -649,6 +650,7 @@ static int dgrad_common(const void* a, int a_dtype, int64_t a_rows, const int32_
   d.N = (int)N;
   d.K = (int)K;
   d.row_scale = row_scale;
+  d.rs_idx = rs_idx;
   d.scatter = scatter;
   d.epilogue = epilogue == NF4MOE_EPI_SWIGLU_BWD ? kDgradEpiSwigluBwd : kDgradEpiNone;
   d.g = g_pre;
@@ -707,7 +709,8 @@ static int dgrad_impl(int qt, const void* a, int a_dtype, int64_t a_rows,
   if (P == 0) return ok();
   int st = dgrad_common(a, a_dtype, a_rows, gather, gather_div, packed, absmax,
                         expert_offsets, E, P, N, K, epilogue, g_pre, g_dtype, row_scale,
-                        scatter, nullptr, nullptr, out, out_dtype, qt, (hipStream_t)stream);
+                        nullptr, scatter, nullptr, nullptr, out, out_dtype, qt,
+                        (hipStream_t)stream);
   if (st != NF4MOE_OK) return st;
   return ok();
 }
@@ -934,9 +937,12 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     if (st != NF4MOE_OK) return st;
   }
 
-  // 4. dG = SwiGLU backward of (w * dy_t) W_dn (+ LoRA), fp16
+  // 4. dG1 = SwiGLU backward of dy_t W_dn (+ LoRA) for a unit routing
+  //    weight, fp16.  Everything downstream is linear in w, so w is applied
+  //    later as a row scale: stored fp16 gradients then keep their precision
+  //    however small a pair's weight is.
   st = dgrad_common(dyh, NF4MOE_F16, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
-                    NF4MOE_EPI_SWIGLU_BWD, G, NF4MOE_F16, wts, nullptr,
+                    NF4MOE_EPI_SWIGLU_BWD, G, NF4MOE_F16, nullptr, nullptr, nullptr,
                     dn_lora ? v_dn : nullptr, dn_lora, dG, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
 
@@ -947,8 +953,8 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     if (st != NF4MOE_OK) return st;
   }
 
-  // 6. gate_up adapter: u = x A_gu^T, then one pass over dG for v = dG B_gu
-  //    and dB_gu = s sum dG u^T
+  // 6. gate_up adapter: u = x A_gu^T, then one pass over dG1 for
+  //    v1 = dG1 B_gu and dB_gu = s sum w dG1 u^T
   if (gu_lora) {
     const int bf = gu_lora->dtype == NF4MOE_BF16;
     err = launch_lora_to_f16(gu_lora->A, bf, 0, E, H, r, a16_gu, cus, s);
@@ -958,23 +964,24 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, a16_gu, u_gu, nullptr, nullptr, nullptr,
                    nullptr, nullptr, 0.f, 0, cus, s);
     if (st != NF4MOE_OK) return st;
-    st = lora_pass(dG, 0, nullptr, 1, offs, E, P, 2 * I, r, bt_gu, v_gu, nullptr, nullptr, u_gu,
+    st = lora_pass(dG, 0, nullptr, 1, offs, E, P, 2 * I, r, bt_gu, v_gu, wts, sorted, u_gu,
                    part, d_gu_B, gu_lora->scale, 0, cus, s);
     if (st != NF4MOE_OK) return st;
   }
 
   // 7. per-pair input gradients dG W_gu (+ LoRA) in pair order, then the sum
   //    over each token's k pairs
+  // (the routing weight w of each pair applied here as the row scale)
   st = dgrad_common(dG, NF4MOE_F16, P, nullptr, 1, gu_packed, gu_absmax, offs, E, P,
-                    2 * (int64_t)I, H, NF4MOE_EPI_NONE, nullptr, 0, nullptr, sorted,
+                    2 * (int64_t)I, H, NF4MOE_EPI_NONE, nullptr, 0, wts, sorted, sorted,
                     gu_lora ? v_gu : nullptr, gu_lora, dXp, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
   err = launch_combine(dXp, nullptr, T, k, H, dx, dx_dtype, cus, s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
 
-  // 8. dA_gu = s sum v x^T
+  // 8. dA_gu = s sum w v1 x^T
   if (gu_lora) {
-    st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, nullptr, nullptr, nullptr, nullptr, v_gu,
+    st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, nullptr, nullptr, wts, sorted, v_gu,
                    part, d_gu_A, gu_lora->scale, 1, cus, s);
     if (st != NF4MOE_OK) return st;
   }

@@ -427,7 +427,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
       const int grow = row0 + (tid < rows_valid ? tid : 0);
       d_orow[par][tid] = g.scatter ? g.scatter[grow] : grow;
       float rs = 1.0f;
-      if (g.row_scale) rs = g.row_scale[g.gather ? g.gather[grow] : grow];
+      if (g.row_scale)
+        rs = g.row_scale[g.rs_idx ? g.rs_idx[grow] : (g.gather ? g.gather[grow] : grow)];
       d_rscale[par][tid] = rs;
     }
 

@@ -121,7 +121,9 @@ struct DgradArgs {
   int64_t P;
   int N;                   // stack rows = contraction
   int K;                   // output columns
-  const float* row_scale;  // nullable, row i scaled by row_scale[gather ? gather[i] : i]
+  const float* row_scale;  // nullable, row i scaled by row_scale[idx(i)], idx(i) =
+                           // rs_idx[i] if rs_idx, else gather[i] if gather, else i
+  const int32_t* rs_idx;   // nullable
   const int32_t* scatter;  // nullable: output row of row i
   int epilogue;
   const void* g;           // SwiGLU backward: pre-activation rows [P, 2K] (row i)

@@ -116,6 +116,8 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
   __shared__ __attribute__((aligned(16))) char nat[kLoraTile * kPitch];  // [row][col]
   __shared__ __attribute__((aligned(16))) char tr[64 * kPitch];         // [col][row]
   __shared__ __attribute__((aligned(16))) _Float16 qt[16][kLoraTile + 8];  // [rank][row]
+  __shared__ float qf[16][kLoraTile];  // the same in fp32, before scaling
+  __shared__ float qexp[16][2];        // per rank: 2^-e applied, 2^e to undo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   build_tile_table<256, kLoraTile>(a.offsets, a.E, tiles, wsum, tid);
@@ -136,7 +138,11 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
       srcs[tid] = a.gather ? a.gather[i] / a.gather_div : i;
     }
     if constexpr (kGrad) {
-      // q^T of the tile with the row scale folded in, fp16
+      // q^T of the tile with the row scale folded in.  Each rank's column is
+      // scaled by a power of two that brings its largest magnitude into
+      // [1/2, 1) before the fp16 conversion (undone on the fp32 result), so
+      // small row scales (a tiny routing weight) stay out of fp16's
+      // subnormal range
       for (int u = tid; u < 16 * kLoraTile; u += 256) {
         const int j = u / kLoraTile, rr = u % kLoraTile;
         float v = 0.f;
@@ -145,7 +151,21 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
           const float rs = a.rs ? a.rs[a.rs_idx ? a.rs_idx[i] : i] : 1.0f;
           v = a.q[i * a.r + j] * rs;
         }
-        qt[j][rr] = (_Float16)v;
+        qf[j][rr] = v;
+      }
+      __syncthreads();
+      if (tid < 16) {
+        float m = 0.f;
+        for (int rr = 0; rr < kLoraTile; ++rr) m = fmaxf(m, fabsf(qf[tid][rr]));
+        int e = 0;
+        if (m > 0.f) frexpf(m, &e);
+        qexp[tid][0] = ldexpf(1.0f, -e);
+        qexp[tid][1] = ldexpf(1.0f, e);
+      }
+      __syncthreads();
+      for (int u = tid; u < 16 * kLoraTile; u += 256) {
+        const int j = u / kLoraTile, rr = u % kLoraTile;
+        qt[j][rr] = (_Float16)(qf[j][rr] * qexp[j][0]);
       }
     }
     __syncthreads();
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int j = 4 * g4 + t;
-          if (j < a.r) part[(int64_t)j * a.C] = accg[t];
+          if (j < a.r) part[(int64_t)j * a.C] = accg[t] * qexp[j][1];
         }
       }
     }

@@ -210,10 +210,20 @@ def _backward_case(gpu_lib, cfg, dx_dtype=torch.bfloat16, x_dtype=torch.bfloat16
 
 
 def _check_lora_grads(grads, ref, what):
+    """Adapter gradients: each expert's block is its own output, so the
+    tolerance applies per expert that received rows (relative to that
+    expert's RMS); an expert without rows must get exact zeros."""
     for name in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
-        if name in grads:
-            assert_parity(grads[name], ref[name], fro_tol=5e-3, maxabs_tol=2e-2,
-                          what=f"{what} {name}", out_dtype="f32")
+        if name not in grads:
+            continue
+        g, r = grads[name], ref[name]
+        assert metrics(g, r, "f32")["fro"] <= 5e-3, (what, name)
+        for e in range(r.shape[0]):
+            if not np.any(r[e]):
+                assert not np.any(g[e]), (what, name, e)
+                continue
+            assert_parity(g[e], r[e], fro_tol=5e-3, maxabs_tol=2e-2,
+                          what=f"{what} {name} expert {e}", out_dtype="f32")
 
 
 @pytest.mark.parametrize("variant", ["plain", "lora", "norenorm", "f16_in_f32_out"])
@@ -321,3 +331,41 @@ def test_backward_full_size_sampled(gpu_lib, name):
         for nm in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
             assert_parity(host(grads[nm][e]), res[nm], fro_tol=5e-3, maxabs_tol=2e-2,
                           what=f"{name} expert {e} {nm}", out_dtype="f32")
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(40, 300, 4, False), (96, 8, 2, True), (1, 16, 4, False)])
+def test_backward_degenerate_routings(gpu_lib, T, E, k, skew):
+    """Many empty experts; every token on the same experts (one expert holds
+    all rows); a single token.  dx and the adapter gradients vs the oracle."""
+    cfg = synth.config("tiny", T=T, E=E, k=k, lora_r=8, lora_alpha=16.0)
+    gp, ga, dp, da = _stacks(cfg)
+    x = synth.activations(cfg)
+    lg = synth.router_logits(cfg)
+    if skew:
+        lg = lg.copy()
+        lg[:, 3] += 50.0
+        lg[:, 5] += 40.0
+    dy = synth.output_grad(cfg)
+    glo, dlo, glo_r, dlo_r = _lora(cfg)
+    dx, grads = gpu_lib.moe_backward(gpu(x, torch.bfloat16), gpu(lg), gpu(dy, torch.bfloat16),
+                                     cfg.k, gpu(gp), gpu(ga), gpu(dp), gpu(da), glo, dlo,
+                                     dx_dtype=torch.float32)
+    ref = oracle.moe_backward(x, lg, dy, cfg.k, gp, ga, dp, da, glo_r, dlo_r)
+    assert_parity(host(dx), ref["dx"], what=f"degenerate T={T} E={E}", out_dtype="f32")
+    _check_lora_grads({n: host(v) for n, v in grads.items()}, ref, "degenerate")
+    used = set(ref["info"]["ids"].reshape(-1).tolist())
+    for e in range(E):
+        if e not in used:
+            assert torch.count_nonzero(grads["dA_gu"][e]) == 0
+
+
+def test_dgrad_minimal_contraction_and_width(gpu_lib):
+    """N = K = 64: one contraction step, one absmax block per row."""
+    rng = np.random.default_rng(29)
+    packed, absmax = _random_stack(rng, 2, 64, 64)
+    offsets = np.array([0, 5, 9], dtype=np.int32)
+    a = rng.standard_normal((9, 64)).astype(np.float16)
+    out = gpu_lib.grouped_dgrad(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), 9,
+                                out_dtype=torch.float32)
+    ref = oracle.grouped_dgrad(a.astype(np.float64), packed, absmax, offsets)
+    assert_parity(host(out), ref, fro_tol=2e-3, maxabs_tol=2e-2, what="N=K=64", out_dtype="f32")
