@@ -570,8 +570,10 @@ def control_lane(cfg, st, x16, off, sp, stream, iters: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: about 30 ms of untimed warmup (the clock ramps up under load
+    # over the first tens of milliseconds) and 55 ms of timed forwards
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="olmoe",
                     choices=["olmoe", "qwen3_zipf", "qlora"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
