@@ -369,3 +369,41 @@ def test_dgrad_minimal_contraction_and_width(gpu_lib):
                                 out_dtype=torch.float32)
     ref = oracle.grouped_dgrad(a.astype(np.float64), packed, absmax, offsets)
     assert_parity(host(out), ref, fro_tol=2e-3, maxabs_tol=2e-2, what="N=K=64", out_dtype="f32")
+
+
+def test_backward_in_hip_graph_replays(gpu_lib):
+    """The layer backward (with adapters) captured once and replayed, with
+    eager work and clearing of every buffer between replays: each replay
+    equals the eager result bit for bit."""
+    cfg = synth.config("tiny", lora_r=8, lora_alpha=16.0)
+    gp, ga, dp, da = _stacks(cfg)
+    x = gpu(synth.activations(cfg), torch.bfloat16)
+    lg = gpu(synth.router_logits(cfg))
+    dy = gpu(synth.output_grad(cfg), torch.bfloat16)
+    glo, dlo, _, _ = _lora(cfg)
+    st = (gpu(gp), gpu(ga), gpu(dp), gpu(da))
+    dx_e, g_e = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo)
+    dx_e, g_e = dx_e.clone(), {k_: v.clone() for k_, v in g_e.items()}
+    nbytes = gpu_lib.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, 8)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    dx = torch.empty_like(dx_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _, grads = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo, dx=dx, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _, grads = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo, dx=dx, workspace=ws)
+    for _ in range(3):
+        dx.zero_()
+        ws.zero_()
+        for v in grads.values():
+            v.fill_(7.0)
+        gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo)  # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx, dx_e)
+        for k_, v in grads.items():
+            assert torch.equal(v, g_e[k_]), k_
