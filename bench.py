@@ -250,17 +250,23 @@ def cpu_baseline(cfg, seconds_target: float = 10.0):
     }
 
 
-def bench_decode(dev, steps: int):
-    """48 distinct decode layers (8 routed experts each) replayed from a graph."""
+def bench_decode(dev, steps: int, mx: bool = False):
+    """48 distinct decode layers (8 routed experts each) replayed from a graph
+    (NF4 stacks, or released-format MXFP4 stacks with ``mx``)."""
     import numpy as np
     import torch
 
     from grouped_nf4_gemm_quantize_amd import binding, synth
 
     cfg = synth.config("decode")
-    st = gpu_stacks(cfg, dev)
-    gp, ga = st["gu"]
-    dp, da = st["dn"]
+    if mx:
+        gp, ga = (torch.from_numpy(t).to(dev) for t in synth.mxfp4_stack(cfg, "gu"))
+        dp, da = (torch.from_numpy(t).to(dev) for t in synth.mxfp4_stack(cfg, "dn"))
+        st = None
+    else:
+        st = gpu_stacks(cfg, dev)
+        gp, ga = st["gu"]
+        dp, da = st["dn"]
     layers = []
     for l in range(DECODE_LAYERS):
         lg = np.random.default_rng(1000 + l).standard_normal((1, cfg.E), dtype=np.float32)
@@ -275,8 +281,12 @@ def bench_decode(dev, steps: int):
 
     def run_all():
         for L in layers:
-            binding.moe_forward(x, L["lg"], cfg.k, L["gp"], L["ga"], L["dp"], L["da"],
-                                y=L["y"], workspace=L["ws"])
+            if mx:
+                binding.moe_forward_mxfp4(x, L["lg"], cfg.k, L["gp"], L["ga"], L["dp"], L["da"],
+                                          y=L["y"], workspace=L["ws"])
+            else:
+                binding.moe_forward(x, L["lg"], cfg.k, L["gp"], L["ga"], L["dp"], L["da"],
+                                    y=L["y"], workspace=L["ws"])
 
     stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(stream):
@@ -291,14 +301,18 @@ def bench_decode(dev, steps: int):
         for _ in range(3):
             g.replay()
         graph_ms = time_events(g.replay, max(steps, 10), stream)
-    per_layer_bytes = cfg.k * (2 * cfg.I * cfg.H + cfg.H * cfg.I) * 9 // 16
+    # packed bytes + scales of the k routed experts: 4 bits + 4 bytes per 64
+    # (NF4), 4 bits + 1 byte per 32 (MXFP4)
+    per_elem_16ths = 9 if not mx else 10
+    per_layer_bytes = cfg.k * (2 * cfg.I * cfg.H + cfg.H * cfg.I) * per_elem_16ths // 16
     gbs = DECODE_LAYERS * per_layer_bytes / (graph_ms * 1e-3) / 1e9
     out = {
         "metric": "packed-weight GB/s (decode M=1)",
         "value": round(gbs, 2),
         "unit": "GB/s",
-        "workload": (f"Qwen3-30B-A3B-shaped decode layer x{DECODE_LAYERS} distinct stacks "
-                     f"(E={cfg.E}, H={cfg.H}, I={cfg.I}, top-{cfg.k}, T=1), HIP graph replay"),
+        "workload": (f"Qwen3-30B-A3B-shaped decode layer x{DECODE_LAYERS} distinct "
+                     f"{'MXFP4' if mx else 'NF4'} stacks (E={cfg.E}, H={cfg.H}, I={cfg.I}, "
+                     f"top-{cfg.k}, T=1), HIP graph replay"),
         "bytes_per_layer": per_layer_bytes,
         "us_per_layer": round(graph_ms * 1e3 / DECODE_LAYERS, 3),
         "us_per_layer_eager": round(eager_ms * 1e3 / DECODE_LAYERS, 3),
@@ -450,6 +464,7 @@ def bench_mxfp4(dev, steps: int):
     }
     del gb, gs, db, ds, ws, h
     torch.cuda.empty_cache()
+    out["decode"] = bench_decode(dev, steps, mx=True)
     return out
 
 

@@ -536,7 +536,7 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
 
   if ((gu_lora != nullptr || dn_lora != nullptr) && (is_8bit(qt) || qt == kQtMXFP4))
     return fail(NF4MOE_EINVAL, "adapters are supported on nf4 and fp4 stacks only");
-  if (qt != kQtMXFP4 && !is_8bit(qt) && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
+  if (!is_8bit(qt) && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
     GemvArgs g{};
     g.x = x;
     g.x_bf16 = x_dtype == NF4MOE_BF16;

@@ -20,7 +20,8 @@
 //
 // Split-K inside a wave: lane l takes the 32-weight chunks l, l+64, ... of a
 // row (16 packed bytes = one 16-byte load; a chunk is half of one 64-block so
-// it needs one absmax), decodes them through the LDS byte->half2 table
+// it needs one absmax -- or, for MXFP4 stacks, exactly one 32-block with its
+// e8m0 scale, applied in fp32), decodes them through the LDS byte->half2 table
 // (common.h) and multiplies with v_dot2_f32_f16 against fp16 activations held
 // in LDS; the 64 partial sums are reduced across the wave.
 
@@ -32,6 +33,7 @@ namespace nf4moe {
 
 __constant__ float c_levels_gemv[16] = NF4MOE_LEVELS_INIT;
 __constant__ float c_levels_gemv_fp4[16] = NF4MOE_FP4_LEVELS_INIT;
+__constant__ float c_levels_gemv_mx[16] = NF4MOE_E2M1_VALUES_INIT;
 
 namespace {
 constexpr int kCopies = 32;
@@ -72,6 +74,26 @@ __device__ __forceinline__ void store1(void* out, int64_t idx, float v) {
   } else {
     reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
   }
+}
+
+// The scale of chunk c (32 weights) of a row: the fp32 absmax of its 64-block,
+// or for MXFP4 stacks the e8m0 byte of its own 32-block as 2^(s - 127) in
+// fp32 (exact over the whole e8m0 range; 255 is NaN).
+__device__ __forceinline__ float chunk_scale(const float* absmax, int64_t row, int chunks,
+                                             int c, bool mx) {
+  if (mx) {
+    const uint32_t b = reinterpret_cast<const uint8_t*>(absmax)[row * chunks + c];
+    return b == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)b - 127);
+  }
+  return absmax[row * (chunks / 2) + (c >> 1)];
+}
+
+__device__ __forceinline__ void fill_table(uint32_t* lut, uint16_t* stage, int qtype, int tid) {
+  if (qtype == kQtMXFP4)
+    lut_fill<kCopies>(lut, stage, c_levels_gemv_mx, tid, kThreads, /*low_first=*/true);
+  else
+    lut_fill<kCopies>(lut, stage, qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv, tid,
+                      kThreads);
 }
 
 // 16-bit activation -> fp16 (bf16 rounds to nearest even; fp16 passes through)
@@ -115,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
   // this wave's items, every load issued before any arithmetic
   const int chunks = H / 32;
   const int64_t row_bytes = H / 2;
-  const int64_t row_blocks = H / 64;
+  const bool mx = g.qtype == kQtMXFP4;
   const int nw = gridDim.x * kWaves;
   const int items = k * I;
   const int q0 = blockIdx.x * kWaves + wave;
@@ -136,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
       if (c >= chunks) c = chunks - 1;
       qg[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + rg * row_bytes + c * 16);
       qu[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + ru * row_bytes + c * 16);
-      sg[it][m] = g.gu_absmax[rg * row_blocks + (c >> 1)];
-      su[it][m] = g.gu_absmax[ru * row_blocks + (c >> 1)];
+      sg[it][m] = chunk_scale(g.gu_absmax, rg, chunks, c, mx);
+      su[it][m] = chunk_scale(g.gu_absmax, ru, chunks, c, mx);
     }
   }
 
@@ -152,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
       s_x[i0 + 3] = to_f16(xr[p].y >> 16, g.x_bf16);
     }
   }
-  lut_fill<kCopies>(s_lut, s_stage, g.qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv, tid, kThreads);  // ends with a barrier
+  fill_table(s_lut, s_stage, g.qtype, tid);  // ends with a barrier
 
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
   _Float16* hout = reinterpret_cast<_Float16*>(g.hbuf);
@@ -194,8 +216,9 @@ __global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
   // this lane's chunks of the concatenated K (the same for every output row)
   const int cps = I / 32;  // chunks per slot
   const int total = k * cps;
+  const bool mx = g.qtype == kQtMXFP4;
   int64_t pk_off[kMaxChunksPerLane];
-  int64_t am_off[kMaxChunksPerLane];
+  int64_t am_off[kMaxChunksPerLane];  // absmax element, or scale byte for MXFP4
   int h_off[kMaxChunksPerLane];
   int nc = 0;
 #pragma unroll
@@ -209,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
     if (cc < total) {
       const int c = cc - j * cps;
       pk_off[m] = (int64_t)e * H * (I / 2) + c * 16;
-      am_off[m] = (int64_t)e * H * (I / 64) + (c >> 1);
+      am_off[m] = mx ? (int64_t)e * H * (I / 32) + c : (int64_t)e * H * (I / 64) + (c >> 1);
       h_off[m] = j * I + c * 32;
       nc = m + 1;
     }
@@ -222,12 +245,17 @@ __global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
   float s[kMaxChunksPerLane];
   auto load_row = [&](int row) {
     const int64_t prow = (int64_t)row * (I / 2);
-    const int64_t arow = (int64_t)row * (I / 64);
+    const int64_t arow = (int64_t)row * (mx ? I / 32 : I / 64);
 #pragma unroll
     for (int m = 0; m < kMaxChunksPerLane; ++m) {
       if (m < nc) {
         q[m] = *reinterpret_cast<const u32x4*>(g.dn_packed + pk_off[m] + prow);
-        s[m] = g.dn_absmax[am_off[m] + arow];
+        if (mx) {
+          const uint32_t b = reinterpret_cast<const uint8_t*>(g.dn_absmax)[am_off[m] + arow];
+          s[m] = b == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)b - 127);
+        } else {
+          s[m] = g.dn_absmax[am_off[m] + arow];
+        }
       }
     }
   };
@@ -237,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
   const _Float16* hin = reinterpret_cast<const _Float16*>(g.hbuf);
   for (int i = tid * 8; i < k * I; i += kThreads * 8)
     *reinterpret_cast<u32x4*>(s_h + i) = *reinterpret_cast<const u32x4*>(hin + i);
-  lut_fill<kCopies>(s_lut, s_stage, g.qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv, tid, kThreads);  // ends with a barrier
+  fill_table(s_lut, s_stage, g.qtype, tid);  // ends with a barrier
 
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
   for (; n < H; n += nw) {

@@ -183,9 +183,13 @@ def mxfp4_stack(cfg: LayerConfig, which: str, seed: int = 0):
     child = _streams(seed)["mx"].spawn(2)[0 if which == "gu" else 1]
     rng = np.random.default_rng(child)
     N, K = (2 * cfg.I, cfg.H) if which == "gu" else (cfg.H, cfg.I)
-    mag = rng.choice(8, size=(cfg.E, N, K), p=_MX_MAG_P).astype(np.uint8)
-    sign = rng.integers(0, 2, size=(cfg.E, N, K), dtype=np.uint8) << 3
-    codes = mag | sign
+    # a random byte per element: bit 7 is the sign, the low 7 bits pick the
+    # magnitude index through a 128-entry table of the frequencies
+    bounds = np.cumsum(_MX_MAG_P) * 128
+    table = np.searchsorted(bounds, np.arange(128) + 0.5).astype(np.uint8)
+    r = rng.integers(0, 256, size=(cfg.E, N, K), dtype=np.uint8)
+    codes = table[r & 127] | ((r >> 7) << 3)
+    del r
     blocks = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
     scales = (127 + rng.integers(-8, -5, size=(cfg.E, N, K // 32))).astype(np.uint8)
     return blocks, scales

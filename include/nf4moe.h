@@ -370,7 +370,9 @@ int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
  * 2^(s-127) is within fp16's range, 2^-24 .. 2^15; s = 255 decodes as NaN);
  * fp32 accumulation.  K must be a multiple of 128 (ESHAPE).  No adapters.
  * Other arguments, layouts and errors as for grouped_nf4_gemm and
- * moe_expert_forward (the T == 1 case runs the grouped kernels). */
+ * moe_expert_forward; the T == 1 case runs the split-K decode GEMVs, which
+ * apply each 32-block's scale in fp32 (the weights have no fp16 range limit
+ * there; h between the projections is fp16). */
 int grouped_mxfp4_gemm(const void* a, int a_dtype, int64_t a_rows,
                        const int32_t* gather, int gather_div,
                        const uint8_t* blocks, const uint8_t* scales,

@@ -90,3 +90,22 @@ def test_mxfp4_forward_matches_oracle(gpu_lib, name, T, E):
     ref = oracle.moe_forward_mxfp4(x, lg, cfg.k, gb, gs, db, ds, cfg.renormalize)
     m = assert_parity(host(y), ref, what=f"mxfp4 {name}")
     print(name, m)
+
+
+def test_mxfp4_decode_scales_beyond_fp16_range(gpu_lib):
+    """T = 1 runs the decode GEMVs, which apply each block's e8m0 scale in
+    fp32: down weights up to 6 * 2^20 (beyond fp16's 65504) stay exact.  (h
+    between the projections is fp16, so the gate_up scales stay moderate.)"""
+    cfg = synth.config("decode", E=16)
+    rng = np.random.default_rng(44)
+    gb, _ = synth.mxfp4_stack(cfg, "gu")
+    db, _ = synth.mxfp4_stack(cfg, "dn")
+    gs = rng.integers(114, 118, size=(cfg.E, 2 * cfg.I, cfg.H // 32)).astype(np.uint8)  # 2^-13..-10
+    ds = rng.integers(143, 148, size=(cfg.E, cfg.H, cfg.I // 32)).astype(np.uint8)      # 2^16..2^20
+    x = synth.activations(cfg)
+    lg = synth.router_logits(cfg)
+    y = gpu_lib.moe_forward_mxfp4(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gb), gpu(gs),
+                                  gpu(db), gpu(ds), y_dtype=torch.float32)
+    ref = oracle.moe_forward_mxfp4(x, lg, cfg.k, gb, gs, db, ds)
+    assert_parity(host(y), ref, fro_tol=2e-3, maxabs_tol=2e-2, what="mx decode range",
+                  out_dtype="f32")
