@@ -150,7 +150,7 @@ def _counter_means(directory: str, counter: str):
             continue
         name = r["Kernel_Name"]
         v = float(r["Counter_Value"])
-        if "grouped_gemm_kernel<true, false, false, 2, 0>" in name:  # the NF4 gate_up
+        if "grouped_gemm_kernel<true, 0, false, 2, 0>" in name:  # the NF4 gate_up
             gemm.append(v)
         elif "copyBuffer" in name:
             copy.append(v)
@@ -170,7 +170,7 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> int:
     fetch_b = f_gemm * f_scale * 1024.0
     write_b = w_gemm * w_scale * 1024.0
     rec = {
-        "kernel": "grouped_gemm_kernel<true,false,false,2> (gate_up + SwiGLU, olmoe prefill)",
+        "kernel": "grouped_gemm_kernel<true,0,false,2,0> (gate_up + SwiGLU, olmoe prefill)",
         "kernel_source_sha256": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest(),
         "fetch_kib_per_launch_raw": round(f_gemm, 1),
         "write_kib_per_launch_raw": round(w_gemm, 1),
@@ -359,7 +359,7 @@ def bench_backward(name: str, dev, steps: int):
     bwd_ms = time_events(step, max(steps, 5), stream)
 
     # the dgrad kernels alone, on this layer's routing and recomputed G
-    fws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+    fws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, r),
                       dtype=torch.uint8, device=dev)
     binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
                         workspace=fws)
@@ -636,7 +636,8 @@ def main() -> int:
         glo = (t["a_gu"], t["b_gu"], cfg.lora_scale)
         dlo = (t["a_dn"], t["b_dn"], cfg.lora_scale)
     y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k),
+    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
+                                                     cfg.lora_r),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 

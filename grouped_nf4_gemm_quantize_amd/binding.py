@@ -66,7 +66,7 @@ _SIGNATURES = {
                                   _c_vp, _c_int, _c_i64, _c_i64, _c_i64,
                                   ctypes.POINTER(LoraStruct), _c_int, _c_vp, _c_vp,
                                   _c_vp, _c_int, _c_vp]),
-    "moe_expert_forward_workspace": (_c_size, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
+    "moe_expert_forward_workspace": (_c_size, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_expert_forward": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                     ctypes.POINTER(LoraStruct), ctypes.POINTER(LoraStruct),
@@ -268,8 +268,9 @@ def grouped_gemm(a, packed, absmax, offsets, P: int, gather=None, gather_div: in
     return out
 
 
-def forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
-    return int(load().moe_expert_forward_workspace(T, H, I, E, k))
+def forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int, r: int = 0) -> int:
+    """Workspace of moe_forward; ``r`` is the larger adapter rank (0: none)."""
+    return int(load().moe_expert_forward_workspace(T, H, I, E, k, r))
 
 
 def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
@@ -287,7 +288,9 @@ def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
     if y is None:
         y = torch.empty((T, H), dtype=y_dtype or torch.bfloat16, device=x.device)
     lib = load()
-    ws_bytes = lib.moe_expert_forward_workspace(T, H, I, E, k)
+    r = max([l[0].shape[1] for l in (gu_lora, dn_lora) if l is not None and l[0] is not None],
+            default=0)
+    ws_bytes = lib.moe_expert_forward_workspace(T, H, I, E, k, r)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     ls_gu = make_lora(*gu_lora) if gu_lora is not None else None
@@ -418,7 +421,7 @@ def moe_forward_mxfp4(x, logits, k: int, gu_blocks, gu_scales, dn_blocks, dn_sca
     if y is None:
         y = torch.empty((T, H), dtype=y_dtype or torch.bfloat16, device=x.device)
     lib = load()
-    ws_bytes = lib.moe_expert_forward_workspace(T, H, I, E, k)
+    ws_bytes = lib.moe_expert_forward_workspace(T, H, I, E, k, 0)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     _check(lib.moe_expert_forward_mxfp4(

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -181,11 +182,15 @@ RouteLayout route_layout(int64_t T, int E) {
 
 // ---- forward workspace layout (the same regions for every path)
 struct FwdLayout {
-  size_t ids, w, sorted, pos, offsets, route, x16, h, o, hbuf, total;
+  size_t ids, w, sorted, pos, offsets, route, x16, h, o, hbuf;
+  // fp16 copies of bf16 adapters (rank r; last, so the routing views above
+  // do not depend on r): A_gu [E,r,H], B_gu [E,2I,r], A_dn [E,r,I], B_dn [E,H,r]
+  size_t a_gu, b_gu, a_dn, b_dn;
+  size_t total;
   RouteLayout r;
 };
 
-FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k) {
+FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k, int r = 0) {
   FwdLayout L;
   const size_t P = (size_t)T * k;
   size_t o = 0;
@@ -205,6 +210,11 @@ FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k) {
   L.h = take(P * (size_t)I * 2);
   L.o = take(P * (size_t)H * 2);
   L.hbuf = take((size_t)k * I * 4);
+  const size_t er = (size_t)E * r * 2;
+  L.a_gu = take(er * H);
+  L.b_gu = take(er * 2 * I);
+  L.a_dn = take(er * I);
+  L.b_dn = take(er * H);
   L.total = o;
   return L;
 }
@@ -465,9 +475,10 @@ int grouped_nbit_gemm(int quant_type, const void* a, int a_dtype, int64_t a_rows
                    out_dtype, stream);
 }
 
-size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k) {
+size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k, int r) {
   if (T < 1 || H < 1 || I < 1 || E < 1 || E > NF4MOE_MAX_EXPERTS || k < 1) return 0;
-  return fwd_layout(T, H, I, E, k).total;
+  if (r < 0 || r > NF4MOE_MAX_LORA_R) return 0;
+  return fwd_layout(T, H, I, E, k, r).total;
 }
 
 int moe_expert_forward_routing(void* workspace, int64_t T, int H, int I, int E,
@@ -521,10 +532,11 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   if (!aligned(x, 16) || !aligned(gu_packed, 16) || !aligned(dn_packed, 16) ||
       !aligned(gu_absmax, 4) || !aligned(dn_absmax, 4) || !aligned(y, 16))
     return fail(NF4MOE_EINVAL, "misaligned buffer (x, y and packed stacks need 16 bytes)");
-  const FwdLayout L = fwd_layout(T, H, I, E, k);
+  const int r_ws = std::max(gu_lora ? gu_lora->r : 0, dn_lora ? dn_lora->r : 0);
+  const FwdLayout L = fwd_layout(T, H, I, E, k, r_ws);
   if (workspace == nullptr || ws_bytes < L.total)
-    return fail(NF4MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
-                workspace ? ws_bytes : (size_t)0);
+    return fail(NF4MOE_EWORKSPACE, "workspace of %zu bytes needed (adapter rank %d), %zu given",
+                L.total, r_ws, workspace ? ws_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(NF4MOE_EINVAL, "workspace must be 256-byte aligned");
   int cus = 0;
   st = cu_count(&cus);
@@ -583,15 +595,42 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   hipError_t err = launch_route(r, s);
   if (err != hipSuccess) return hip_fail(err, "route launch");
 
+  // bf16 adapters: fp16 copies, made once here, so the GEMMs' k-loops read
+  // fp16 adapter rows (the same rounding as converting them in the loop)
+  HalfCopies hc{};
+  nf4moe_lora gu16{}, dn16{};
+  auto to_f16 = [&](const nf4moe_lora* l, size_t a_off, size_t b_off, int kdim, int n,
+                    nf4moe_lora* out) -> const nf4moe_lora* {
+    if (l == nullptr || l->dtype != NF4MOE_BF16) return l;
+    *out = *l;
+    out->A = ws + a_off;
+    out->B = ws + b_off;
+    out->dtype = NF4MOE_F16;
+    const int64_t na = (int64_t)E * l->r * kdim, nb = (int64_t)E * n * l->r;
+    hc.src[hc.count] = (const uint16_t*)l->A;
+    hc.dst[hc.count] = (_Float16*)(ws + a_off);
+    hc.n8[hc.count++] = na / 8;
+    hc.src[hc.count] = (const uint16_t*)l->B;
+    hc.dst[hc.count] = (_Float16*)(ws + b_off);
+    hc.n8[hc.count++] = nb / 8;
+    return out;
+  };
+  const nf4moe_lora* gu_l = to_f16(gu_lora, L.a_gu, L.b_gu, H, 2 * I, &gu16);
+  const nf4moe_lora* dn_l = to_f16(dn_lora, L.a_dn, L.b_dn, I, H, &dn16);
+  if (hc.count > 0) {
+    err = launch_half_copies(hc, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "adapter conversion launch");
+  }
+
   const void* xa = conv ? (const void*)(ws + L.x16) : x;
   _Float16* h = (_Float16*)(ws + L.h);
   _Float16* o = (_Float16*)(ws + L.o);
   st = gemm_common(xa, NF4MOE_F16, T, r.sorted_pair, k, gu_packed, gu_absmax,
-                   r.expert_offsets, E, P, 2 * (int64_t)I, H, gu_lora,
+                   r.expert_offsets, E, P, 2 * (int64_t)I, H, gu_l,
                    NF4MOE_EPI_SWIGLU, nullptr, nullptr, h, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
   st = gemm_common(h, NF4MOE_F16, P, nullptr, 1, dn_packed, dn_absmax, r.expert_offsets,
-                   E, P, H, I, dn_lora, NF4MOE_EPI_NONE, nullptr,
+                   E, P, H, I, dn_l, NF4MOE_EPI_NONE, nullptr,
                    r.sorted_pair, o, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
   err = launch_combine(o, wts, T, k, H, y, y_dtype, cus, s);

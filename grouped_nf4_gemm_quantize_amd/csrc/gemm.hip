@@ -94,6 +94,10 @@ constexpr int kW4 = 0;   // 4-bit codes through the decode table, fp32 absmax pe
 constexpr int kWMx = 1;  // MXFP4: e2m1 codes through the table, e8m0 scale per 32
 constexpr int kWI8 = 2;  // 8-bit int8 codes, fp32 absmax per 64
 constexpr int kWF8 = 3;  // 8-bit fp8 e4m3 codes, fp32 absmax per 64
+// Adapter storage, a compile-time choice so the k-loop carries no select
+constexpr int kLoraNone = 0;
+constexpr int kLoraF16 = 1;
+constexpr int kLoraBF16 = 2;
 
 }  // namespace
 
@@ -144,19 +148,19 @@ struct Src {
 
 // Copies per wave: activations of one step (+ LoRA A), the packed codes of
 // a step pair, an absmax group.
-template <bool kLora>
-constexpr int kDmaA() { return kLora ? 3 : 2; }
+template <int kLora>
+constexpr int kDmaA() { return kLora != kLoraNone ? 3 : 2; }
 constexpr int kDmaB = 4;
 constexpr int kDmaAbs = 1;
 
 // Activations (and LoRA A rows) of step `kb` (clamped) into the A stage at
 // LDS address `st`.
-template <bool kLora>
+template <int kLora>
 __device__ __forceinline__ void issue_a(const Src& s, int kb, uint32_t st, int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     dma16(s.a_rsrc, s.a_off[i], (uint32_t)kb * (BK * 2), st + (wave * 2 + i) * 1024);
-  if constexpr (kLora)
+  if constexpr (kLora != kLoraNone)
     dma4(s.l_rsrc, s.l_off, (uint32_t)kb * (BK * 2), st + OFF_L + wave * 256);
 }
 
@@ -296,11 +300,11 @@ __device__ __forceinline__ void decode_b8(const StepRegs& r, f16x8 (&bf)[NT]) {
 // ahead of use), while the A fragments and table words of the next substep
 // are read -- for S = 3 those of substep 0 of the next step, from the next
 // stage `nst` (valid once the barrier before substep 3 has passed).
-template <int S, int MTV, bool kLora, bool kABf16, int kW>
+template <int S, int MTV, int kLora, bool kABf16, int kW>
 __device__ __forceinline__ void substep(const char* st, const char* nst, const char* nbst,
                                         int next_step, const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
-                                        uint32_t (&d)[NT][4], int lora_live, int lora_bf16,
+                                        uint32_t (&d)[NT][4],
                                         f32x16 (&acc)[MT][NT], f32x4& acc_u) {
   f16x8 af_n[MT];
   uint32_t dn[NT][4];
@@ -313,11 +317,10 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
     if constexpr (kW < kWI8) lut_lookups(nxt, 0, rd.lane_off, dn);
   }
   // LoRA: u[this wave's 16 rows][16 ranks] += X A_e^T, k half S - 1
-  if constexpr (kLora && (S == 1 || S == 2)) {
+  if constexpr (kLora != kLoraNone && (S == 1 || S == 2)) {
     constexpr int s2 = S - 1;
     u32x4 l = *reinterpret_cast<const u32x4*>(st + OFF_L + rd.ul + s2 * 64);
-    if (lora_bf16) l = bf16x8_to_f16x8(l);
-    if (!lora_live) l = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kLora == kLoraBF16) l = bf16x8_to_f16x8(l);
     u32x4 v = *reinterpret_cast<const u32x4*>(st + rd.ua[s2]);
     if constexpr (kABf16) v = bf16x8_to_f16x8(v);
     acc_u = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_u, 0, 0, 0);
@@ -355,9 +358,9 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
 // complete in order.  Pairs and activations are issued at least one full
 // step before use, codes and absmax two.  Past the last step the copies of
 // the last step / pair / group are repeated, so the counts hold throughout.
-template <int MTV, bool kLora, bool kABf16, int kW>
+template <int MTV, int kLora, bool kABf16, int kW>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
-                                      int lora_r, int lora_bf16, f32x16 (&acc)[MT][NT],
+                                      f32x16 (&acc)[MT][NT],
                                       f32x4& acc_u) {
   constexpr int NA = kDmaA<kLora>();
   const uint32_t ring = lds_addr(g_ring);
@@ -371,7 +374,6 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
   issue_a<kLora>(src, min(1, last), ring + ASTAGE, wave);
   // 8-bit codes: one step per stage (64 bytes of a row), not a step pair
   issue_b(src, kW >= kWI8 ? min(1, last) : min(1, last_pair), ring + OFF_BR + BPAIR, wave);
-  const int lora_live = (lane & 15) < lora_r;
 
   // absmax group 0, pair 0 and step 0's activations complete
   wait_vm_barrier<NA + kDmaB>();
@@ -387,9 +389,9 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
     const char* np = g_ring + (a ^ 1) * ASTAGE;        // step kb + 1's
     const char* nbp = g_ring + OFF_BR +
                       ((kW >= kWI8 ? (kb + 1) : ((kb + 1) >> 1)) & 1) * BPAIR;  // kb + 1's codes
-    substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
-    substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
     if constexpr (kW >= kWI8) {
       // 8-bit codes: every batch carries the next step's codes and
       // activations, both needed now
@@ -427,14 +429,14 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
         issue_abs(src, min(grp, last >> 2), grp & 1, wave);
       }
     }
-    substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, lora_live, lora_bf16, acc, acc_u);
+    substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
     cur = nxt;
   }
 }
 
 }  // namespace
 
-template <bool kSwiglu, bool kLora, bool kABf16, int kOut, int kW>
+template <bool kSwiglu, int kLora, bool kABf16, int kOut, int kW>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
   constexpr bool kMx = kW == kWMx;
   const int tid = threadIdx.x;
@@ -458,6 +460,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   const int K = g.K;
   const int I = N >> 1;  // SwiGLU: output columns
   const int nk = K / BK;
+  // adapter rows of B_e load as one 16-byte vector per 8 ranks
+  const bool lora_vec = (g.lora_r & 7) == 0 && (reinterpret_cast<uintptr_t>(g.lora_b) & 15) == 0;
 
   Rd rd;
 #pragma unroll
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     // 64), 16 bytes (kAbsGroup steps) per row
     src.s_off = (uint32_t)weight_row(wave * 64 + lane, n_idx) *
                 (kMx ? (uint32_t)(K / 32) : (uint32_t)nk * 4u);
-    if constexpr (kLora) {
+    if constexpr (kLora != kLoraNone) {
       const uint32_t l_bytes = (uint32_t)g.lora_r * (uint32_t)K * 2u;
       src.l_rsrc = make_rsrc(reinterpret_cast<const char*>(g.lora_a) + (int64_t)e * l_bytes, l_bytes);
       // LoRA A: 16 rows x 128 B per step; dword d of the block is row d / 32
@@ -605,39 +609,55 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     // every wave is done with the previous tile's stages (and LoRA exchange)
     lds_barrier();
     switch (mtv) {
-      case 1: kloop<1, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      case 2: kloop<2, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      case 3: kloop<3, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
-      default: kloop<4, kLora, kABf16, kW>(src, nk, rd, wave, lane, g.lora_r, g.lora_bf16, acc, acc_u); break;
+      case 1: kloop<1, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
+      case 2: kloop<2, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
+      case 3: kloop<3, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
+      default: kloop<4, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
+    }
+    // LoRA B_e: ranks 8 g2 .. 8 g2 + 7 of this lane's weight row in each
+    // n-tile (zero past r), loaded before the final wait so their latency
+    // overlaps it; one 16-byte load when the rows are 16-byte aligned
+    f16x8 bl2[NT];
+    if constexpr (kLora != kLoraNone) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int l = wave * BNW + nt * 32 + n32;
+        const uint16_t* lb = reinterpret_cast<const uint16_t*>(g.lora_b) +
+                             ((int64_t)e * N + weight_row(l, n_idx)) * g.lora_r;
+        if (lora_vec) {
+          u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+          if (g2 * 8 < g.lora_r) raw = *reinterpret_cast<const u32x4*>(lb + g2 * 8);
+          if constexpr (kLora == kLoraBF16) raw = bf16x8_to_f16x8(raw);
+          bl2[nt] = as_f16x8(raw);
+        } else {
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            const int rho = g2 * 8 + tt;
+            _Float16 hv = (_Float16)0.f;
+            if (rho < g.lora_r) {
+              const uint16_t raw = lb[rho];
+              if constexpr (kLora == kLoraBF16) hv = (_Float16)bf16_bits_to_f32(raw);
+              else hv = __builtin_bit_cast(_Float16, raw);
+            }
+            bl2[nt][tt] = hv;
+          }
+        }
+      }
     }
     // every copy has landed and every wave is done with the ring: the
     // epilogue stages its output there
     wait_vm_barrier<0>();
 
     // ---- LoRA: G += (scale * u) B_e^T, u exchanged between the waves in fp16
-    if constexpr (kLora) {
-      // 16x16 accumulator layout: lane holds rank c16 of rows 4*g4 + i
+    if constexpr (kLora != kLoraNone) {
+      // 16x16 accumulator layout: lane holds rank c16 of rows 4*g4 + i.
+      // Ranks c16 >= r multiplied a stand-in row of A_e (the copies clamp
+      // to row 0): they are stored as zero.
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        u_buf()[(wave * 16 + g4 * 4 + i) * kMaxLoraR + c16] = (_Float16)(acc_u[i] * g.lora_scale);
+        u_buf()[(wave * 16 + g4 * 4 + i) * kMaxLoraR + c16] =
+            c16 < g.lora_r ? (_Float16)(acc_u[i] * g.lora_scale) : (_Float16)0.f;
       lds_barrier();
-      f16x8 bl2[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int l = wave * BNW + nt * 32 + n32;
-        const uint16_t* lb = reinterpret_cast<const uint16_t*>(g.lora_b) +
-                             ((int64_t)e * N + weight_row(l, n_idx)) * g.lora_r;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const int rho = g2 * 8 + tt;
-          _Float16 hv = (_Float16)0.f;
-          if (rho < g.lora_r) {
-            const uint16_t raw = lb[rho];
-            hv = g.lora_bf16 ? (_Float16)bf16_bits_to_f32(raw) : __builtin_bit_cast(_Float16, raw);
-          }
-          bl2[nt][tt] = hv;
-        }
-      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const f16x8 au = *reinterpret_cast<const f16x8*>(&u_buf()[(mt * 32 + n32) * kMaxLoraR + g2 * 8]);
@@ -708,7 +728,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kSwiglu, bool kLora, bool kABf16, int kW>
+template <bool kSwiglu, int kLora, bool kABf16, int kW>
 static void launch_out(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
   switch (g.out_dtype) {
     case kF32:
@@ -726,7 +746,7 @@ static void launch_out(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s)
   }
 }
 
-template <bool kSwiglu, bool kLora, int kW = kW4>
+template <bool kSwiglu, int kLora, int kW = kW4>
 static void launch_a(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
   if (g.a_bf16) launch_out<kSwiglu, kLora, true, kW>(g, grid, n_tiles, s);
   else launch_out<kSwiglu, kLora, false, kW>(g, grid, n_tiles, s);
@@ -743,26 +763,29 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t strea
   const bool lora = g.lora_a != nullptr;
   // no adapters on MXFP4 or 8-bit stacks (checked by the caller)
   if (g.qtype == kQtMXFP4) {
-    if (g.swiglu) launch_a<true, false, kWMx>(g, dg, n_tiles, stream);
-    else launch_a<false, false, kWMx>(g, dg, n_tiles, stream);
+    if (g.swiglu) launch_a<true, kLoraNone, kWMx>(g, dg, n_tiles, stream);
+    else launch_a<false, kLoraNone, kWMx>(g, dg, n_tiles, stream);
     return hipGetLastError();
   }
   if (g.qtype == kQtINT8 || g.qtype == kQtFP8) {
     if (g.qtype == kQtINT8) {
-      if (g.swiglu) launch_a<true, false, kWI8>(g, dg, n_tiles, stream);
-      else launch_a<false, false, kWI8>(g, dg, n_tiles, stream);
+      if (g.swiglu) launch_a<true, kLoraNone, kWI8>(g, dg, n_tiles, stream);
+      else launch_a<false, kLoraNone, kWI8>(g, dg, n_tiles, stream);
     } else {
-      if (g.swiglu) launch_a<true, false, kWF8>(g, dg, n_tiles, stream);
-      else launch_a<false, false, kWF8>(g, dg, n_tiles, stream);
+      if (g.swiglu) launch_a<true, kLoraNone, kWF8>(g, dg, n_tiles, stream);
+      else launch_a<false, kLoraNone, kWF8>(g, dg, n_tiles, stream);
     }
     return hipGetLastError();
   }
+  const int kind = !lora ? kLoraNone : g.lora_bf16 ? kLoraBF16 : kLoraF16;
   if (g.swiglu) {
-    if (lora) launch_a<true, true>(g, dg, n_tiles, stream);
-    else launch_a<true, false>(g, dg, n_tiles, stream);
+    if (kind == kLoraBF16) launch_a<true, kLoraBF16>(g, dg, n_tiles, stream);
+    else if (kind == kLoraF16) launch_a<true, kLoraF16>(g, dg, n_tiles, stream);
+    else launch_a<true, kLoraNone>(g, dg, n_tiles, stream);
   } else {
-    if (lora) launch_a<false, true>(g, dg, n_tiles, stream);
-    else launch_a<false, false>(g, dg, n_tiles, stream);
+    if (kind == kLoraBF16) launch_a<false, kLoraBF16>(g, dg, n_tiles, stream);
+    else if (kind == kLoraF16) launch_a<false, kLoraF16>(g, dg, n_tiles, stream);
+    else launch_a<false, kLoraNone>(g, dg, n_tiles, stream);
   }
   return hipGetLastError();
 }

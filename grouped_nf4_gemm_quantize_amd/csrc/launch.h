@@ -169,6 +169,15 @@ hipError_t launch_swiglu_rows(const _Float16* g, int64_t P, int I, _Float16* h, 
                               hipStream_t s);
 hipError_t launch_bf16_to_f16(const void* src, int64_t n, _Float16* dst, int num_cus,
                               hipStream_t s);
+// Up to four bf16 arrays (each a multiple of 8 elements, dst 16-byte
+// aligned) converted to fp16 in one launch.
+struct HalfCopies {
+  const uint16_t* src[4];
+  _Float16* dst[4];
+  int64_t n8[4];  // elements / 8
+  int count;
+};
+hipError_t launch_half_copies(const HalfCopies& c, int num_cus, hipStream_t s);
 hipError_t launch_lora_to_f16(const void* src, int src_bf16, int transpose, int E, int C,
                               int r, _Float16* dst, int num_cus, hipStream_t s);
 hipError_t launch_lora_pass(const LoraPassArgs& a, int num_cus, hipStream_t s);

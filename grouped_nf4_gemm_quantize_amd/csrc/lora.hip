@@ -79,6 +79,33 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __rest
   }
 }
 
+// bf16 adapter factors -> fp16 copies in their own layout (round to nearest
+// even, as the GEMM's in-loop conversion of bf16 adapters): the layer
+// forward converts once per call, so its k-loops read fp16 adapter rows.
+// Up to four arrays in one launch; 8 elements per thread and step, read as
+// one 16-byte vector where the source is 16-byte aligned.
+__global__ __launch_bounds__(256) void half_copies_kernel(HalfCopies c) {
+  int64_t total = 0;
+  for (int i = 0; i < c.count; ++i) total += c.n8[i];
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    int seg = 0;
+    int64_t local = q;
+    while (seg + 1 < c.count && local >= c.n8[seg]) local -= c.n8[seg++];
+    const uint16_t* src = c.src[seg] + local * 8;
+    u32x4 v;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      v = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = (uint32_t)src[2 * t] | ((uint32_t)src[2 * t + 1] << 16);
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    *reinterpret_cast<u32x4*>(c.dst[seg] + local * 8) = bf16x8_to_f16x8(v);
+  }
+}
+
 // An adapter matrix as fp16 [E, r, C]: src is [E, r, C] (transpose = 0,
 // the A factor) or [E, C, r] (transpose = 1, the B factor), bf16 or fp16.
 __global__ __launch_bounds__(256) void lora_to_f16_kernel(const uint16_t* __restrict__ src,
@@ -282,6 +309,16 @@ hipError_t launch_bf16_to_f16(const void* src, int64_t n, _Float16* dst, int num
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(src), n8, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_half_copies(const HalfCopies& c, int num_cus, hipStream_t s) {
+  int64_t total = 0;
+  for (int i = 0; i < c.count; ++i) total += c.n8[i];
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  if (grid > (int64_t)num_cus * 8) grid = (int64_t)num_cus * 8;
+  hipLaunchKernelGGL(half_copies_kernel, dim3((unsigned)grid), dim3(256), 0, s, c);
   return hipGetLastError();
 }
 

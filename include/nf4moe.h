@@ -208,11 +208,17 @@ int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
  *   router_logits   fp32 [T, E];
  *   H, I            multiples of 64; E <= NF4MOE_MAX_EXPERTS; k <= min(E, 32);
  *   gu_*            gate_up stack [E, 2I, H]; dn_* down stack [E, H, I];
- *   gu_lora/dn_lora [host] nullable adapters (r must match the size query);
+ *   gu_lora/dn_lora [host] nullable adapters; BF16 adapters are copied to
+ *                   fp16 in the workspace once per call (the same rounding
+ *                   the GEMM applies to bf16 adapters itself);
  *   y               [T, H] in y_dtype (BF16, F16 or F32);
- *   workspace       moe_expert_forward_workspace(T, H, I, E, k) bytes.
+ *   workspace       moe_expert_forward_workspace(T, H, I, E, k, r) bytes,
+ *                   256-byte aligned, r = the larger adapter rank (0 without
+ *                   adapters); too small -> EWORKSPACE, naming the size.
+ * moe_expert_forward_workspace returns 0 for invalid sizes (r outside
+ * [0, NF4MOE_MAX_LORA_R] included).
  */
-size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k);
+size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k, int r);
 int moe_expert_forward(const void* x, int x_dtype, const float* router_logits,
                        int64_t T, int H, int I, int E, int k, int renormalize,
                        const uint8_t* gu_packed, const float* gu_absmax,

@@ -169,8 +169,14 @@ def test_gemm_validation(lib):
 def test_forward_validation(lib):
     f = lib.moe_expert_forward
     T, H, I, E, k = 64, 256, 128, 8, 2
-    wsb = lib.moe_expert_forward_workspace(T, H, I, E, k)
+    wsb = lib.moe_expert_forward_workspace(T, H, I, E, k, 0)
     assert wsb > T * k * (H + I) * 2
+    # adapters of rank r take their fp16 copies on top: E * r * (2H + 3I) * 2 bytes
+    r = 8
+    extra = lib.moe_expert_forward_workspace(T, H, I, E, k, r) - wsb
+    assert E * r * (2 * H + 3 * I) * 2 <= extra < E * r * (2 * H + 3 * I) * 2 + 4 * 256
+    assert lib.moe_expert_forward_workspace(T, H, I, E, k, -1) == 0
+    assert lib.moe_expert_forward_workspace(T, H, I, E, k, 17) == 0
 
     def call(**kw):
         a = dict(x=FAKE, xdt=1, lg=FAKE, T=T, H=H, I=I, E=E, k=k, renorm=1, gp=FAKE,
@@ -191,6 +197,10 @@ def test_forward_validation(lib):
     assert call(ws=FAKE + 64) == -1  # workspace must be 256-byte aligned
     bad = binding.LoraStruct(None, FAKE, 8, 2.0, 1)
     assert call(gl=ctypes.byref(bad)) == -1
+    # an adapter needs the workspace sized for its rank
+    good = binding.LoraStruct(FAKE, FAKE, 8, 2.0, 1)
+    assert call(dl=ctypes.byref(good)) == -6
+    assert "adapter rank 8" in _last(lib)
 
 
 def test_status_strings(lib):

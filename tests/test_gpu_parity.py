@@ -299,6 +299,55 @@ def test_lora_with_zero_b_is_bitwise_no_lora(gpu_lib):
         assert torch.equal(plain, zero)
 
 
+def _adapter_b(B, offset):
+    """B as a GPU bf16 tensor whose storage starts ``offset`` elements into a
+    larger buffer (offset 1: only 2-byte aligned)."""
+    t = B.reshape(-1)
+    buf = torch.empty(t.size + offset, dtype=torch.bfloat16, device=DEV)
+    view = buf[offset:].view(B.shape)
+    view.copy_(gpu(B, torch.bfloat16))
+    return view
+
+
+@pytest.mark.parametrize("swiglu,r,offset", [(False, 8, 0), (True, 8, 0), (True, 5, 1)])
+def test_bf16_adapters_match_their_f16_copies_bitwise(gpu_lib, swiglu, r, offset):
+    """bf16 adapters are rounded to fp16 (nearest even) inside the kernel;
+    the same adapters rounded by torch give the same bits.  r = 5 with a
+    B only 2-byte aligned takes the element-wise B loads."""
+    rng = np.random.default_rng(30 + r + swiglu)
+    E, N, K = 3, 640, 256
+    counts = [150, 0, 97]
+    P = sum(counts)
+    packed, absmax, offsets, a = _random_gemm_case(rng, E, N, K, counts, P)
+    A = gpu(rng.standard_normal((E, r, K), dtype=np.float32) * 0.05, torch.bfloat16)
+    B = _adapter_b(rng.standard_normal((E, N, r), dtype=np.float32) * 0.05, offset)
+    outs = []
+    for lo in ((A, B, 2.0), (A.half(), B.half(), 2.0)):
+        outs.append(gpu_lib.grouped_gemm(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                                         lora=lo, swiglu=swiglu, out_dtype=torch.float32))
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("r,offset", [(8, 0), (5, 1)])
+def test_forward_adapter_copies_match_f16_adapters_bitwise(gpu_lib, r, offset):
+    """The layer forward copies bf16 adapters to fp16 in its workspace (one
+    launch for the four factors); fp16 adapters are used as given.  Both give
+    the same bits."""
+    cfg = synth.config("qlora", T=256, E=16, lora_r=r)
+    gp, ga, dp, da = _stacks(cfg)
+    x, lg = synth.activations(cfg), synth.router_logits(cfg)
+    lw = synth.lora_weights(cfg)
+    s = cfg.lora_scale
+    glo = (gpu(lw["a_gu"], torch.bfloat16), _adapter_b(lw["b_gu"], offset), s)
+    dlo = (gpu(lw["a_dn"], torch.bfloat16), _adapter_b(lw["b_dn"], offset), s)
+    half = lambda lo: (lo[0].half(), lo[1].half(), lo[2])
+    ys = [gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gp), gpu(ga),
+                              gpu(dp), gpu(da), g_, d_, y_dtype=torch.float32)
+          for g_, d_ in ((glo, dlo), (half(glo), half(dlo)))]
+    assert torch.equal(ys[0], ys[1])
+    assert torch.count_nonzero(ys[0]) > 0
+
+
 def test_forward_token_permutation_equivariance(gpu_lib):
     """Permuting the tokens permutes the output rows, bit for bit."""
     cfg = synth.config("tiny", T=96)
