@@ -356,20 +356,27 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
 // an absmax group; anything older (codes and absmax needed by step kb + 1,
 // issued two or more steps earlier) has landed with them, since copies
 // complete in order.  Pairs and activations are issued at least one full
-// step before use, codes and absmax two.  Past the last step the copies of
-// the last step / pair / group are repeated, so the counts hold throughout.
+// step before use, codes and absmax two.  Nothing past the last step, pair
+// or group is fetched (only the prologue repeats the last ones, when K has
+// one or two steps); batches from kb = last - 2 on may therefore carry
+// fewer copies than the counts assume, so the last three steps drain all
+// copies instead -- theirs were issued a step or more earlier.  The tile
+// then ends with no copy in flight.
 template <int MTV, int kLora, bool kABf16, int kW>
 __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int wave, int lane,
-                                      f32x16 (&acc)[MT][NT],
+                                      bool early, f32x16 (&acc)[MT][NT],
                                       f32x4& acc_u) {
   constexpr int NA = kDmaA<kLora>();
   const uint32_t ring = lds_addr(g_ring);
   const int last = nk - 1;
   const int last_pair = last >> 1;
-  // prologue: absmax group 0, pair 0, activations of steps 0 and 1, pair 1 --
-  // as if batch -1 (odd, activations then a pair) were the last one issued
-  issue_abs(src, 0, 0, wave);
-  issue_b(src, 0, ring + OFF_BR, wave);
+  // prologue: absmax group 0, pair 0 (unless issued early, under the
+  // previous tile's epilogue), activations of steps 0 and 1, pair 1 -- as if
+  // batch -1 (odd, activations then a pair) were the last one issued
+  if (!early) {
+    issue_abs(src, 0, 0, wave);
+    issue_b(src, 0, ring + OFF_BR, wave);
+  }
   issue_a<kLora>(src, 0, ring, wave);
   issue_a<kLora>(src, min(1, last), ring + ASTAGE, wave);
   // 8-bit codes: one step per stage (64 bytes of a row), not a step pair
@@ -392,7 +399,11 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
     substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
     substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
     substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
-    if constexpr (kW >= kWI8) {
+    if (kb >= last - 2) {
+      // the batches of the last steps skip every copy past the end, so the
+      // counts below no longer describe them: drain
+      wait_vm_barrier<0>();
+    } else if constexpr (kW >= kWI8) {
       // 8-bit codes: every batch carries the next step's codes and
       // activations, both needed now
       wait_vm_barrier<0>();
@@ -409,24 +420,26 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
         default: wait_vm_barrier<0>(); break;                // batch kb - 1 even
       }
     }
-    issue_a<kLora>(src, min(kb + 2, last), ring + a * ASTAGE, wave);
+    // nothing past the last step, pair or group is fetched: the tile's
+    // last wait then has no copy left in flight
+    if (kb + 2 <= last) issue_a<kLora>(src, kb + 2, ring + a * ASTAGE, wave);
     if constexpr (kW >= kWI8) {
-      issue_b(src, min(kb + 2, last), ring + OFF_BR + a * BPAIR, wave);
+      if (kb + 2 <= last) issue_b(src, kb + 2, ring + OFF_BR + a * BPAIR, wave);
       if ((kb & 3) == 1) {
         const int grp = (kb + 3) >> 2;
-        issue_abs(src, min(grp, last >> 2), grp & 1, wave);
+        if (grp <= (last >> 2)) issue_abs(src, grp, grp & 1, wave);
       }
     } else if (kb & 1) {
       const int pn = (kb + 3) >> 1;
-      issue_b(src, min(pn, last_pair), ring + OFF_BR + (pn & 1) * BPAIR, wave);
+      if (pn <= last_pair) issue_b(src, pn, ring + OFF_BR + (pn & 1) * BPAIR, wave);
       if constexpr (kW == kWMx) {
         if ((kb & 7) == 5) {
           const int grp = (kb + 3) >> 3;
-          issue_abs(src, min(grp, last >> 3), grp & 1, wave);
+          if (grp <= (last >> 3)) issue_abs(src, grp, grp & 1, wave);
         }
       } else if ((kb & 3) == 1) {
         const int grp = (kb + 3) >> 2;
-        issue_abs(src, min(grp, last >> 2), grp & 1, wave);
+        if (grp <= (last >> 2)) issue_abs(src, grp, grp & 1, wave);
       }
     }
     substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
@@ -514,35 +527,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   // halves (the same weights, half the rows each), one per workgroup.
   const int q = total / G, rem = total - q * G;
   const bool split_tail = rem > 0 && 2 * rem <= G;
-  for (int r = 0;; ++r) {
+  // Tile r of this workgroup: expert, N-tile, first row, valid rows.
+  struct Tile {
+    int e, n_idx, row0, rows_valid, mtv;
+  };
+  auto find_tile = [&](int r, Tile& t) -> bool {
     const int u = xcd * (G >> 3) + pos;  // position within the round
     int tix, half = -1;
     if (split_tail && r == q) {
-      if (u >= 2 * rem) break;
+      if (u >= 2 * rem) return false;
       tix = q * G + (u >> 1);
       half = u & 1;
     } else {
       tix = r * G + u;
-      if (tix >= total) break;
+      if (tix >= total) return false;
     }
     const int mt_global = tix / n_tiles;
-    const int n_idx = tix - mt_global * n_tiles;
+    t.n_idx = tix - mt_global * n_tiles;
     int lo = 0, hi = g.E;  // g_tiles[lo] <= mt_global < g_tiles[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (g_tiles[mid] <= mt_global) lo = mid; else hi = mid;
     }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int m_local = mt_global - __builtin_amdgcn_readfirstlane(g_tiles[e]);
-    int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + m_local * BM;
-    int rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
+    t.e = __builtin_amdgcn_readfirstlane(lo);
+    const int m_local = mt_global - __builtin_amdgcn_readfirstlane(g_tiles[t.e]);
+    t.row0 = __builtin_amdgcn_readfirstlane(g.offsets[t.e]) + m_local * BM;
+    t.rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[t.e + 1]) - t.row0);
     if (half >= 0) {
-      row0 += half * (BM / 2);
-      rows_valid = min(BM / 2, rows_valid - half * (BM / 2));
-      if (rows_valid <= 0) break;  // the tile's rows fit its first half
+      t.row0 += half * (BM / 2);
+      t.rows_valid = min(BM / 2, t.rows_valid - half * (BM / 2));
+      if (t.rows_valid <= 0) return false;  // the tile's rows fit its first half
     }
-    const int mtv = (rows_valid + 31) >> 5;
+    t.mtv = (t.rows_valid + 31) >> 5;
+    return true;
+  };
 
+  // The copy sources of a tile.
+  auto make_src = [&](const Tile& t) -> Src {
+    const int e = t.e, n_idx = t.n_idx, row0 = t.row0, rows_valid = t.rows_valid;
     Src src;
     src.a_rsrc = a_rsrc;
     const uint32_t brow = kW >= kWI8 ? (uint32_t)K : (uint32_t)(K / 2);  // code bytes per row
@@ -589,6 +611,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       src.l_off = 0;
     }
 
+    return src;
+  };
+
+  // The epilogue stages its output in the A stages only (for 16-bit
+  // outputs, and 32-bit SwiGLU ones): the next tile's absmax group 0 and
+  // code pair 0 are then copied in under the epilogue.
+  constexpr int kStageBytes =
+      NWAVES * 32 * ((kSwiglu ? BNW / 2 : BNW) * (kOut == kF32 ? 4 : 2) + 16);
+  constexpr bool kEarly = kStageBytes <= OFF_BR && kLora == kLoraNone;
+
+  // (the found flags are made wave-uniform explicitly: the copy sources
+  // below must stay in scalar registers)
+  Tile tile;
+  bool have = __builtin_amdgcn_readfirstlane((int)find_tile(0, tile)) != 0;
+  bool early = false;  // this tile's absmax group 0 and pair 0 are issued
+  for (int r = 0; have; ++r) {
+    const int e = tile.e, n_idx = tile.n_idx, row0 = tile.row0, rows_valid = tile.rows_valid;
+    const int mtv = tile.mtv;
+    const Src src = make_src(tile);
     // output row and row scale of every tile row, for the epilogue
     const int par = r & 1;
     if (tid < BM) {
@@ -609,10 +650,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     // every wave is done with the previous tile's stages (and LoRA exchange)
     lds_barrier();
     switch (mtv) {
-      case 1: kloop<1, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
-      case 2: kloop<2, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
-      case 3: kloop<3, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
-      default: kloop<4, kLora, kABf16, kW>(src, nk, rd, wave, lane, acc, acc_u); break;
+      case 1: kloop<1, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
+      case 2: kloop<2, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
+      case 3: kloop<3, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
+      default: kloop<4, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
     }
     // LoRA B_e: ranks 8 g2 .. 8 g2 + 7 of this lane's weight row in each
     // n-tile (zero past r), loaded before the final wait so their latency
@@ -647,6 +688,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
     // every copy has landed and every wave is done with the ring: the
     // epilogue stages its output there
     wait_vm_barrier<0>();
+
+    // the next tile; its first absmax group and code pair go out now
+    Tile next;
+    const bool have_next = __builtin_amdgcn_readfirstlane((int)find_tile(r + 1, next)) != 0;
+    early = kEarly && have_next;
+    if (early) {
+      const Src ns = make_src(next);
+      issue_abs(ns, 0, 0, wave);
+      issue_b(ns, 0, lds_addr(g_ring) + OFF_BR, wave);
+    }
 
     // ---- LoRA: G += (scale * u) B_e^T, u exchanged between the waves in fp16
     if constexpr (kLora != kLoraNone) {
@@ -683,6 +734,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       constexpr int CPR = COLS * ESZ / 16;          // 16-byte chunks per row
       constexpr int EPC = 16 / ESZ;                 // elements per chunk
       static_assert(NWAVES * 32 * PITCH <= RING, "staging fits the ring");
+      static_assert(NWAVES * 32 * PITCH == kStageBytes, "staging size as assumed");
       char* ws = g_ring + wave * 32 * PITCH;
       const int ncols = kSwiglu ? I : N;
       const int cbase = kSwiglu ? n_idx * 256 + wave * (BNW / 2) : n_idx * BN + wave * BNW;
@@ -723,8 +775,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
         }
       }
     }
+    tile = next;
+    have = have_next;
   }
-  // the repeated copies past a tile's last step may still be landing in LDS
+  // no memory operation of the wave is left in flight when it ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
