@@ -238,8 +238,10 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int par
 // barrier of step kb (every wave is done reading stage kb % 3, whose last
 // reads are substep 2's) the wave issues batch kb + 3 there.  Before that
 // barrier step kb + 1 must have landed: batch kb + 2 may still be pending,
-// so the wait leaves kDma copies outstanding.  Past the last step the last
-// batch is repeated, so the count holds throughout.
+// so the wait leaves kDma copies outstanding.  Nothing past the last step is
+// fetched (only the prologue repeats the last batch, when there are fewer
+// than three steps); in the last two steps batch kb + 2 does not exist, so
+// they drain all copies instead, and the tile ends with none in flight.
 template <int MTV, bool kABf16>
 __device__ __forceinline__ void kloop(const DSrc& src, int nk, const DRd& rd, int wave,
                                       int lane, f32x16 (&acc)[MT][NT]) {
@@ -270,8 +272,9 @@ __device__ __forceinline__ void kloop(const DSrc& src, int nk, const DRd& rd, in
     substep<0, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
     substep<1, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
     substep<2, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
-    wait_vm_barrier<kDma>();
-    issue_step(src, min(kb + 3, last), ring + sidx * STAGE, wave);
+    if (kb >= last - 1) wait_vm_barrier<0>();
+    else wait_vm_barrier<kDma>();
+    if (kb + 3 <= last) issue_step(src, kb + 3, ring + sidx * STAGE, wave);
     substep<3, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
     sidx = nidx;
   }
