@@ -20,7 +20,8 @@ I=1024, top-8, T=4096 tokens); the value is its algorithmic TFLOP/s
                 replayed from a HIP graph;
   mxfp4         the same prefill layer on released-MXFP4-format stacks
                 (e2m1 + e8m0 bytes multiplied in place);
-  storage_modes the same layer with the stacks stored as fp4, int8, fp8;
+  storage_modes the same layer with the stacks stored as fp4, int8, fp8 and
+                as plain bf16 / fp16 weights (the passthrough modes);
   backward      the QLoRA training backward of a layer (olmoe without
                 adapters, qlora with r=8 adapters): time per backward and
                 its two dgrad kernels timed alone;
@@ -483,18 +484,24 @@ def bench_storage_modes(dev, steps: int):
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     out = {}
-    for qt in ("fp4", "int8", "fp8"):
+    for qt in ("fp4", "int8", "fp8", "bf16", "fp16"):
         st = {}
         for which, (n, kk) in (("gu", (2 * cfg.I, cfg.H)), ("dn", (cfg.H, cfg.I))):
-            per = 1 if qt in binding.EIGHT_BIT else 2
-            p = torch.empty((cfg.E, n, kk // per), dtype=torch.uint8, device=dev)
-            a = torch.empty((cfg.E, n, kk // 64), dtype=torch.float32, device=dev)
+            if qt in binding.PASSTHROUGH:  # the weights themselves, no absmax
+                p = torch.empty((cfg.E, n, kk), device=dev,
+                                dtype=torch.bfloat16 if qt == "bf16" else torch.float16)
+                a = None
+            else:
+                per = 1 if qt in binding.EIGHT_BIT else 2
+                p = torch.empty((cfg.E, n, kk // per), dtype=torch.uint8, device=dev)
+                a = torch.empty((cfg.E, n, kk // 64), dtype=torch.float32, device=dev)
             for e0 in range(0, cfg.E, 16):
                 ex = range(e0, min(e0 + 16, cfg.E))
                 w = torch.from_numpy(synth.stack_weights(cfg, which, 0, ex)).to(dev)
                 pp, aa = binding.quantize(w, quant_type=qt)
                 p[e0:e0 + len(ex)] = pp
-                a[e0:e0 + len(ex)] = aa
+                if a is not None:
+                    a[e0:e0 + len(ex)] = aa
                 del w
             st[which] = (p, a)
         gp, ga = st["gu"]
@@ -509,7 +516,8 @@ def bench_storage_modes(dev, steps: int):
         ms = time_events(step, max(steps, 5), stream)
         out[qt] = {"us_per_forward": round(ms * 1e3, 2),
                    "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
-                   "stack_bytes": int(sum(t.numel() * t.element_size() for t in (gp, ga, dp, da)))}
+                   "stack_bytes": int(sum(t.numel() * t.element_size()
+                                          for t in (gp, ga, dp, da) if t is not None))}
         del st, gp, ga, dp, da
         torch.cuda.empty_cache()
     return out

@@ -99,8 +99,10 @@ _SIGNATURES = {
 }
 
 # storage modes of the nbit entry points (NF4MOE_QT_* in include/nf4moe.h)
-QUANT_TYPES = {"nf4": 0, "fp4": 1, "int8": 3, "fp8": 4}
+QUANT_TYPES = {"nf4": 0, "fp4": 1, "int8": 3, "fp8": 4, "bf16": 5, "fp16": 6}
 EIGHT_BIT = ("int8", "fp8")  # one byte per element: packed stacks are [E, N, K]
+PASSTHROUGH = ("bf16", "fp16")  # the weights themselves, [E, N, K], no absmax
+WHOLE = EIGHT_BIT + PASSTHROUGH  # one element per K position
 
 
 def _qt(quant_type: str) -> int:
@@ -188,11 +190,21 @@ def packed_bytes(E: int, N: int, K: int) -> int:
 
 
 def quantize(w, nonfinite_flag=None, quant_type: str = "nf4"):
-    """Quantise w [E, N, K] (fp32 or bf16, GPU) -> (packed u8, absmax f32)."""
+    """Quantise w [E, N, K] (fp32 or bf16, GPU) -> (packed u8, absmax f32).
+
+    The passthrough modes return (the [E, N, K] bf16 / fp16 weights, None).
+    """
     torch = _torch()
     if w.dim() != 3:
         raise ValueError("w must be [E, N, K]")
     E, N, K = w.shape
+    if quant_type in PASSTHROUGH:
+        dt = torch.bfloat16 if quant_type == "bf16" else torch.float16
+        packed = torch.empty((E, N, K), dtype=dt, device=w.device)
+        args = (_ptr(w), _dtype_code(w.dtype), E, N, K, 64, _ptr(packed), None,
+                _ptr(nonfinite_flag), _stream(w.device))
+        _check(load().nbit_quantize_experts(_qt(quant_type), *args))
+        return packed, None
     per_byte = 1 if quant_type in EIGHT_BIT else 2
     packed = torch.empty((E, N, K // per_byte), dtype=torch.uint8, device=w.device)
     absmax = torch.empty((E, N, max(K // 64, 1)), dtype=torch.float32, device=w.device)
@@ -249,7 +261,7 @@ def grouped_gemm(a, packed, absmax, offsets, P: int, gather=None, gather_div: in
     """
     torch = _torch()
     E, N, K2 = packed.shape
-    K = K2 if quant_type in EIGHT_BIT else K2 * 2
+    K = K2 if quant_type in WHOLE else K2 * 2
     n_out = N // 2 if swiglu else N
     if out is None:
         rows = out_rows if out_rows is not None else P
@@ -284,7 +296,7 @@ def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
     torch = _torch()
     T, H = x.shape
     E = logits.shape[1]
-    I = dn_packed.shape[2] * (1 if quant_type in EIGHT_BIT else 2)
+    I = dn_packed.shape[2] * (1 if quant_type in WHOLE else 2)
     if y is None:
         y = torch.empty((T, H), dtype=y_dtype or torch.bfloat16, device=x.device)
     lib = load()

@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnf4moe.so")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "dgrad.hip", "lora.hip", "gemv.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "gemm16.hip", "dgrad.hip", "lora.hip", "gemv.hip",
+           "abi.cpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

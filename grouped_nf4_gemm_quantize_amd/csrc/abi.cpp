@@ -103,9 +103,13 @@ const QuantThresholds& thresholds(int qt) {
 }
 
 bool valid_qtype(int qt) {
-  return qt == kQtNF4 || qt == kQtFP4 || qt == kQtINT8 || qt == kQtFP8;
+  return qt == kQtNF4 || qt == kQtFP4 || qt == kQtINT8 || qt == kQtFP8 || qt == kQtBF16 ||
+         qt == kQtF16;
 }
 bool is_8bit(int qt) { return qt == kQtINT8 || qt == kQtFP8; }
+bool is_16bit(int qt) { return qt == kQtBF16 || qt == kQtF16; }
+// stack bytes of one [N, K] expert block per element, times 2
+int64_t bytes_x2(int qt) { return is_16bit(qt) ? 4 : is_8bit(qt) ? 2 : 1; }
 
 std::atomic<int> g_cu_cache[64];
 
@@ -256,7 +260,7 @@ int nf4moe_codebook(float* out16) {
 
 int nbit_codebook(int quant_type, float* out16) {
   if (out16 == nullptr) return fail(NF4MOE_EINVAL, "out16 is NULL");
-  if (!valid_qtype(quant_type) || is_8bit(quant_type))
+  if (!valid_qtype(quant_type) || is_8bit(quant_type) || is_16bit(quant_type))
     return fail(NF4MOE_EINVAL, "storage mode %d has no 16-level codebook", quant_type);
   std::memcpy(out16, quant_type == kQtFP4 ? kLevelsFP4 : kLevels, sizeof(kLevels));
   return ok();
@@ -274,7 +278,7 @@ int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K) {
 static int quantize_impl(int qt, const void* w, int w_dtype, int64_t E, int64_t N,
                          int64_t K, int blocksize, uint8_t* packed,
                          float* absmax, int32_t* nonfinite_flag, void* stream) {
-  if (w == nullptr || packed == nullptr || absmax == nullptr)
+  if (w == nullptr || packed == nullptr || (absmax == nullptr && !is_16bit(qt)))
     return fail(NF4MOE_EINVAL, "w, packed and absmax must be non-null");
   if (E < 1 || N < 1 || K < 1)
     return fail(NF4MOE_EINVAL, "E, N, K must be positive (got %lld, %lld, %lld)",
@@ -291,9 +295,18 @@ static int quantize_impl(int qt, const void* w, int w_dtype, int64_t E, int64_t 
   if (!aligned(w, w_dtype == NF4MOE_F32 ? 16 : 8) || !aligned(packed, 2) ||
       !aligned(absmax, 4))
     return fail(NF4MOE_EINVAL, "misaligned buffer (w needs 16 bytes for F32, 8 for BF16)");
+  if (is_16bit(qt) && (!aligned(w, 16) || !aligned(packed, 16)))
+    return fail(NF4MOE_EINVAL, "passthrough storage needs w and packed 16-byte aligned");
   int cus = 0;
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
+  if (is_16bit(qt)) {
+    // passthrough: the weights rounded to the storage type, nothing else
+    hipError_t err = launch_to16(w, w_dtype == NF4MOE_BF16, n, qt == kQtBF16,
+                                 reinterpret_cast<uint16_t*>(packed), cus, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "passthrough conversion launch");
+    return ok();
+  }
   hipError_t err = launch_quantize(w, w_dtype, n, packed, absmax, nonfinite_flag,
                                    thresholds(qt), cus, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "quantize launch");
@@ -393,7 +406,8 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
   g.out = out;
   g.out_dtype = out_dtype;
   g.qtype = qt;
-  hipError_t err = launch_grouped_gemm(g, cus, stream);
+  hipError_t err =
+      is_16bit(qt) ? launch_grouped_gemm16(g, cus, stream) : launch_grouped_gemm(g, cus, stream);
   if (err != hipSuccess) return hip_fail(err, "grouped GEMM launch");
   return NF4MOE_OK;
 }
@@ -406,7 +420,7 @@ static int gemm_impl(int qt, const void* a, int a_dtype, int64_t a_rows,
                      int epilogue, const float* row_scale,
                      const int32_t* scatter, void* out, int out_dtype,
                      void* stream) {
-  if (a == nullptr || packed == nullptr || absmax == nullptr ||
+  if (a == nullptr || packed == nullptr || (absmax == nullptr && !is_16bit(qt)) ||
       expert_offsets == nullptr || out == nullptr)
     return fail(NF4MOE_EINVAL, "a, packed, absmax, expert_offsets and out must be non-null");
   if (E < 1 || E > NF4MOE_MAX_EXPERTS)
@@ -431,9 +445,9 @@ static int gemm_impl(int qt, const void* a, int a_dtype, int64_t a_rows,
   // the kernel addresses activations and one expert's weights with 32-bit
   // byte offsets
   if (a_rows * K * 2 > (int64_t)UINT32_MAX ||
-      N * K / (is_8bit(qt) ? 1 : 2) > (int64_t)UINT32_MAX)
+      N * K * bytes_x2(qt) / 2 > (int64_t)UINT32_MAX)
     return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
-  if (lora != nullptr && (is_8bit(qt) || qt == kQtMXFP4))
+  if (lora != nullptr && (is_8bit(qt) || is_16bit(qt) || qt == kQtMXFP4))
     return fail(NF4MOE_EINVAL, "adapters are supported on nf4 and fp4 stacks only");
   int st = check_lora(lora, "lora");
   if (st != NF4MOE_OK) return st;
@@ -505,8 +519,8 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
                        void* y, int y_dtype, void* workspace, size_t ws_bytes,
                        void* stream) {
   if (x == nullptr || router_logits == nullptr || gu_packed == nullptr ||
-      gu_absmax == nullptr || dn_packed == nullptr || dn_absmax == nullptr ||
-      y == nullptr)
+      dn_packed == nullptr || y == nullptr ||
+      (!is_16bit(qt) && (gu_absmax == nullptr || dn_absmax == nullptr)))
     return fail(NF4MOE_EINVAL, "x, router_logits, the four stack buffers and y must be non-null");
   int st = check_route_shape(T, E, k);
   if (st != NF4MOE_OK) return st;
@@ -527,7 +541,7 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   // the GEMMs address activations and one expert's weights with 32-bit byte
   // offsets
   if (T * H * 2 > (int64_t)UINT32_MAX || P * I * 2 > (int64_t)UINT32_MAX ||
-      2 * (int64_t)I * H / (is_8bit(qt) ? 1 : 2) > (int64_t)UINT32_MAX)
+      2 * (int64_t)I * H * bytes_x2(qt) / 2 > (int64_t)UINT32_MAX)
     return fail(NF4MOE_EOVERFLOW, "activations or one expert's stack exceed 4 GiB");
   if (!aligned(x, 16) || !aligned(gu_packed, 16) || !aligned(dn_packed, 16) ||
       !aligned(gu_absmax, 4) || !aligned(dn_absmax, 4) || !aligned(y, 16))
@@ -546,9 +560,10 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   int32_t* ids = (int32_t*)(ws + L.ids);
   float* wts = (float*)(ws + L.w);
 
-  if ((gu_lora != nullptr || dn_lora != nullptr) && (is_8bit(qt) || qt == kQtMXFP4))
+  if ((gu_lora != nullptr || dn_lora != nullptr) &&
+      (is_8bit(qt) || is_16bit(qt) || qt == kQtMXFP4))
     return fail(NF4MOE_EINVAL, "adapters are supported on nf4 and fp4 stacks only");
-  if (!is_8bit(qt) && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
+  if (!is_8bit(qt) && !is_16bit(qt) && use_decode_path(T, H, I, k, gu_lora, dn_lora)) {
     GemvArgs g{};
     g.x = x;
     g.x_bf16 = x_dtype == NF4MOE_BF16;

@@ -41,6 +41,8 @@ constexpr int kQtFP4 = 1;
 constexpr int kQtMXFP4 = 2;  // e2m1 + e8m0 per 32, low nibble first (own entry points)
 constexpr int kQtINT8 = 3;   // 8-bit codes: int8, value = code / 127 * absmax
 constexpr int kQtFP8 = 4;    // 8-bit codes: fp8 e4m3, value = e4m3(code) / 448 * absmax
+constexpr int kQtBF16 = 5;   // passthrough: the weights themselves as bf16, no absmax
+constexpr int kQtF16 = 6;    // passthrough: the weights themselves as fp16, no absmax
 }  // namespace nf4moe
 
 namespace nf4moe {

@@ -79,6 +79,12 @@ constexpr int kGemmBM = 128;  // rows of an M-tile (one expert's rows only)
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus,
                                hipStream_t stream);
+// The same contract on a 16-bit passthrough stack (qtype kQtBF16 / kQtF16:
+// packed is the [E, N, K] weights, absmax unused, no adapters).
+hipError_t launch_grouped_gemm16(const GemmArgs& g, int num_cus, hipStream_t stream);
+// fp32 or bf16 weights -> bf16 or fp16 (round to nearest even); n % 8 == 0.
+hipError_t launch_to16(const void* w, bool w_bf16, int64_t n, bool out_bf16, uint16_t* out,
+                       int num_cus, hipStream_t s);
 
 struct GemvArgs {
   const void* x;  // [H] bf16 or f16

@@ -316,15 +316,27 @@ int moe_expert_backward(const void* x, int x_dtype, const float* router_logits,
  *                  nearest OCP fp8 e4m3 value of x/absmax * 448 (ties to the
  *                  even mantissa; zero of either sign is code 0), value =
  *                  e4m3(code) / 448 * absmax.
- * The 8-bit modes have no 16-level codebook (nbit_codebook returns
- * NF4MOE_EINVAL), run the grouped kernels for every T, and take no adapters;
- * the dgrad and the backward take nf4 and fp4 only.  The pages name int8 and
- * fp8 blockwise modes of ExpertsNbit but not their maps; these are the plain
+ *   NF4MOE_QT_BF16 passthrough: packed is the weights themselves, [E, N, K]
+ *   NF4MOE_QT_F16  bf16 (resp. fp16) values, 2 bytes per element, rounded
+ *                  to nearest even from the input by nbit_quantize_experts
+ *                  (fp32 beyond fp16's range becomes +-inf); absmax is
+ *                  neither written nor read and may be NULL; the
+ *                  nonfinite flag is not set.  The GEMM multiplies in fp16
+ *                  (bf16 weights converted in registers: exact in fp16's
+ *                  normal range, smaller magnitudes rounded to fp16
+ *                  subnormals) with fp32 accumulation.
+ * The 8-bit and 16-bit modes have no 16-level codebook (nbit_codebook
+ * returns NF4MOE_EINVAL), run the grouped kernels for every T, and take no
+ * adapters; the dgrad and the backward take nf4 and fp4 only.  The pages
+ * name int8, fp8, bf16 and fp16 modes of ExpertsNbit (README "Training +
+ * expert offload", QUANT_TYPE) but not the 8-bit maps; these are the plain
  * absmax-scaled readings.  An unknown mode returns NF4MOE_EINVAL. */
 #define NF4MOE_QT_NF4 0
 #define NF4MOE_QT_FP4 1
 #define NF4MOE_QT_INT8 3
 #define NF4MOE_QT_FP8 4
+#define NF4MOE_QT_BF16 5
+#define NF4MOE_QT_F16 6
 int nbit_codebook(int quant_type, float* out16);  /* [host] levels by code */
 int nbit_quantize_experts(int quant_type, const void* w, int w_dtype, int64_t E,
                           int64_t N, int64_t K, int blocksize, uint8_t* packed,

@@ -76,6 +76,17 @@ from .mxfp4 import (  # noqa: F401
     grouped_gemm_mxfp4,
     moe_forward_mxfp4,
 )
+from .passthrough import (  # noqa: F401
+    PASSTHROUGH,
+    bf16_store,
+    bf16_value,
+    fp16_store,
+    fp16_value,
+    store16,
+    value16,
+    grouped_gemm16,
+    moe_forward16,
+)
 from .nbit8 import (  # noqa: F401
     e4m3_value,
     int8_code,

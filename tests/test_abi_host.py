@@ -81,6 +81,28 @@ def test_nbit_entry_points_reject_unknown_modes(lib):
     assert lib.nbit_quantize_experts(1, FAKE, 0, 1, 1, 64, 32, FAKE, FAKE, None, None) == -3
 
 
+def test_passthrough_modes_host_checks(lib):
+    """bf16 (5) and fp16 (6) passthrough: no codebook, no absmax needed, no
+    adapters, no dgrad; the 4- and 8-bit modes still need their absmax."""
+    buf = (ctypes.c_float * 16)()
+    assert lib.nbit_codebook(5, buf) == -1 and lib.nbit_codebook(6, buf) == -1
+    gemm = lambda qt, absmax, lora: lib.grouped_nbit_gemm(
+        qt, FAKE, 2, 8, None, 1, FAKE, absmax, FAKE, 1, 8, 64, 64, lora, 0, None, None,
+        FAKE, 2, None)
+    good = binding.LoraStruct(FAKE, FAKE, 8, 2.0, 1)
+    assert gemm(5, None, ctypes.byref(good)) == -1   # absmax may be NULL; adapters refused
+    assert "adapters" in _last(lib)
+    assert gemm(6, None, ctypes.byref(good)) == -1
+    assert gemm(3, None, None) == -1                 # int8 needs its absmax
+    assert "absmax" in _last(lib)
+    assert lib.grouped_nbit_gemm_dgrad(5, FAKE, 2, 8, None, 1, FAKE, None, FAKE, 1, 8, 64, 64,
+                                       0, None, 2, None, None, FAKE, 2, None) == -1
+    # the conversion needs 16-byte aligned buffers (bf16 input at 8 bytes)
+    assert lib.nbit_quantize_experts(5, FAKE + 8, 1, 1, 1, 64, 64, FAKE, None, None,
+                                     None) == -1
+    assert "16-byte" in _last(lib)
+
+
 @pytest.mark.parametrize("E,N,K", [(128, 1536, 2048), (128, 2048, 768), (8, 256, 256),
                                    (64, 2048, 2048), (1, 16, 64)])
 def test_packed_bytes_matches_the_format(lib, E, N, K):
