@@ -8,15 +8,15 @@
 // the 4-bit code bytes, so this kernel has its own, simpler tiling rather
 // than a mode of the 4-bit one:
 //
-//   - tile: 128 rows of one expert x 256 weight rows (SwiGLU: the gate and
-//     up rows of 128 output columns), 64-wide k-steps; 8 waves as 2 (M) x 4
-//     (N), each 64 rows x 64 weight rows = 2 x 2 accumulator tiles of
+//   - tile: 256 rows of one expert x 256 weight rows (SwiGLU: the gate and
+//     up rows of 128 output columns), 32-wide k-steps; 8 waves as 2 (M) x 4
+//     (N), each 128 rows x 64 weight rows = 4 x 2 accumulator tiles of
 //     v_mfma_f32_32x32x16_f16 with the weights as the first operand, so an
 //     accumulator tile is the transposed output block (lane: output row
 //     lane & 31; column 8 (j / 4) + 4 (lane / 32) + j % 4);
-//   - staging: a 3-stage ring (activations 16 KB + weights 32 KB per
+//   - staging: a 3-stage ring (activations 16 KB + weights 16 KB per
 //     stage), batches copied up to three steps ahead straight to LDS; the
-//     16-byte chunk c of a 128-byte row r sits at c ^ ((r >> 1) & 7), so the
+//     16-byte chunk c of a 64-byte row r sits at c ^ ((r >> 2) & 3), so the
 //     16 lanes of a fragment read cover all 64 banks;
 //   - operands: fp16 MFMA.  bf16 weights are converted to fp16 in
 //     registers (exact for magnitudes in fp16's normal range; smaller ones
@@ -24,7 +24,10 @@
 //     fp16 activations with bf16 weights needs fp16 operands to keep fp16's
 //     mantissa on the activations.
 //
-// Tiles are dealt to a persistent grid round-robin, expert-major, by XCD.
+// An expert's 16-bit gate_up block (8 MB at olmoe size) does not fit an
+// XCD's 4 MB L2, so each row tile reads its expert's weights again: 256-row
+// tiles halve that traffic against 128-row ones.  Tiles are dealt to a
+// persistent grid round-robin, expert-major, by XCD.
 
 #include "common.h"
 #include "launch.h"
@@ -34,18 +37,18 @@ namespace nf4moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;               // 128 rows per tile
-constexpr int BK = 64;                    // k per step (128 bytes of a row)
-constexpr int BN = 256;                   // weight rows per tile
+constexpr int BM = 256;                   // rows per tile
+constexpr int BK = 32;                    // k per step (64 bytes of a row)
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int WN = 4;                     // waves along N (2 along M)
-constexpr int MT = 2;                     // 32-row m-tiles per wave
+constexpr int MT = 4;                     // 32-row m-tiles per wave (128 rows)
 constexpr int NT = 2;                     // 32-row n-tiles per wave
+constexpr int BN = WN * NT * 32;          // 256 weight rows per tile
 constexpr int A_BYTES = BM * BK * 2;      // 16 KB
-constexpr int B_BYTES = BN * BK * 2;      // 32 KB
-constexpr int STAGE = A_BYTES + B_BYTES;  // 48 KB
-constexpr int kDma = 6;                   // copies per wave and step: 2 + 4
+constexpr int B_BYTES = BN * BK * 2;      // 16 KB
+constexpr int STAGE = A_BYTES + B_BYTES;  // 32 KB
+constexpr int kDma = 4;                   // copies per wave and step: 2 + 2
 
 __shared__ __attribute__((aligned(16))) char s_ring[3 * STAGE];
 __shared__ int32_t s_tiles[kMaxExperts + 1];
@@ -56,19 +59,19 @@ __shared__ float s_rscale[2][BM];    // row scale of each tile row
 struct Src16 {
   i32x4 a_rsrc, b_rsrc;
   uint32_t a_off[2];  // activations: 2 x 16 B per lane and step
-  uint32_t b_off[4];  // weights: 4 x 16 B per lane and step
+  uint32_t b_off[2];  // weights: 2 x 16 B per lane and step
 };
 
 // Batch kb (clamped by the caller) into the stage at LDS address st: wave
-// instruction i of the activations covers LDS rows 8 (2 wave + i) .. +8, of
-// the weights rows 8 (4 wave + i) .. +8 (64 lanes x 16 B = 8 rows).
+// instruction i covers LDS rows 16 (2 wave + i) .. +16 of the activations,
+// and of the weights (64 lanes x 16 B = 16 rows of 64 B).
 __device__ __forceinline__ void issue(const Src16& s, int kb, uint32_t st, int wave) {
   const uint32_t soff = (uint32_t)kb * (BK * 2);
 #pragma unroll
   for (int i = 0; i < 2; ++i) dma16(s.a_rsrc, s.a_off[i], soff, st + (wave * 2 + i) * 1024);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma16(s.b_rsrc, s.b_off[i], soff, st + A_BYTES + (wave * 4 + i) * 1024);
+  for (int i = 0; i < 2; ++i)
+    dma16(s.b_rsrc, s.b_off[i], soff, st + A_BYTES + (wave * 2 + i) * 1024);
 }
 
 template <bool kBf16>
@@ -78,26 +81,26 @@ __device__ __forceinline__ f16x8 frag(const char* p) {
   return as_f16x8(v);
 }
 
-// The fragments of substep s (k chunk 4 g2 + s of each row) from stage st.
+// The fragments of substep s (k chunk 2 s + g2 of each row) from stage st.
 template <bool kABf16, bool kWBf16>
 __device__ __forceinline__ void load_frags(const char* st, uint32_t ro, uint32_t a_base,
                                            uint32_t b_base, f16x8 (&af)[MT], f16x8 (&bf)[NT]) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) af[mt] = frag<kABf16>(st + a_base + mt * 32 * 128 + ro);
+  for (int mt = 0; mt < MT; ++mt) af[mt] = frag<kABf16>(st + a_base + mt * 32 * 64 + ro);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) bf[nt] = frag<kWBf16>(st + A_BYTES + b_base + nt * 32 * 128 + ro);
+  for (int nt = 0; nt < NT; ++nt) bf[nt] = frag<kWBf16>(st + A_BYTES + b_base + nt * 32 * 64 + ro);
 }
 
 // Substep S of a step: its MFMAs on af/bf while the next substep's
-// fragments are read (for S = 3 those of the next step's substep 0, from
+// fragments are read (for S = 1 those of the next step's substep 0, from
 // the next stage).
 template <int S, bool kABf16, bool kWBf16>
-__device__ __forceinline__ void substep(const char* st, const char* nst, const uint32_t (&ro)[4],
+__device__ __forceinline__ void substep(const char* st, const char* nst, const uint32_t (&ro)[2],
                                         uint32_t a_base, uint32_t b_base, int mtv,
                                         f16x8 (&af)[MT], f16x8 (&bf)[NT],
                                         f32x16 (&acc)[MT][NT]) {
   f16x8 an[MT], bn[NT];
-  if constexpr (S < 3) load_frags<kABf16, kWBf16>(st, ro[S + 1], a_base, b_base, an, bn);
+  if constexpr (S == 0) load_frags<kABf16, kWBf16>(st, ro[1], a_base, b_base, an, bn);
   else load_frags<kABf16, kWBf16>(nst, ro[0], a_base, b_base, an, bn);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -115,14 +118,14 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const u
 
 // The k-loop of one tile.  Batch kb goes into stage kb % 3; the prologue
 // issues batches 0, 1, 2.  After the barrier of step kb (every wave has read
-// its fragments of stage kb % 3: substep 2 read the last ones) the wave
+// its fragments of stage kb % 3: substep 0 read the last ones) the wave
 // issues batch kb + 3 there.  Before that barrier step kb + 1 must have
 // landed, while batch kb + 2 may be pending: the wait leaves kDma copies.
 // Nothing past the last step is fetched (only the prologue repeats the last
 // batch when there are fewer than three steps); in the last two steps batch
 // kb + 2 does not exist, so they drain instead.
 template <bool kABf16, bool kWBf16>
-__device__ __forceinline__ void kloop(const Src16& src, int nk, const uint32_t (&ro)[4],
+__device__ __forceinline__ void kloop(const Src16& src, int nk, const uint32_t (&ro)[2],
                                       uint32_t a_base, uint32_t b_base, int mtv, int wave,
                                       f32x16 (&acc)[MT][NT]) {
   const uint32_t ring = lds_addr(s_ring);
@@ -139,12 +142,10 @@ __device__ __forceinline__ void kloop(const Src16& src, int nk, const uint32_t (
     const char* st = s_ring + sidx * STAGE;
     const char* nst = s_ring + nidx * STAGE;
     substep<0, kABf16, kWBf16>(st, nst, ro, a_base, b_base, mtv, af, bf, acc);
-    substep<1, kABf16, kWBf16>(st, nst, ro, a_base, b_base, mtv, af, bf, acc);
-    substep<2, kABf16, kWBf16>(st, nst, ro, a_base, b_base, mtv, af, bf, acc);
     if (kb >= last - 1) wait_vm_barrier<0>();
     else wait_vm_barrier<kDma>();
     if (kb + 3 <= last) issue(src, kb + 3, ring + sidx * STAGE, wave);
-    substep<3, kABf16, kWBf16>(st, nst, ro, a_base, b_base, mtv, af, bf, acc);
+    substep<1, kABf16, kWBf16>(st, nst, ro, a_base, b_base, mtv, af, bf, acc);
     sidx = nidx;
   }
 }
@@ -177,16 +178,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm16_kernel(GemmArgs g,
 
   const int N = g.N, K = g.K, I = N >> 1;
   const int nk = K / BK;
-  // fragment offsets: row n32 of a 32-row block, k chunk 4 g2 + s
-  uint32_t ro[4];
+  // fragment offsets: row n32 of a 32-row block, k chunk 2 s + g2
+  uint32_t ro[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) ro[s] = n32 * 128 + (((g2 * 4 + s) ^ ((n32 >> 1) & 7)) << 4);
-  const uint32_t a_base = (uint32_t)wm * 64 * 128;
-  const uint32_t b_base = (uint32_t)wn * 64 * 128;
+  for (int s = 0; s < 2; ++s) ro[s] = n32 * 64 + (((2 * s + g2) ^ ((n32 >> 2) & 3)) << 4);
+  const uint32_t a_base = (uint32_t)wm * 128 * 64;
+  const uint32_t b_base = (uint32_t)wn * 64 * 64;
 
   // weight row of LDS B row l (0..255) of N-tile n_idx, clamped to a valid
-  // row.  SwiGLU: wave wn's n-tile 0 holds the gate rows and n-tile 1 the up
-  // rows of output columns n_idx * 128 + 32 wn + [0, 32).
+  // row.  SwiGLU: wave column wn's n-tile 0 holds the gate rows and n-tile 1
+  // the up rows of output columns n_idx * 128 + 32 wn + [0, 32).
   auto weight_row = [&](int l, int n_idx) -> int {
     if constexpr (kSwiglu) {
       const int w = l >> 6, nt = (l >> 5) & 1, n = l & 31;
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm16_kernel(GemmArgs g,
     const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + m_local * BM;
     const int rows_valid = min(BM, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
     // this wave's valid 32-row m-tiles
-    const int mtv = max(0, min(MT, (rows_valid - wm * 64 + 31) >> 5));
+    const int mtv = max(0, min(MT, (rows_valid - wm * 128 + 31) >> 5));
 
     Src16 src;
     src.a_rsrc = a_rsrc;
@@ -226,18 +227,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm16_kernel(GemmArgs g,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = (wave * 2 + i) * 64 + lane;
-      const int row = c >> 3;
-      const int gchunk = (c & 7) ^ ((row >> 1) & 7);
+      const int row = c >> 2;
+      const int gchunk = (c & 3) ^ ((row >> 2) & 3);
       const int rr = row < rows_valid ? row : 0;
       const int idx = row0 + rr;
       const uint32_t a_src = g.gather ? (uint32_t)(g.gather[idx] / g.gather_div) : (uint32_t)idx;
       src.a_off[i] = (a_src * (uint32_t)K + gchunk * 8) * 2;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (wave * 4 + i) * 64 + lane;
-      const int l = c >> 3;
-      const int gchunk = (c & 7) ^ ((l >> 1) & 7);
+    for (int i = 0; i < 2; ++i) {
+      const int c = (wave * 2 + i) * 64 + lane;
+      const int l = c >> 2;
+      const int gchunk = (c & 3) ^ ((l >> 2) & 3);
       src.b_off[i] = ((uint32_t)weight_row(l, n_idx) * (uint32_t)K + gchunk * 8) * 2;
     }
 
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm16_kernel(GemmArgs g,
     const int ncols = kSwiglu ? I : N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int trow = wm * 64 + mt * 32 + n32;
+      const int trow = wm * 128 + mt * 32 + n32;
       if (mt >= mtv || trow >= rows_valid) continue;
       const int64_t orow = s_orow[par][trow];
       const float rs = s_rscale[par][trow];
