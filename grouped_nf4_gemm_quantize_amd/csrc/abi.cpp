@@ -797,7 +797,8 @@ int grouped_nbit_gemm_dgrad(int quant_type, const void* a, int a_dtype, int64_t 
 
 struct BwdLayout {
   FwdLayout f;  // routing regions and x16 (h and o unused)
-  size_t dy16, g, dg, dxp, h, u_gu, v_gu, u_dn, v_dn, a16_gu, bt_gu, a16_dn, bt_dn, part, total;
+  size_t dy16, g, dg, dxp, h, u_gu, v_gu, u_dn, v_dn, a16_gu, bt_gu, a16_dn, bt_dn, b16_gu, part,
+      total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int H, int I, int E, int k, int r) {
@@ -824,6 +825,7 @@ static BwdLayout bwd_layout(int64_t T, int H, int I, int E, int k, int r) {
   L.bt_gu = take((size_t)E * rr * 2 * I * 2);
   L.a16_dn = take((size_t)E * rr * I * 2);
   L.bt_dn = take((size_t)E * rr * H * 2);
+  L.b16_gu = take((size_t)E * 2 * I * rr * 2);  // B_gu as fp16 [E, 2I, r] (recompute)
   const size_t cmax = (size_t)(H > 2 * I ? H : 2 * I);
   L.part = take(rr ? ((P + 63) / 64 + (size_t)E) * rr * cmax * 4 : 0);
   L.total = o;
@@ -968,9 +970,33 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     dyh = ws + L.dy16;
   }
 
-  // 2. recompute the gate_up pre-activation G = x W_gu^T (+ LoRA), fp16
+  // 2. recompute the gate_up pre-activation G = x W_gu^T (+ LoRA), fp16.
+  //    A_gu goes to fp16 once here (the adapter passes below read it too);
+  //    bf16 adapters get an fp16 B_gu as well, so the recompute's k-loop
+  //    reads fp16 adapter rows (the same rounding the GEMM would apply)
+  nf4moe_lora gu16{};
+  const nf4moe_lora* gu_rc = gu_lora;
+  if (gu_lora) {
+    const int bf = gu_lora->dtype == NF4MOE_BF16;
+    err = launch_lora_to_f16(gu_lora->A, bf, 0, E, H, r, a16_gu, cus, s);
+    if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
+    if (bf) {
+      HalfCopies hc{};
+      hc.src[0] = (const uint16_t*)gu_lora->B;
+      hc.dst[0] = (_Float16*)(ws + L.b16_gu);
+      hc.n8[0] = (int64_t)E * 2 * I * r / 8;
+      hc.count = 1;
+      err = launch_half_copies(hc, cus, s);
+      if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
+      gu16 = *gu_lora;
+      gu16.A = a16_gu;
+      gu16.B = ws + L.b16_gu;
+      gu16.dtype = NF4MOE_F16;
+      gu_rc = &gu16;
+    }
+  }
   st = gemm_common(xa, NF4MOE_F16, T, sorted, k, gu_packed, gu_absmax, offs, E, P,
-                   2 * (int64_t)I, H, gu_lora, NF4MOE_EPI_NONE, nullptr, nullptr, G,
+                   2 * (int64_t)I, H, gu_rc, NF4MOE_EPI_NONE, nullptr, nullptr, G,
                    NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;
 
@@ -1011,9 +1037,7 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
   //    v1 = dG1 B_gu and dB_gu = s sum w dG1 u^T
   if (gu_lora) {
     const int bf = gu_lora->dtype == NF4MOE_BF16;
-    err = launch_lora_to_f16(gu_lora->A, bf, 0, E, H, r, a16_gu, cus, s);
-    if (err == hipSuccess)
-      err = launch_lora_to_f16(gu_lora->B, bf, 1, E, 2 * I, r, bt_gu, cus, s);
+    err = launch_lora_to_f16(gu_lora->B, bf, 1, E, 2 * I, r, bt_gu, cus, s);
     if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
     st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, a16_gu, u_gu, nullptr, nullptr, nullptr,
                    nullptr, nullptr, 0.f, 0, cus, s);

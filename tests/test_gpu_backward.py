@@ -276,6 +276,27 @@ def test_backward_is_deterministic(gpu_lib):
         assert torch.equal(g1[k], g2[k]), k
 
 
+def test_backward_bf16_adapters_match_their_f16_copies_bitwise(gpu_lib):
+    """bf16 adapters are rounded to fp16 (nearest even) for the recomputed
+    gate_up and the adapter passes; handing in the same adapters already
+    rounded by torch gives the same dx and adapter gradients, bit for bit."""
+    cfg = synth.config("tiny", T=200, lora_r=8, lora_alpha=16.0)
+    gp, ga, dp, da = _stacks(cfg)
+    x = gpu(synth.activations(cfg), torch.bfloat16)
+    lg = gpu(synth.router_logits(cfg))
+    dy = gpu(synth.output_grad(cfg), torch.bfloat16)
+    glo, dlo, _, _ = _lora(cfg)
+    half = lambda lo: (lo[0].half(), lo[1].half(), lo[2])
+    st = (gpu(gp), gpu(ga), gpu(dp), gpu(da))
+    dx1, g1 = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo, dx_dtype=torch.float32)
+    dx2, g2 = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, half(glo), half(dlo),
+                                   dx_dtype=torch.float32)
+    assert torch.equal(dx1, dx2)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+    assert torch.count_nonzero(g1["dA_gu"]) > 0
+
+
 def test_backward_with_zero_b_has_zero_a_gradient(gpu_lib):
     """B = 0 adapters: dA is exactly zero and dx equals the adapter-free dx."""
     cfg = synth.config("tiny", lora_r=8, lora_alpha=16.0)
