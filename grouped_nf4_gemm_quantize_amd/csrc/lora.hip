@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void lora_to_f16_kernel(const uint16_t* __rest
 // the sum over rows).  Wave w projects rows 16w..16w+15 and sums columns
 // 16w..16w+15 of each chunk; ranks beyond r are zero.
 constexpr int kPitch = 64 * 2 + 16;  // LDS row pitch of a staged chunk (bytes)
+constexpr int kAhead = 4;            // chunks of m in flight per thread
 
 template <bool kProj, bool kGrad, bool kMBf16>
 __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
@@ -197,66 +198,82 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
     }
     __syncthreads();
     f32x4 accp = {0.f, 0.f, 0.f, 0.f};
-    // this thread's two 16-byte pieces of a chunk: rows tid/8 and tid/8 + 32,
-    // columns 8 * (tid % 8)
-    const int lr = tid >> 3, lc = (tid & 7) * 8;
-    u32x4 pre[2];
-    auto load_chunk = [&](int ch) {
+    // this thread's two 16-byte pieces of a chunk: row tid % 64, columns
+    // 8 g and 8 (g + 4) with g = tid / 64, so a wave's lanes are 64
+    // consecutive rows of one 8-column group: its column-major writes are
+    // 128 contiguous bytes each (no bank conflict).  kAhead chunks are in
+    // flight (a register ring over the unrolled chunk loop): with one, each
+    // chunk waited a full memory round trip.
+    const int rr = tid & 63;
+    u32x4 pre[kAhead][2];
+    auto load_chunk = [&](int ch, u32x4 (&dst)[2]) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int rr = lr + 32 * h;
+        const int lc = 8 * ((tid >> 6) + 4 * h);
         u32x4 v = {0u, 0u, 0u, 0u};
         if (rr < rows) {
           v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.m) +
                                               (int64_t)srcs[rr] * a.C + ch * 64 + lc);
           if constexpr (kMBf16) v = bf16x8_to_f16x8(v);
         }
-        pre[h] = v;
+        dst[h] = v;
       }
     };
-    load_chunk(0);
-    for (int ch = 0; ch < nchunk; ++ch) {
-      __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rr = lr + 32 * h;
-        *reinterpret_cast<u32x4*>(nat + rr * kPitch + lc * 2) = pre[h];
-        const uint32_t w4[4] = {pre[h].x, pre[h].y, pre[h].z, pre[h].w};
+    for (int p = 0; p < kAhead; ++p)
+      if (p < nchunk) load_chunk(p, pre[p]);
+    for (int ch0 = 0; ch0 < nchunk; ch0 += kAhead) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          *reinterpret_cast<uint16_t*>(tr + (lc + 2 * t) * kPitch + rr * 2) = (uint16_t)(w4[t] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(tr + (lc + 2 * t + 1) * kPitch + rr * 2) = (uint16_t)(w4[t] >> 16);
+      for (int p = 0; p < kAhead; ++p) {
+        const int ch = ch0 + p;
+        if (ch >= nchunk) break;
+        __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int lc = 8 * ((tid >> 6) + 4 * h);
+          if constexpr (kProj)
+            *reinterpret_cast<u32x4*>(nat + rr * kPitch + lc * 2) = pre[p][h];
+          if constexpr (kGrad) {
+            const uint32_t w4[4] = {pre[p][h].x, pre[p][h].y, pre[p][h].z, pre[p][h].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              *reinterpret_cast<uint16_t*>(tr + (lc + 2 * t) * kPitch + rr * 2) =
+                  (uint16_t)(w4[t] & 0xffffu);
+              *reinterpret_cast<uint16_t*>(tr + (lc + 2 * t + 1) * kPitch + rr * 2) =
+                  (uint16_t)(w4[t] >> 16);
+            }
+          }
         }
-      }
-      __syncthreads();
-      if (ch + 1 < nchunk) load_chunk(ch + 1);
-      if constexpr (kProj) {
+        __syncthreads();
+        if (ch + kAhead < nchunk) load_chunk(ch + kAhead, pre[p]);
+        if constexpr (kProj) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(nat + (16 * wave + l16) * kPitch +
-                                                           (32 * u + 8 * g4) * 2);
-          u32x4 bv = {0u, 0u, 0u, 0u};
-          if (l16 < a.r)
-            bv = *reinterpret_cast<const u32x4*>(a.w + ((int64_t)e * a.r + l16) * a.C +
-                                                 ch * 64 + 32 * u + 8 * g4);
-          accp = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(bv), accp, 0, 0, 0);
+          for (int u = 0; u < 2; ++u) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(nat + (16 * wave + l16) * kPitch +
+                                                             (32 * u + 8 * g4) * 2);
+            u32x4 bv = {0u, 0u, 0u, 0u};
+            if (l16 < a.r)
+              bv = *reinterpret_cast<const u32x4*>(a.w + ((int64_t)e * a.r + l16) * a.C +
+                                                   ch * 64 + 32 * u + 8 * g4);
+            accp = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(bv), accp, 0, 0, 0);
+          }
         }
-      }
-      if constexpr (kGrad) {
-        f32x4 accg = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kGrad) {
+          f32x4 accg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f16x8 qa = *reinterpret_cast<const f16x8*>(&qt[l16][32 * u + 8 * g4]);
-          const u32x4 bv = *reinterpret_cast<const u32x4*>(tr + (16 * wave + l16) * kPitch +
-                                                           (32 * u + 8 * g4) * 2);
-          accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_f16x8(bv), accg, 0, 0, 0);
-        }
-        // lane holds ranks 4 g4 + t of column 16 wave + l16
-        float* part = a.part + (int64_t)tix * a.r * a.C + ch * 64 + 16 * wave + l16;
+          for (int u = 0; u < 2; ++u) {
+            const f16x8 qa = *reinterpret_cast<const f16x8*>(&qt[l16][32 * u + 8 * g4]);
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(tr + (16 * wave + l16) * kPitch +
+                                                             (32 * u + 8 * g4) * 2);
+            accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_f16x8(bv), accg, 0, 0, 0);
+          }
+          // lane holds ranks 4 g4 + t of column 16 wave + l16
+          float* part = a.part + (int64_t)tix * a.r * a.C + ch * 64 + 16 * wave + l16;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int j = 4 * g4 + t;
-          if (j < a.r) part[(int64_t)j * a.C] = accg[t] * qexp[j][1];
+          for (int t = 0; t < 4; ++t) {
+            const int j = 4 * g4 + t;
+            if (j < a.r) part[(int64_t)j * a.C] = accg[t] * qexp[j][1];
+          }
         }
       }
     }
