@@ -601,7 +601,9 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   r.expert_offsets = (int32_t*)(ws + L.offsets);
   r.chunk_masks = (uint32_t*)(ws + L.route + L.r.masks);
   r.chunk_base = (int32_t*)(ws + L.route + L.r.base);
-  const bool conv = x_dtype == NF4MOE_BF16;
+  // bf16 activations go to fp16 once for the GEMMs, except on a bf16
+  // passthrough stack, whose gate_up multiplies bf16 by bf16 as stored
+  const bool conv = x_dtype == NF4MOE_BF16 && qt != kQtBF16;
   r.x_in = x;
   r.x_bf16 = conv ? 1 : 0;
   r.x16 = conv ? (_Float16*)(ws + L.x16) : nullptr;
@@ -638,9 +640,10 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
   }
 
   const void* xa = conv ? (const void*)(ws + L.x16) : x;
+  const int xa_dtype = conv ? NF4MOE_F16 : x_dtype;
   _Float16* h = (_Float16*)(ws + L.h);
   _Float16* o = (_Float16*)(ws + L.o);
-  st = gemm_common(xa, NF4MOE_F16, T, r.sorted_pair, k, gu_packed, gu_absmax,
+  st = gemm_common(xa, xa_dtype, T, r.sorted_pair, k, gu_packed, gu_absmax,
                    r.expert_offsets, E, P, 2 * (int64_t)I, H, gu_l,
                    NF4MOE_EPI_SWIGLU, nullptr, nullptr, h, NF4MOE_F16, qt, s);
   if (st != NF4MOE_OK) return st;

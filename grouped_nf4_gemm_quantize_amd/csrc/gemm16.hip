@@ -18,10 +18,11 @@
 //     stage), batches copied up to three steps ahead straight to LDS; the
 //     16-byte chunk c of a 64-byte row r sits at c ^ ((r >> 2) & 3), so the
 //     16 lanes of a fragment read cover all 64 banks;
-//   - operands: fp16 MFMA.  bf16 weights are converted to fp16 in
-//     registers (exact for magnitudes in fp16's normal range; smaller ones
-//     round to fp16 subnormals), bf16 activations likewise: the product of
-//     fp16 activations with bf16 weights needs fp16 operands to keep fp16's
+//   - operands: bf16 activations with bf16 weights go to bf16 MFMAs as
+//     stored (exact products); otherwise fp16 MFMAs, bf16 weights or
+//     activations converted to fp16 in registers (exact for magnitudes in
+//     fp16's normal range; smaller ones round to fp16 subnormals): fp16
+//     activations with bf16 weights need fp16 operands to keep fp16's
 //     mantissa on the activations.
 //
 // An expert's 16-bit gate_up block (8 MB at olmoe size) does not fit an
@@ -81,14 +82,23 @@ __device__ __forceinline__ f16x8 frag(const char* p) {
   return as_f16x8(v);
 }
 
-// The fragments of substep s (k chunk 2 s + g2 of each row) from stage st.
+// bf16 activations with bf16 weights: bf16 MFMAs on the raw bits
+template <bool kABf16, bool kWBf16>
+constexpr bool kNativeBf16 = kABf16 && kWBf16;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// The fragments of substep s (k chunk 2 s + g2 of each row) from stage st
+// (raw bits for the bf16 MFMAs, else fp16).
 template <bool kABf16, bool kWBf16>
 __device__ __forceinline__ void load_frags(const char* st, uint32_t ro, uint32_t a_base,
                                            uint32_t b_base, f16x8 (&af)[MT], f16x8 (&bf)[NT]) {
+  constexpr bool kNat = kNativeBf16<kABf16, kWBf16>;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) af[mt] = frag<kABf16>(st + a_base + mt * 32 * 64 + ro);
+  for (int mt = 0; mt < MT; ++mt) af[mt] = frag<kABf16 && !kNat>(st + a_base + mt * 32 * 64 + ro);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) bf[nt] = frag<kWBf16>(st + A_BYTES + b_base + nt * 32 * 64 + ro);
+  for (int nt = 0; nt < NT; ++nt)
+    bf[nt] = frag<kWBf16 && !kNat>(st + A_BYTES + b_base + nt * 32 * 64 + ro);
 }
 
 // Substep S of a step: its MFMAs on af/bf while the next substep's
@@ -106,8 +116,14 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const u
   for (int mt = 0; mt < MT; ++mt) {
     if (mt < mtv) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nt], af[mt], acc[mt][nt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (kNativeBf16<kABf16, kWBf16>)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, bf[nt]), __builtin_bit_cast(bf16x8_t, af[mt]),
+              acc[mt][nt], 0, 0, 0);
+        else
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nt], af[mt], acc[mt][nt], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
