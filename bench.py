@@ -618,7 +618,7 @@ def main() -> int:
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the expert path here runs on a single GPU "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
