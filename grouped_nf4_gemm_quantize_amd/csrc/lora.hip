@@ -222,6 +222,20 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
 #pragma unroll
     for (int p = 0; p < kAhead; ++p)
       if (p < nchunk) load_chunk(p, pre[p]);
+    // the projection's adapter fragments (w rows l16, from L2) one chunk
+    // ahead, so no chunk waits on them
+    u32x4 wnext[2];
+    auto load_w = [&](int ch, u32x4 (&dst)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 bv = {0u, 0u, 0u, 0u};
+        if (l16 < a.r)
+          bv = *reinterpret_cast<const u32x4*>(a.w + ((int64_t)e * a.r + l16) * a.C + ch * 64 +
+                                               32 * u + 8 * g4);
+        dst[u] = bv;
+      }
+    };
+    if constexpr (kProj) load_w(0, wnext);
     for (int ch0 = 0; ch0 < nchunk; ch0 += kAhead) {
 #pragma unroll
       for (int p = 0; p < kAhead; ++p) {
@@ -247,15 +261,14 @@ __global__ __launch_bounds__(256) void lora_pass_kernel(LoraPassArgs a) {
         __syncthreads();
         if (ch + kAhead < nchunk) load_chunk(ch + kAhead, pre[p]);
         if constexpr (kProj) {
+          const u32x4 wcur[2] = {wnext[0], wnext[1]};
+          if (ch + 1 < nchunk) load_w(ch + 1, wnext);
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const u32x4 av = *reinterpret_cast<const u32x4*>(nat + (16 * wave + l16) * kPitch +
                                                              (32 * u + 8 * g4) * 2);
-            u32x4 bv = {0u, 0u, 0u, 0u};
-            if (l16 < a.r)
-              bv = *reinterpret_cast<const u32x4*>(a.w + ((int64_t)e * a.r + l16) * a.C +
-                                                   ch * 64 + 32 * u + 8 * g4);
-            accp = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(bv), accp, 0, 0, 0);
+            accp = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(av), as_f16x8(wcur[u]), accp,
+                                                          0, 0, 0);
           }
         }
         if constexpr (kGrad) {
