@@ -184,6 +184,11 @@ def test_gemm_validation(lib):
     assert call(lora=ctypes.byref(bad)) == -5
     bad = binding.LoraStruct(FAKE, FAKE, 17, 2.0, 1)
     assert call(lora=ctypes.byref(bad)) == -1
+    # sizes past the kernels' 32-bit row indexing and 32-bit buffer offsets
+    assert call(P=2**31 - 1) == -7
+    assert call(N=2**30 + 16) == -7
+    assert call(arows=2**21, K=1024) == -7  # 4 GiB of activations
+    assert call(N=2**19, K=2**14) == -7     # one expert's stack past 4 GiB
     # P == 0 is a valid empty problem: nothing is enqueued
     assert call(P=0) == 0
 
@@ -223,6 +228,11 @@ def test_forward_validation(lib):
     good = binding.LoraStruct(FAKE, FAKE, 8, 2.0, 1)
     assert call(dl=ctypes.byref(good)) == -6
     assert "adapter rank 8" in _last(lib)
+    # sizes past the 32-bit pair indexing and the kernels' 32-bit buffer offsets
+    assert call(T=2**31 // k + 1) == -7     # T * k pairs overflow int32
+    assert call(T=2**20, H=2**12) == -7     # 8 GiB of token rows
+    assert call(T=2**22, I=512) == -7       # h, T * k * I fp16 values, 8 GiB (x 2 GiB)
+    assert call(H=2**16, I=2**16) == -7     # one expert's gate_up stack past 4 GiB
 
 
 def test_status_strings(lib):
