@@ -186,7 +186,7 @@ RouteLayout route_layout(int64_t T, int E) {
 
 // ---- forward workspace layout (the same regions for every path)
 struct FwdLayout {
-  size_t ids, w, sorted, pos, offsets, route, x16, h, o, hbuf;
+  size_t ids, w, sorted, pos, offsets, route, x16, h, o, bar;
   // fp16 copies of bf16 adapters (rank r; last, so the routing views above
   // do not depend on r): A_gu [E,r,H], B_gu [E,2I,r], A_dn [E,r,I], B_dn [E,H,r]
   size_t a_gu, b_gu, a_dn, b_dn;
@@ -213,7 +213,7 @@ FwdLayout fwd_layout(int64_t T, int H, int I, int E, int k, int r = 0) {
   L.x16 = take((size_t)T * H * 2);
   L.h = take(P * (size_t)I * 2);
   L.o = take(P * (size_t)H * 2);
-  L.hbuf = take((size_t)k * I * 4);
+  L.bar = take(decode_exchange_bytes((int64_t)k * I));
   const size_t er = (size_t)E * r * 2;
   L.a_gu = take(er * H);
   L.b_gu = take(er * 2 * I);
@@ -579,7 +579,10 @@ static int forward_impl(int qt, const void* x, int x_dtype, const float* router_
     g.dn_absmax = dn_absmax;
     g.topk_ids = ids;
     g.topk_w = wts;
-    g.hbuf = ws + L.hbuf;
+    g.sorted_pair = (int32_t*)(ws + L.sorted);
+    g.expert_offsets = (int32_t*)(ws + L.offsets);
+    g.barrier = (uint64_t*)(ws + L.bar);
+    g.spin_limit = kDecodeSpinLimit;
     g.y = y;
     g.y_dtype = y_dtype;
     g.qtype = qt;

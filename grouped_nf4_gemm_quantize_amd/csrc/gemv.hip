@@ -1,22 +1,37 @@
-// Single-token (T = 1) decode path: split-K GEMVs over the routed experts.
+// Single-token (T = 1) decode path: one fused kernel over the routed experts.
 //
 // At batch 1 the expert projection is a matrix-vector product per routed
 // expert that streams the packed bytes once (experts4bit-qlora 0.22.0 README,
 // "Inference": the single-token decode fast path uses a fused 4-bit GEMV).  HBM
 // bandwidth on the NF4 codes + absmax is the roofline, and with only ~21 MB
-// per layer the time is set by the chain of dependent memory round trips, so
-// each kernel issues its weight loads as early as their addresses are known
-// and overlaps everything else (activation staging, the decode table) with
-// them.
+// per layer the time is set by the chain of dependent memory round trips:
+// the router logits, then the weights.  So one kernel does the whole layer
+// and issues every weight load -- gate/up rows and down rows alike -- as soon
+// as the routing is known:
 //
-//   gemv_gate_up_kernel  every wave routes the token itself (a top-k over the
-//     E logits costs a few hundred cycles -- cheaper than a barrier), then
-//     owns up to kMaxItems (slot j, column i) items: the gate row i and the
-//     up row I+i of expert ids[j], dotted with x; it writes
-//     h[j, i] = w_j * silu(gate) * up  (fp16).
-//   gemv_down_kernel  one wave per output row n: the K of the row is the
-//     concatenation of the k routed experts' I inputs, so the combine over
-//     the slots is part of the dot product; y[n] is written directly.
+//   1. every wave routes the token itself (a top-k over the E logits costs a
+//      few hundred cycles, cheaper than any exchange);
+//   2. it issues the loads of its (slot j, column i) gate/up items -- the gate
+//      row i and the up row I+i of expert ids[j] -- and of its down output
+//      row n, whose K is the concatenation of the k experts' I inputs (so the
+//      combine over the slots is part of the dot product);
+//   3. while they are in flight it stages x as fp16 and builds the decode
+//      table, then computes h[j, i] = w_j * silu(gate) * up (fp32) and
+//      publishes it;
+//   4. a grid-wide exchange of h: each workgroup writes its h values, then its
+//      flag; every workgroup waits for all flags (a bounded wait), then reads
+//      the whole h (fp16 in LDS) and finishes its down rows, whose weights
+//      arrived meanwhile.
+//
+// The exchange needs every workgroup resident at once: the grid is at most one
+// workgroup per compute unit, and each workgroup fits on one.  Its state is
+// a generation word and one flag per workgroup in the caller's workspace; the
+// flag value of a launch is a hash of (generation + 1, workspace address), so
+// stale or uninitialised workspace bytes never match it (the workspace needs
+// no clearing), and the launch advances the generation once every flag is
+// seen.  A wait that exceeds its bound writes NaN to the workgroup's outputs
+// and advances the generation, so a failure is loud and does not poison the
+// next call.
 //
 // Split-K inside a wave: lane l takes the 32-weight chunks l, l+64, ... of a
 // row (16 packed bytes = one 16-byte load; a chunk is half of one 64-block so
@@ -39,8 +54,8 @@ namespace {
 constexpr int kCopies = 32;
 constexpr int kThreads = 512;          // 8 waves per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxItems = 4;           // gate/up items per wave and round
-constexpr int kMaxChunksPerLane = 16;  // down: chunks of the concatenated K
+constexpr int kMaxChunksPerLane = 8;   // down: chunks of the concatenated K (k*I <= 16384)
+constexpr int kDnFirst = 3;            // of which always loaded (k*I <= 6144 in one pass)
 
 __device__ __forceinline__ float dot_chunk(const uint32_t* lut, uint32_t lane_off,
                                            u32x4 q, const _Float16* act) {
@@ -76,24 +91,19 @@ __device__ __forceinline__ void store1(void* out, int64_t idx, float v) {
   }
 }
 
-// The scale of chunk c (32 weights) of a row: the fp32 absmax of its 64-block,
-// or for MXFP4 stacks the e8m0 byte of its own 32-block as 2^(s - 127) in
-// fp32 (exact over the whole e8m0 range; 255 is NaN).
-__device__ __forceinline__ float chunk_scale(const float* absmax, int64_t row, int chunks,
-                                             int c, bool mx) {
-  if (mx) {
-    const uint32_t b = reinterpret_cast<const uint8_t*>(absmax)[row * chunks + c];
-    return b == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)b - 127);
-  }
-  return absmax[row * (chunks / 2) + (c >> 1)];
+// The scale of chunk c (32 weights) of a row, loaded as raw bits and turned
+// into a value only where it is used (so no load waits at issue): the fp32
+// absmax of its 64-block, or for MXFP4 stacks the e8m0 byte of its own
+// 32-block, 2^(s - 127) in fp32 (exact over the whole e8m0 range; 255 is NaN).
+__device__ __forceinline__ uint32_t chunk_scale_bits(const float* absmax, int64_t row,
+                                                     int chunks, int c, bool mx) {
+  if (mx) return reinterpret_cast<const uint8_t*>(absmax)[row * chunks + c];
+  return reinterpret_cast<const uint32_t*>(absmax)[row * (chunks / 2) + (c >> 1)];
 }
 
-__device__ __forceinline__ void fill_table(uint32_t* lut, uint16_t* stage, int qtype, int tid) {
-  if (qtype == kQtMXFP4)
-    lut_fill<kCopies>(lut, stage, c_levels_gemv_mx, tid, kThreads, /*low_first=*/true);
-  else
-    lut_fill<kCopies>(lut, stage, qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv, tid,
-                      kThreads);
+__device__ __forceinline__ float scale_value(uint32_t b, bool mx) {
+  if (mx) return b == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)b - 127);
+  return __uint_as_float(b);
 }
 
 // 16-bit activation -> fp16 (bf16 rounds to nearest even; fp16 passes through)
@@ -103,65 +113,202 @@ __device__ __forceinline__ _Float16 to_f16(uint16_t raw, bool bf16) {
 
 }  // namespace
 
-// kCpl = ceil(H / 2048) <= 4: 32-weight chunks of one row per lane.
-template <int kRegs, int kCpl>
-__global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
+// splitmix64 finaliser: the tag of generation `g` for an exchange buffer at
+// address `a` (a bijection of g for a fixed a); the top 48 bits are used.
+__device__ __forceinline__ uint64_t exchange_tag(uint64_t g, uint64_t a) {
+  uint64_t z = g * 0x9E3779B97F4A7C15ull ^ a;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (z ^ (z >> 31)) & ~0xffffull;
+}
+
+__device__ __forceinline__ uint64_t load_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The routing views of a T = 1 forward (written by one wave; lane j < k
+// holds slot j): ids, weights, the pairs p = j grouped by expert (the k ids are
+// distinct, so a pair's position is the number of smaller ids) and the
+// per-expert offsets (offsets[e] = number of selected ids below e).
+__device__ __forceinline__ void write_routing(const GemvArgs& g, int lane, int id, float w) {
+  const int k = g.k;
+  if (lane < k) {
+    g.topk_ids[lane] = id;
+    g.topk_w[lane] = w;
+  }
+  int below = 0;
+  for (int j = 0; j < k; ++j) below += __builtin_amdgcn_readlane(id, j) < id ? 1 : 0;
+  if (lane < k) g.sorted_pair[below] = lane;
+  for (int e = lane; e <= g.E; e += 64) {
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += __builtin_amdgcn_readlane(id, j) < e ? 1 : 0;
+    g.expert_offsets[e] = c;
+  }
+}
+
+// The expert of slot j (lane-varying, lo <= j <= hi, wave-uniform bounds)
+// from the ids held by lanes 0..k-1: one readlane per slot the wave spans.
+__device__ __forceinline__ int slot_expert(int id, int j, int lo, int hi) {
+  int e = 0;
+  for (int jj = lo; jj <= hi; ++jj) {
+    const int v = __builtin_amdgcn_readlane(id, jj);
+    e = j == jj ? v : e;
+  }
+  return e;
+}
+
+// kCpl = ceil(H / 2048) <= 4: 32-weight chunks of one gate/up row per lane;
+// kItems gate/up items per wave are loaded at once (3 of one chunk per lane
+// -- the Qwen3-30B-A3B decode layer on 256 compute units has exactly 3 --, 2
+// of two, 1 of four).
+template <int kRegs, int kCpl, bool kMx>
+__global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
+  constexpr int kItems = kCpl == 1 ? 3 : 4 / kCpl;
+  constexpr int kHPer = 8;  // exchange words per thread and pass
   __shared__ uint32_t s_lut[256 * kCopies];
   __shared__ uint16_t s_stage[16];
-  extern __shared__ __attribute__((aligned(16))) _Float16 s_x[];  // [H]
+  __shared__ int s_fail;
+  extern __shared__ __attribute__((aligned(16))) _Float16 s_dyn[];  // x [H], then h [k*I]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = g.H, I = g.I, k = g.k;
+  _Float16* s_x = s_dyn;
+  _Float16* s_h = s_dyn + H;
 
-  // activations: issued first, consumed after the weight loads are out
+  // the router logits first: they head the only dependent chain before the
+  // weight loads (the other loads below are consumed much later)
+  float lgv[kRegs];
+  route_load<kRegs>(g.logits, g.E, lane, lgv);
+
+  // activations: consumed while the weight loads are in flight
   constexpr int kXPer = 4;  // x elements per thread and pass
   uint2 xr[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int i0 = (p * kThreads + tid) * kXPer;
-    xr[p] = i0 < H ? *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) + i0)
-                   : make_uint2(0u, 0u);
+    // clamped: every thread loads (the staging below skips i0 >= H)
+    xr[p] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.x) +
+                                            (i0 < H ? i0 : H - kXPer));
   }
+
+  // this launch's tag: the generation is read before this workgroup
+  // publishes anything, and it is advanced only once every value is seen
+  uint64_t* gen_p = g.barrier;
+  uint64_t* hx = g.barrier + kDecodeFlagOffset;
+  const uint64_t gen = load_agent(gen_p);
 
   // route in every wave: lane j < k holds slot j
   int id;
   float w;
-  route_one_token<kRegs>(g.logits, g.E, k, g.renormalize, lane, &id, &w);
-  if (blockIdx.x == 0 && wave == 0 && lane < k) {
-    g.topk_ids[lane] = id;
-    g.topk_w[lane] = w;
-  }
+  route_select<kRegs>(lgv, g.E, k, g.renormalize, lane, &id, &w);
 
-  // this wave's items, every load issued before any arithmetic
   const int chunks = H / 32;
   const int64_t row_bytes = H / 2;
-  const bool mx = g.qtype == kQtMXFP4;
+  constexpr bool mx = kMx;
   const int nw = gridDim.x * kWaves;
-  const int items = k * I;
   const int q0 = blockIdx.x * kWaves + wave;
-  u32x4 qg[kMaxItems][kCpl], qu[kMaxItems][kCpl];
-  float sg[kMaxItems][kCpl], su[kMaxItems][kCpl];
+
+  // ---- down rows of this wave: n = q0 + r * nw; this lane's chunks of the
+  // concatenated K are cc = lane + 64 m, the same for every row.  The first
+  // kDnFirst chunks are loaded for every lane (a lane past the end re-reads
+  // the last chunk and contributes zero), the rest only where they exist.
+  // Unconditional loads let the compiler count the loads in flight exactly,
+  // so no later use waits for more of them than it needs.
+  const int cps = I / 32;  // chunks per slot
+  const int total = k * cps;
+  // j = cc / cps through an fp32 reciprocal: with k*I <= 16384 there are at
+  // most 512 chunks, so cps <= 512 and (cc + 1/2) / cps lies at least 2^-10
+  // from an integer, while the rounded product is within 2^-15 of it: the
+  // truncation is exact
+  const float inv_cps = 1.0f / (float)cps;
+  const uint32_t dn_stride = (uint32_t)H * (uint32_t)(I / 2);                 // bytes / expert
+  const uint32_t am_stride = (uint32_t)H * (uint32_t)(mx ? I / 32 : I / 64);  // scales / expert
+  uint64_t pk_off[kMaxChunksPerLane];
+  uint64_t am_off[kMaxChunksPerLane];  // absmax element, or scale byte for MXFP4
+  int h_off[kMaxChunksPerLane];
+  bool dvalid[kMaxChunksPerLane];
 #pragma unroll
-  for (int it = 0; it < kMaxItems; ++it) {
-    const int q = q0 + it * nw;
-    const int qq = q < items ? q : (q0 < items ? q0 : 0);  // clamp: re-read a valid item
-    const int j = qq / I;
-    const int i = qq - j * I;
-    const int e = __builtin_amdgcn_readlane(id, j);  // j is wave-uniform
+  for (int m = 0; m < kMaxChunksPerLane; ++m) {
+    const int cc0 = lane + 64 * m;
+    dvalid[m] = cc0 < total;
+    pk_off[m] = 0;
+    am_off[m] = 0;
+    h_off[m] = 0;
+    if (m < kDnFirst || 64 * m < total) {  // compile-time or wave-uniform
+      const int cc = dvalid[m] ? cc0 : total - 1;
+      const int j = (int)(((float)cc + 0.5f) * inv_cps);
+      const int lo = (int)(((float)(64 * m < total ? 64 * m : total - 1) + 0.5f) * inv_cps);
+      const int hi = (int)(((float)(64 * m + 63 < total ? 64 * m + 63 : total - 1) + 0.5f) * inv_cps);
+      const uint32_t e = (uint32_t)slot_expert(id, j, lo, hi);
+      const uint32_t c = (uint32_t)(cc - j * cps);
+      pk_off[m] = (uint64_t)e * dn_stride + c * 16u;
+      am_off[m] = (uint64_t)e * am_stride + (mx ? c : c >> 1);
+      h_off[m] = j * I + (int)c * 32;
+    }
+  }
+  // ---- gate/up items of this wave: q = q0 + it * nw, it < n_items.  The
+  // first kItems slots are loaded unconditionally (a slot past n_items
+  // re-reads a valid item and publishes nothing).
+  const int items = k * I;
+  const int n_items = q0 < items ? (items - 1 - q0) / nw + 1 : 0;
+  u32x4 qg[kItems][kCpl], qu[kItems][kCpl];
+  uint32_t sg[kItems][kCpl], su[kItems][kCpl];
+  auto load_item = [&](int t, int q) {
+    const int j = q / I;  // wave-uniform: scalar arithmetic
+    const int i = q - j * I;
+    const int e = __builtin_amdgcn_readlane(id, j);
     const int64_t rg = (int64_t)e * 2 * I + i;
     const int64_t ru = rg + I;
 #pragma unroll
     for (int m = 0; m < kCpl; ++m) {
       int c = lane + 64 * m;
       if (c >= chunks) c = chunks - 1;
-      qg[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + rg * row_bytes + c * 16);
-      qu[it][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + ru * row_bytes + c * 16);
-      sg[it][m] = chunk_scale(g.gu_absmax, rg, chunks, c, mx);
-      su[it][m] = chunk_scale(g.gu_absmax, ru, chunks, c, mx);
+      qg[t][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + rg * row_bytes + c * 16);
+      qu[t][m] = *reinterpret_cast<const u32x4*>(g.gu_packed + ru * row_bytes + c * 16);
+      sg[t][m] = chunk_scale_bits(g.gu_absmax, rg, chunks, c, mx);
+      su[t][m] = chunk_scale_bits(g.gu_absmax, ru, chunks, c, mx);
     }
+  };
+  auto item_q = [&](int it) {  // a valid item for every slot
+    const int last = n_items > 0 ? n_items - 1 : 0;
+    const int q = q0 + (it < last ? it : last) * nw;
+    return q < items ? q : 0;
+  };
+
+  u32x4 qd[kMaxChunksPerLane];
+  uint32_t sd[kMaxChunksPerLane];
+  auto load_chunk = [&](int m, int row) {
+    const int64_t prow = (int64_t)row * (I / 2);
+    const int64_t arow = (int64_t)row * (mx ? I / 32 : I / 64);
+    qd[m] = *reinterpret_cast<const u32x4*>(g.dn_packed + pk_off[m] + prow);
+    sd[m] = mx ? reinterpret_cast<const uint8_t*>(g.dn_absmax)[am_off[m] + arow]
+               : reinterpret_cast<const uint32_t*>(g.dn_absmax)[am_off[m] + arow];
+  };
+  auto load_row = [&](int row) {
+#pragma unroll
+    for (int m = 0; m < kMaxChunksPerLane; ++m)
+      if (m < kDnFirst || 64 * m < total) load_chunk(m, row);
+  };
+
+  // every load of the first round goes out back to back (the address
+  // arithmetic above is done, so no wait for an earlier load intervenes)
+#pragma unroll
+  for (int t = 0; t < kItems; ++t) load_item(t, item_q(t));
+  int n = q0;
+  {
+    const int row = n < H ? n : H - 1;
+#pragma unroll
+    for (int m = 0; m < kDnFirst; ++m) load_chunk(m, row);
+#pragma unroll
+    for (int m = kDnFirst; m < kMaxChunksPerLane; ++m)
+      if (64 * m < total) load_chunk(m, row);
   }
+  if (blockIdx.x == 0 && wave == 0) write_routing(g, lane, id, w);
 
   // stage x as fp16 and build the table while the weights are in flight
 #pragma unroll
@@ -174,148 +321,152 @@ __global__ __launch_bounds__(kThreads) void gemv_gate_up_kernel(GemvArgs g) {
       s_x[i0 + 3] = to_f16(xr[p].y >> 16, g.x_bf16);
     }
   }
-  fill_table(s_lut, s_stage, g.qtype, tid);  // ends with a barrier
+  if (tid == 0) {
+    s_fail = 0;
+    // the 16 levels (uniform addresses: scalar loads), rounded to fp16
+    const float* levels = g.qtype == kQtMXFP4 ? c_levels_gemv_mx
+                          : g.qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_stage[i] = __builtin_bit_cast(uint16_t, (_Float16)levels[i]);
+  }
+  __syncthreads();
+  {
+    const bool low_first = g.qtype == kQtMXFP4;
+    for (int i = tid; i < 256 * kCopies; i += kThreads) {
+      const int b = i / kCopies;
+      const int first = low_first ? (b & 15) : (b >> 4);
+      const int second = low_first ? (b >> 4) : (b & 15);
+      s_lut[i] = (uint32_t)s_stage[first] | ((uint32_t)s_stage[second] << 16);
+    }
+  }
+  __syncthreads();
 
+  // ---- gate/up dots -> h (w_j * silu(gate) * up, rounded once to fp16),
+  // published as one 64-bit word: this launch's tag | the fp16 bits
+  const uint64_t tag = exchange_tag(gen + 1, (uint64_t)(uintptr_t)g.barrier);
   const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
-  _Float16* hout = reinterpret_cast<_Float16*>(g.hbuf);
+  auto item_dots = [&](int it0) {
 #pragma unroll
-  for (int it = 0; it < kMaxItems; ++it) {
-    const int q = q0 + it * nw;
-    float accg = 0.f, accu = 0.f;
+    for (int t = 0; t < kItems; ++t) {
+      if (it0 + t < n_items) {  // wave-uniform
+        const int q = q0 + (it0 + t) * nw;
+        float accg = 0.f, accu = 0.f;
 #pragma unroll
-    for (int m = 0; m < kCpl; ++m) {
-      const int c = lane + 64 * m;
-      if (c < chunks) {
-        const _Float16* xs = s_x + c * 32;
-        accg = fmaf(dot_chunk(s_lut, lane_off, qg[it][m], xs), sg[it][m], accg);
-        accu = fmaf(dot_chunk(s_lut, lane_off, qu[it][m], xs), su[it][m], accu);
-      }
-    }
-    accg = wave_sum(accg);
-    accu = wave_sum(accu);
-    const int j = q < items ? q / I : 0;
-    const float wj = lane_f(w, j);
-    if (lane == 0 && q < items) hout[q] = (_Float16)(silu_g(accg) * accu * wj);
-  }
-}
-
-template <int kOut>
-__global__ __launch_bounds__(kThreads) void gemv_down_kernel(GemvArgs g) {
-  __shared__ uint32_t s_lut[256 * kCopies];
-  __shared__ uint16_t s_stage[16];
-  extern __shared__ __attribute__((aligned(16))) _Float16 s_h[];  // [k, I]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = g.H, I = g.I, k = g.k;
-
-  // the routed experts (lane j < k holds slot j's id)
-  const int id = lane < k ? g.topk_ids[lane] : 0;
-
-  // this lane's chunks of the concatenated K (the same for every output row)
-  const int cps = I / 32;  // chunks per slot
-  const int total = k * cps;
-  const bool mx = g.qtype == kQtMXFP4;
-  int64_t pk_off[kMaxChunksPerLane];
-  int64_t am_off[kMaxChunksPerLane];  // absmax element, or scale byte for MXFP4
-  int h_off[kMaxChunksPerLane];
-  int nc = 0;
-#pragma unroll
-  for (int m = 0; m < kMaxChunksPerLane; ++m) {
-    const int cc = lane + 64 * m;
-    const int j = cc < total ? cc / cps : 0;
-    const int e = __shfl(id, j, 64);
-    pk_off[m] = 0;
-    am_off[m] = 0;
-    h_off[m] = 0;
-    if (cc < total) {
-      const int c = cc - j * cps;
-      pk_off[m] = (int64_t)e * H * (I / 2) + c * 16;
-      am_off[m] = mx ? (int64_t)e * H * (I / 32) + c : (int64_t)e * H * (I / 64) + (c >> 1);
-      h_off[m] = j * I + c * 32;
-      nc = m + 1;
-    }
-  }
-  // one output row per wave and round; the first row's loads go out before
-  // h is staged and the table is built
-  const int nw = gridDim.x * kWaves;
-  int n = blockIdx.x * kWaves + wave;
-  u32x4 q[kMaxChunksPerLane];
-  float s[kMaxChunksPerLane];
-  auto load_row = [&](int row) {
-    const int64_t prow = (int64_t)row * (I / 2);
-    const int64_t arow = (int64_t)row * (mx ? I / 32 : I / 64);
-#pragma unroll
-    for (int m = 0; m < kMaxChunksPerLane; ++m) {
-      if (m < nc) {
-        q[m] = *reinterpret_cast<const u32x4*>(g.dn_packed + pk_off[m] + prow);
-        if (mx) {
-          const uint32_t b = reinterpret_cast<const uint8_t*>(g.dn_absmax)[am_off[m] + arow];
-          s[m] = b == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)b - 127);
-        } else {
-          s[m] = g.dn_absmax[am_off[m] + arow];
+        for (int m = 0; m < kCpl; ++m) {
+          const int c = lane + 64 * m;
+          if (c < chunks) {
+            const _Float16* xs = s_x + c * 32;
+            accg = fmaf(dot_chunk(s_lut, lane_off, qg[t][m], xs), scale_value(sg[t][m], mx), accg);
+            accu = fmaf(dot_chunk(s_lut, lane_off, qu[t][m], xs), scale_value(su[t][m], mx), accu);
+          }
         }
+        accg = wave_sum(accg);
+        accu = wave_sum(accu);
+        const float wj = lane_f(w, q / I);
+        const _Float16 hv = (_Float16)(silu_g(accg) * accu * wj);
+        if (lane == 0) store_agent(hx + q, tag | __builtin_bit_cast(uint16_t, hv));
       }
     }
   };
-  if (n < H) load_row(n);
+  // the first round's loads went out before the table was built; later
+  // rounds (more items than waves * kItems) load and compute in turn
+  item_dots(0);
+  for (int it0 = kItems; it0 < n_items; it0 += kItems) {
+#pragma unroll
+    for (int t = 0; t < kItems; ++t) load_item(t, item_q(it0 + t));
+    item_dots(it0);
+  }
 
-  // h (fp16, k*I values, a multiple of 8) -> LDS
-  const _Float16* hin = reinterpret_cast<const _Float16*>(g.hbuf);
-  for (int i = tid * 8; i < k * I; i += kThreads * 8)
-    *reinterpret_cast<u32x4*>(s_h + i) = *reinterpret_cast<const u32x4*>(hin + i);
-  fill_table(s_lut, s_stage, g.qtype, tid);  // ends with a barrier
+  // ---- grid-wide exchange of h: every workgroup reads all k*I words until
+  // each carries this launch's tag (a bounded wait), keeping the fp16 value
+  bool ok = true;
+  for (int i0 = tid; i0 < items; i0 += kThreads * kHPer) {
+    uint64_t v[kHPer];
+    uint32_t pending = 0;
+#pragma unroll
+    for (int t = 0; t < kHPer; ++t)
+      if (i0 + t * kThreads < items) pending |= 1u << t;
+    for (uint32_t spin = 0; pending != 0 && spin < g.spin_limit; ++spin) {
+      if (spin > 0) __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int t = 0; t < kHPer; ++t)
+        if (pending & (1u << t)) v[t] = load_agent(hx + i0 + t * kThreads);
+#pragma unroll
+      for (int t = 0; t < kHPer; ++t) {
+        if ((pending & (1u << t)) && (v[t] & ~0xffffull) == tag) {
+          s_h[i0 + t * kThreads] = __builtin_bit_cast(_Float16, (uint16_t)(v[t] & 0xffffu));
+          pending &= ~(1u << t);
+        }
+      }
+    }
+    ok = ok && pending == 0;
+  }
+  if (!ok) s_fail = 1;
+  __syncthreads();
+  const bool failed = s_fail != 0;
+  // every workgroup published before it could finish its wait, so all of
+  // them have read the generation: advance it (also after a failed wait, so
+  // the next launch does not reuse this tag)
+  if (tid == 0 && (blockIdx.x == 0 || failed)) store_agent(gen_p, gen + 1);
 
-  const uint32_t lane_off = lut_lane_offset<kCopies>(lane);
+  // ---- down rows
   for (; n < H; n += nw) {
     float acc = 0.f;
 #pragma unroll
     for (int m = 0; m < kMaxChunksPerLane; ++m) {
-      if (m < nc) acc = fmaf(dot_chunk(s_lut, lane_off, q[m], s_h + h_off[m]), s[m], acc);
+      if (m < kDnFirst || 64 * m < total) {  // compile-time or wave-uniform
+        const float p =
+            dot_chunk(s_lut, lane_off, qd[m], s_h + h_off[m]) * scale_value(sd[m], mx);
+        acc += dvalid[m] ? p : 0.f;
+      }
     }
     if (n + nw < H) load_row(n + nw);
     acc = wave_sum(acc);
-    if (lane == 0) store1<kOut>(g.y, n, acc);
+    if (failed) acc = __builtin_nanf("");
+    if (lane == 0) {
+      if (g.y_dtype == kF32) store1<kF32>(g.y, n, acc);
+      else if (g.y_dtype == kBF16) store1<kBF16>(g.y, n, acc);
+      else store1<kF16>(g.y, n, acc);
+    }
   }
 }
 
-template <int kRegs>
-static void launch_gate_up(const GemvArgs& g, int grid, size_t xs, hipStream_t stream) {
+template <int kRegs, bool kMx>
+static void launch_layer(const GemvArgs& g, int grid, size_t lds, hipStream_t stream) {
   const int cpl = (g.H + 2047) / 2048;
   if (cpl <= 1)
-    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 1>), dim3(grid), dim3(kThreads), xs, stream, g);
+    hipLaunchKernelGGL((decode_layer_kernel<kRegs, 1, kMx>), dim3(grid), dim3(kThreads), lds,
+                       stream, g);
   else if (cpl <= 2)
-    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 2>), dim3(grid), dim3(kThreads), xs, stream, g);
+    hipLaunchKernelGGL((decode_layer_kernel<kRegs, 2, kMx>), dim3(grid), dim3(kThreads), lds,
+                       stream, g);
   else
-    hipLaunchKernelGGL((gemv_gate_up_kernel<kRegs, 4>), dim3(grid), dim3(kThreads), xs, stream, g);
+    hipLaunchKernelGGL((decode_layer_kernel<kRegs, 4, kMx>), dim3(grid), dim3(kThreads), lds,
+                       stream, g);
+}
+
+template <bool kMx>
+static void launch_regs(const GemvArgs& g, int grid, size_t lds, hipStream_t stream) {
+  const int regs = (g.E + 63) / 64;
+  if (regs <= 1) launch_layer<1, kMx>(g, grid, lds, stream);
+  else if (regs <= 2) launch_layer<2, kMx>(g, grid, lds, stream);
+  else if (regs <= 4) launch_layer<4, kMx>(g, grid, lds, stream);
+  else if (regs <= 8) launch_layer<8, kMx>(g, grid, lds, stream);
+  else launch_layer<16, kMx>(g, grid, lds, stream);
 }
 
 hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream) {
-  const int regs = (g.E + 63) / 64;
-  const size_t xs = (size_t)g.H * sizeof(_Float16);
-  // gate/up: enough waves that every item is loaded in one round
+  // one workgroup per compute unit at most: the h exchange needs the whole
+  // grid resident.  Every workgroup owns at least one h value (item q0 =
+  // 8 * block), so each one has read the generation before the exchange can
+  // complete anywhere.
   const int items = g.k * g.I;
-  int grid_gu = (items + kWaves * kMaxItems - 1) / (kWaves * kMaxItems);
-  if (grid_gu < num_cus) grid_gu = (items + kWaves - 1) / kWaves < num_cus
-                                       ? (items + kWaves - 1) / kWaves : num_cus;
-  if (grid_gu < 1) grid_gu = 1;
-  if (regs <= 1) launch_gate_up<1>(g, grid_gu, xs, stream);
-  else if (regs <= 2) launch_gate_up<2>(g, grid_gu, xs, stream);
-  else if (regs <= 4) launch_gate_up<4>(g, grid_gu, xs, stream);
-  else if (regs <= 8) launch_gate_up<8>(g, grid_gu, xs, stream);
-  else launch_gate_up<16>(g, grid_gu, xs, stream);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  int grid_dn = (g.H + kWaves - 1) / kWaves;
-  if (grid_dn > num_cus * 2) grid_dn = num_cus * 2;
-  const size_t hs = (size_t)g.k * g.I * sizeof(_Float16);
-  if (g.y_dtype == kF32)
-    hipLaunchKernelGGL(gemv_down_kernel<kF32>, dim3(grid_dn), dim3(kThreads), hs, stream, g);
-  else if (g.y_dtype == kBF16)
-    hipLaunchKernelGGL(gemv_down_kernel<kBF16>, dim3(grid_dn), dim3(kThreads), hs, stream, g);
-  else
-    hipLaunchKernelGGL(gemv_down_kernel<kF16>, dim3(grid_dn), dim3(kThreads), hs, stream, g);
+  int grid = num_cus;
+  if (grid > (items + kWaves - 1) / kWaves) grid = (items + kWaves - 1) / kWaves;
+  if (grid < 1) grid = 1;
+  const size_t lds = ((size_t)g.H + (size_t)g.k * g.I) * sizeof(_Float16);
+  if (g.qtype == kQtMXFP4) launch_regs<true>(g, grid, lds, stream);
+  else launch_regs<false>(g, grid, lds, stream);
   return hipGetLastError();
 }
 

@@ -99,13 +99,22 @@ struct GemvArgs {
   const float* gu_absmax;
   const uint8_t* dn_packed;
   const float* dn_absmax;
-  int32_t* topk_ids;  // [k]
-  float* topk_w;      // [k]
-  void* hbuf;         // [k, I] fp16 h, already scaled by the routing weight
-  void* y;            // [H]
+  int32_t* topk_ids;        // [k]
+  float* topk_w;            // [k]
+  int32_t* sorted_pair;     // [k] the pairs grouped by expert
+  int32_t* expert_offsets;  // [E+1]
+  uint64_t* barrier;        // kDecodeBarrierBytes(k*I): generation word, then the h exchange
+  uint32_t spin_limit;      // polls before the h exchange gives up (outputs NaN)
+  void* y;                  // [H]
   int y_dtype;
-  int qtype;          // storage mode of both stacks (kQtNF4 / kQtFP4)
+  int qtype;                // storage mode of both stacks (kQtNF4 / kQtFP4 / kQtMXFP4)
 };
+
+// The decode kernel's grid-wide exchange of h: a generation word, then one
+// 64-bit word per h value (a 48-bit tag of the launch | the fp16 bits).
+constexpr int kDecodeFlagOffset = 32;  // words: the generation owns the first 256 bytes
+constexpr size_t decode_exchange_bytes(int64_t kI) { return (kDecodeFlagOffset + kI) * 8; }
+constexpr uint32_t kDecodeSpinLimit = 1u << 20;
 
 hipError_t launch_decode(const GemvArgs& g, int num_cus, hipStream_t stream);
 

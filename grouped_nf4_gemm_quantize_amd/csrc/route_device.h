@@ -14,8 +14,10 @@ __device__ __forceinline__ void route_load(const float* __restrict__ lg_row, int
 #pragma unroll
   for (int r = 0; r < kRegs; ++r) {
     const int e = lane + 64 * r;
-    v[r] = (e < E) ? lg_row[e] : -__builtin_inff();
+    v[r] = lg_row[e < E ? e : E - 1];  // clamped: no branch around the load
   }
+#pragma unroll
+  for (int r = 0; r < kRegs; ++r) v[r] = (lane + 64 * r < E) ? v[r] : -__builtin_inff();
 }
 
 // Order-preserving 32-bit key of a logit: larger key = larger logit.  -0.0
@@ -44,9 +46,12 @@ template <int kRegs>
 __device__ __forceinline__ void route_select(const float v[kRegs], int E, int k,
                                              int renormalize, int lane, int* out_id,
                                              float* out_w) {
+  // keys computed for every lane, then masked (branch-free: the first use of
+  // the loaded logits is then a wait in uniform control flow)
   uint32_t hk[kRegs];
 #pragma unroll
-  for (int r = 0; r < kRegs; ++r) hk[r] = (lane + 64 * r < E) ? logit_key(v[r]) : 0u;
+  for (int r = 0; r < kRegs; ++r)
+    hk[r] = logit_key(v[r]) & (lane + 64 * r < E ? 0xffffffffu : 0u);
 
   // 1. the k-th largest key (padding keys are 0, below every real key)
   uint32_t t = 0;

@@ -201,9 +201,15 @@ int grouped_nf4_gemm(const void* a, int a_dtype, int64_t a_rows,
  * SwiGLU, down (+LoRA), combine over the slots in ascending slot order
  * (experts summed per token in group-sorted pair order, 0.22.0 README
  * "Which training path?").  T == 1 without adapters (and H <= 8192,
- * k*I <= 16384) runs the split-K decode GEMV kernels (the single-token fast
+ * k*I <= 16384) runs one fused split-K decode kernel (the single-token fast
  * path, 0.22.0 README "Inference"); otherwise the grouped MFMA kernels.  Same
- * contract either way.
+ * contract either way.  The decode kernel exchanges h between its
+ * workgroups inside one launch: it needs its grid (at most one workgroup per
+ * compute unit) resident at once, and keeps a generation word and the
+ * exchanged values in the workspace, tagged per launch, so the workspace
+ * needs no clearing between calls; two calls must not share a workspace
+ * while both run (as for every path).  Should that exchange ever wait past
+ * its bound, y is written as NaN (a loud failure, never a stale value).
  *   x [T, H]        BF16 or F16 activations;
  *   router_logits   fp32 [T, E];
  *   H, I            multiples of 64; E <= NF4MOE_MAX_EXPERTS; k <= min(E, 32);
@@ -388,8 +394,8 @@ int moe_expert_backward_nbit(int quant_type, const void* x, int x_dtype,
  * 2^(s-127) is within fp16's range, 2^-24 .. 2^15; s = 255 decodes as NaN);
  * fp32 accumulation.  K must be a multiple of 128 (ESHAPE).  No adapters.
  * Other arguments, layouts and errors as for grouped_nf4_gemm and
- * moe_expert_forward; the T == 1 case runs the split-K decode GEMVs, which
- * apply each 32-block's scale in fp32 (the weights have no fp16 range limit
+ * moe_expert_forward; the T == 1 case runs the fused split-K decode kernel,
+ * which applies each 32-block's scale in fp32 (the weights have no fp16 range limit
  * there; h between the projections is fp16). */
 int grouped_mxfp4_gemm(const void* a, int a_dtype, int64_t a_rows,
                        const int32_t* gather, int gather_div,
@@ -407,8 +413,9 @@ int moe_expert_forward_mxfp4(const void* x, int x_dtype, const float* router_log
 
 /* Device-pointer views into a moe_expert_forward workspace (for inspection of
  * the routing a forward used; valid after the forward completes on its
- * stream).  Any out-pointer may be NULL.  Returns a negative status on bad
- * sizes. */
+ * stream, the T == 1 decode path included: it writes ids, weights, the k
+ * pairs grouped by expert and the offsets as well).  Any out-pointer may be
+ * NULL.  Returns a negative status on bad sizes. */
 int moe_expert_forward_routing(void* workspace, int64_t T, int H, int I,
                                int E, int k, int32_t** topk_ids,
                                float** topk_w, int32_t** sorted_pair,

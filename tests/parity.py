@@ -13,6 +13,10 @@ Qwen3-30B-A3B Zipf layer, so the clause taken literally could not be met by
 any bf16 result there.  Every report also gives the literal max-abs figure
 and that rounding floor, max|bf16(y_ref) - y_ref| / RMS.
 
+For fp32 outputs, where the output's own rounding is negligible, the clause
+is also judged as written (``assert_parity_literal``): max|y - y_ref| itself
+must stay within 2e-2 * RMS(y_ref), so the kernel's error is seen on its own.
+
 Integer decisions (codes, ids, permutation) are compared bit for bit.
 """
 
@@ -65,4 +69,14 @@ def assert_parity(y_gpu, y_ref, fro_tol: float = FRO_TOL, maxabs_tol: float = MA
         f"{what}: rel-Frobenius {m['fro']:.3e} (tol {fro_tol:g}), max-abs/RMS beyond "
         f"{out_dtype} rounding {m['maxabs_beyond_rounding']:.3e} (tol {maxabs_tol:g}); "
         f"literal max-abs/RMS {m['maxabs']:.3e}, bf16 floor {m['floor']:.3e}")
+    return m
+
+
+def assert_parity_literal(y_gpu, y_ref, what: str = "") -> dict:
+    """Both clauses as written, with no allowance for output rounding: for
+    fp32 outputs of the layer."""
+    m = metrics(y_gpu, y_ref, "f32")
+    assert m["fro"] <= FRO_TOL and m["maxabs"] <= MAXABS_TOL, (
+        f"{what}: rel-Frobenius {m['fro']:.3e} (tol {FRO_TOL:g}), literal max-abs/RMS "
+        f"{m['maxabs']:.3e} (tol {MAXABS_TOL:g})")
     return m

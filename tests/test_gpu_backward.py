@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from grouped_nf4_gemm_quantize_amd import synth
-from parity import assert_parity, metrics
+from fullsize import full_stacks
+from parity import assert_parity, assert_parity_literal, metrics
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -315,43 +316,31 @@ def test_backward_with_zero_b_has_zero_a_gradient(gpu_lib):
     assert torch.equal(dx, dx0)
 
 
-def _expert_grads_ref(cfg, x, lg, dy, gp, ga, dp, da, lgu, ldn, e):
-    """One expert's adapter gradients from its own pairs (oracle)."""
-    ids, w = oracle.route_topk(lg, cfg.k, cfg.renormalize)
-    t_idx, j_idx = np.nonzero(ids == e)
-    order = np.argsort(t_idx * cfg.k + j_idx, kind="stable")
-    t_idx, j_idx = t_idx[order], j_idx[order]
-    dO = w[t_idx, j_idx][:, None].astype(np.float64) * dy[t_idx].astype(np.float64)
-    res = oracle.expert_backward(x[t_idx], oracle.dequantize_blockwise(gp[e:e + 1], ga[e:e + 1])[0],
-                                 oracle.dequantize_blockwise(dp[e:e + 1], da[e:e + 1])[0], dO,
-                                 lgu, ldn, e)
-    return res
-
-
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["olmoe", "qlora"])
-def test_backward_full_size_sampled(gpu_lib, name):
-    """The full-size layer on the GPU; dx of sampled tokens and one expert's
-    adapter gradients recomputed by the oracle."""
+def test_backward_full_size(gpu_lib, name):
+    """The full-size layer backward on the GPU against the oracle's on every
+    token: dx of all T tokens (bf16, and fp32 under the clause as written)
+    and, with adapters, every expert's adapter gradients.  The stacks are the
+    full-size ones whose every expert was checked bit for bit."""
     cfg = synth.config(name)
-    gp, ga, dp, da = _stacks(cfg)
+    (gp, ga, dp, da), (gpr, gar, dpr, dar) = full_stacks(gpu_lib, cfg)
     x = synth.activations(cfg)
     lg = synth.router_logits(cfg)
     dy = synth.output_grad(cfg)
     glo, dlo, glo_r, dlo_r = _lora(cfg)
-    dx, grads = gpu_lib.moe_backward(gpu(x, torch.bfloat16), gpu(lg), gpu(dy, torch.bfloat16),
-                                     cfg.k, gpu(gp), gpu(ga), gpu(dp), gpu(da), glo, dlo,
-                                     cfg.renormalize)
-    toks = np.random.default_rng(5).choice(cfg.T, size=6, replace=False)
-    ref = oracle.moe_backward_tokens(toks, x, lg, dy, cfg.k, gp, ga, dp, da, glo_r, dlo_r,
-                                     cfg.renormalize)
-    assert_parity(host(dx)[toks], ref, what=f"{name} sampled dx")
+    args = (gpu(x, torch.bfloat16), gpu(lg), gpu(dy, torch.bfloat16), cfg.k, gp, ga, dp, da,
+            glo, dlo, cfg.renormalize)
+    dx, grads = gpu_lib.moe_backward(*args)
+    dx, grads = host(dx), {n: host(v) for n, v in grads.items()}
+    dxf, _ = gpu_lib.moe_backward(*args, dx_dtype=torch.float32)
+    ref = oracle.moe_backward(x, lg, dy, cfg.k, gpr, gar, dpr, dar, glo_r, dlo_r,
+                              cfg.renormalize)
+    m = assert_parity(dx, ref["dx"], what=f"{name} dx")
+    mf = assert_parity_literal(host(dxf), ref["dx"], what=f"{name} dx f32")
+    print(name, "dx bf16", m, "f32", mf)
     if glo is not None:
-        e = cfg.E // 3
-        res = _expert_grads_ref(cfg, x, lg, dy, gp, ga, dp, da, glo_r, dlo_r, e)
-        for nm in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
-            assert_parity(host(grads[nm][e]), res[nm], fro_tol=5e-3, maxabs_tol=2e-2,
-                          what=f"{name} expert {e} {nm}", out_dtype="f32")
+        _check_lora_grads(grads, ref, f"{name} full size")
 
 
 @pytest.mark.parametrize("T,E,k,skew", [(40, 300, 4, False), (96, 8, 2, True), (1, 16, 4, False)])

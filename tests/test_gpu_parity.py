@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from grouped_nf4_gemm_quantize_amd import synth
-from parity import assert_parity, metrics
+from fullsize import full_stacks
+from parity import assert_parity, assert_parity_literal, metrics
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -86,16 +87,24 @@ def test_quantize_nonfinite_flag(gpu_lib):
     assert int(flag.item()) == 1
 
 
-@pytest.mark.parametrize("name", ["tiny", "olmoe", "qwen3_zipf"])
-def test_quantize_config_stacks(gpu_lib, name):
-    cfg = synth.config(name)
-    experts = range(cfg.E) if name == "tiny" else [0, cfg.E // 2 + 1, cfg.E - 1]
+def test_quantize_config_stacks(gpu_lib):
+    cfg = synth.config("tiny")
     for which in ("gu", "dn"):
-        w = np.stack([synth.expert_weights(cfg, which, e) for e in experts])
+        w = synth.stack_weights(cfg, which)
         p_ref, a_ref = oracle.quantize_blockwise(w)
         p, a = gpu_lib.quantize(gpu(w))
-        assert np.array_equal(host(p), p_ref), (name, which)
-        assert np.array_equal(host(a), a_ref), (name, which)
+        assert np.array_equal(host(p), p_ref), which
+        assert np.array_equal(host(a), a_ref), which
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["olmoe", "qwen3_zipf"])
+def test_quantize_full_stacks_every_expert(gpu_lib, name):
+    """Both full-size stacks, every expert: codes and absmax of gate_up and
+    down bit for bit against the oracle (the comparison is in full_stacks)."""
+    cfg = synth.config(name)
+    (gp, ga, dp, da), (gpr, gar, dpr, dar) = full_stacks(gpu_lib, cfg)
+    assert gp.shape == gpr.shape and da.shape == dar.shape
 
 
 # ------------------------------------------------------------------- routing
@@ -433,19 +442,68 @@ def test_forward_real_widths(gpu_lib, name, T, E):
     print(name, m)
 
 
-def test_decode_gemv_variants(gpu_lib):
-    cfg = synth.config("decode", E=32)
+@pytest.mark.parametrize("name,T,E", [("olmoe", 320, 16), ("qwen3_zipf", 600, 24),
+                                      ("qlora", 256, 16), ("decode", 1, 32)])
+def test_forward_real_widths_f32_literal(gpu_lib, name, T, E):
+    """fp32 layer outputs judged by the clause as written (no allowance for
+    output rounding), so the kernels' own error is what is measured."""
+    cfg = synth.config(name, T=T, E=E)
+    y, ref = _forward_case(gpu_lib, cfg, y_dtype=torch.float32)
+    m = assert_parity_literal(y, ref, what=f"{name} f32")
+    print(name, "f32", m)
+
+
+def _decode_routing(gpu_lib, cfg, x, lg, stacks, renorm=True, y_dtype=torch.bfloat16):
+    """One decode forward through an explicit workspace; returns y and the
+    routing views the forward leaves in it."""
+    nbytes = gpu_lib.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)  # stale bytes: the views must be written by this forward
+    y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, *stacks,
+                            renormalize=renorm, y_dtype=y_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    ptrs = gpu_lib.forward_routing(ws, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    base = ws.data_ptr()
+    P = cfg.T * cfg.k
+
+    def view(ptr, n, dt):
+        off = ptr - base
+        return host(ws[off: off + n * 4].view(dt))
+
+    views = dict(ids=view(ptrs["ids"], P, torch.int32).reshape(cfg.T, cfg.k),
+                 w=view(ptrs["w"], P, torch.float32).reshape(cfg.T, cfg.k),
+                 sorted_pair=view(ptrs["sorted_pair"], P, torch.int32),
+                 offsets=view(ptrs["offsets"], cfg.E + 1, torch.int32))
+    return y, views
+
+
+@pytest.mark.parametrize("E,H", [(32, 2048), (128, 2048), (300, 2048), (32, 3072)])
+def test_decode_gemv_variants(gpu_lib, E, H):
+    """T = 1: routing views bit-exact against the oracle (ids, permutation,
+    offsets), weights within 1e-6, and y for both renormalisations and all
+    output types.  E = 300 takes five logit registers per lane; H = 3072 a
+    partial second chunk of each row per lane."""
+    cfg = synth.config("decode", E=E, H=H)
     gp, ga, dp, da = _stacks(cfg)
+    stacks = (gpu(gp), gpu(ga), gpu(dp), gpu(da))
     x = synth.activations(cfg)
     lg = synth.router_logits(cfg)
     for renorm in (True, False):
+        ids_ref, w_ref = oracle.route_topk(lg, cfg.k, renorm)
+        sp_ref, _, off_ref = oracle.permute_pairs(ids_ref, cfg.E)
+        ref, _ = oracle.moe_forward(x, lg, cfg.k, gp, ga, dp, da, renormalize=renorm)
         for y_dt in (torch.float32, torch.bfloat16, torch.float16):
-            y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gp), gpu(ga),
-                                    gpu(dp), gpu(da), renormalize=renorm, y_dtype=y_dt)
-            ref, _ = oracle.moe_forward(x, lg, cfg.k, gp, ga, dp, da, renormalize=renorm)
+            y, v = _decode_routing(gpu_lib, cfg, x, lg, stacks, renorm, y_dt)
+            assert np.array_equal(v["ids"], ids_ref)
+            assert np.array_equal(v["sorted_pair"], sp_ref)
+            assert np.array_equal(v["offsets"], off_ref)
+            assert np.max(np.abs(v["w"] - w_ref) / w_ref) < 1e-6
             name = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[y_dt]
-            tol = (2e-3, 2e-2) if y_dt == torch.float32 else (5e-3, 2e-2)
-            assert_parity(host(y), ref, *tol, what=f"decode {renorm} {name}", out_dtype=name)
+            what = f"decode E={E} H={H} renorm={renorm} {name}"
+            if y_dt == torch.float32:
+                assert_parity_literal(host(y), ref, what=what)
+            else:
+                assert_parity(host(y), ref, what=what, out_dtype=name)
 
 
 def test_forward_is_deterministic(gpu_lib):
@@ -523,57 +581,65 @@ def test_forward_in_hip_graph_replays(gpu_lib):
         assert torch.equal(y, eager)
 
 
-# -------------------------------------------------- full sizes, sampled tokens
+def test_decode_workspace_reuse_and_graph_replays(gpu_lib):
+    """The decode kernel's grid-wide exchange keeps its state in the
+    workspace: back-to-back calls on one workspace, a graph replayed several
+    times without clearing it, and replays after the workspace was cleared or
+    filled with other bytes all give the eager result bit for bit."""
+    cfg = synth.config("decode", E=64)
+    gp, ga, dp, da = _stacks(cfg)
+    x, lg = synth.activations(cfg), synth.router_logits(cfg)
+    args = [gpu(x, torch.bfloat16), gpu(lg), cfg.k, gpu(gp), gpu(ga), gpu(dp), gpu(da)]
+    eager = gpu_lib.moe_forward(*args, y_dtype=torch.float32).clone()
+    nbytes = gpu_lib.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=DEV)
+    for _ in range(5):
+        y.fill_(7.0)
+        gpu_lib.moe_forward(*args, y=y, workspace=ws)
+        assert torch.equal(y, eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gpu_lib.moe_forward(*args, y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu_lib.moe_forward(*args, y=y, workspace=ws)
+    for rep in range(6):
+        y.fill_(7.0)
+        if rep == 3:
+            ws.zero_()
+        if rep == 4:
+            ws.fill_(0xFF)
+        gpu_lib.moe_forward(*args, y_dtype=torch.float32)  # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), rep
 
-def _full_sampled(gpu_lib, name, n_tokens=6, seed=0):
-    cfg = synth.config(name)
-    x = synth.activations(cfg, seed)
-    lg = synth.router_logits(cfg, seed)
-    glo, dlo, glo_r, dlo_r = _lora(cfg)
-    # quantise the whole stacks on the GPU, one expert group at a time
-    gp = torch.empty((cfg.E, 2 * cfg.I, cfg.H // 2), dtype=torch.uint8, device=DEV)
-    ga = torch.empty((cfg.E, 2 * cfg.I, cfg.H // 64), dtype=torch.float32, device=DEV)
-    dp = torch.empty((cfg.E, cfg.H, cfg.I // 2), dtype=torch.uint8, device=DEV)
-    da = torch.empty((cfg.E, cfg.H, cfg.I // 64), dtype=torch.float32, device=DEV)
-    step = 16
-    for e0 in range(0, cfg.E, step):
-        ex = range(e0, min(e0 + step, cfg.E))
-        p, a = gpu_lib.quantize(gpu(synth.stack_weights(cfg, "gu", seed, ex)))
-        gp[e0:e0 + len(ex)] = p
-        ga[e0:e0 + len(ex)] = a
-        p, a = gpu_lib.quantize(gpu(synth.stack_weights(cfg, "dn", seed, ex)))
-        dp[e0:e0 + len(ex)] = p
-        da[e0:e0 + len(ex)] = a
-    y = gpu_lib.moe_forward(gpu(x, torch.bfloat16), gpu(lg), cfg.k, gp, ga, dp, da, glo, dlo,
-                            cfg.renormalize)
-    yh = host(y)
-    assert np.all(np.isfinite(yh))
-    rng = np.random.default_rng(99)
-    if cfg.T <= n_tokens:
-        toks = list(range(cfg.T))
-    else:
-        pick = rng.choice(np.arange(1, cfg.T - 1), n_tokens - 2, replace=False)
-        toks = sorted(set([0, cfg.T - 1] + [int(t) for t in pick]))
-    ids_ref, _ = oracle.route_topk(lg[toks], cfg.k)
-    need = sorted(set(ids_ref.ravel().tolist()))
-    # the oracle quantises the experts it needs from the same fp32 weights
-    gpr, gar, dpr, dar = {}, {}, {}, {}
-    for e in need:
-        gpr[e], gar[e] = oracle.quantize_blockwise(synth.expert_weights(cfg, "gu", e, seed))
-        dpr[e], dar[e] = oracle.quantize_blockwise(synth.expert_weights(cfg, "dn", e, seed))
-        # the GPU quantiser produced the same bytes for these experts
-        assert np.array_equal(host(gp[e]), gpr[e]) and np.array_equal(host(da[e]), dar[e])
-    ref = oracle.moe_forward_tokens(toks, x, lg, cfg.k, gpr, gar, dpr, dar, glo_r, dlo_r,
-                                    cfg.renormalize)
-    return yh[toks], ref
 
+# ------------------------------------------------ full sizes, every token
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["olmoe", "qwen3_zipf", "qlora", "decode"])
-def test_forward_full_size_sampled_tokens(gpu_lib, name):
-    y, ref = _full_sampled(gpu_lib, name, n_tokens=1 if name == "decode" else 6)
-    m = assert_parity(y, ref, what=name)
-    print(name, m)
+def test_forward_full_size(gpu_lib, name):
+    """The full-size layer in the launch configuration the benchmark times:
+    every expert's bytes verified against the oracle's (full_stacks), then
+    every token's output compared -- bf16 y under the relaxed max-abs reading
+    and fp32 y under the clause as written."""
+    cfg = synth.config(name)
+    (gp, ga, dp, da), (gpr, gar, dpr, dar) = full_stacks(gpu_lib, cfg)
+    x = synth.activations(cfg)
+    lg = synth.router_logits(cfg)
+    glo, dlo, glo_r, dlo_r = _lora(cfg)
+    args = (gpu(x, torch.bfloat16), gpu(lg), cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize)
+    yb = host(gpu_lib.moe_forward(*args))
+    yf = host(gpu_lib.moe_forward(*args, y_dtype=torch.float32))
+    ref, _ = oracle.moe_forward(x, lg, cfg.k, gpr, gar, dpr, dar, glo_r, dlo_r, cfg.renormalize)
+    m = assert_parity(yb, ref, what=name)
+    mf = assert_parity_literal(yf, ref, what=f"{name} f32")
+    print(name, "bf16", m, "f32", mf)
 
 
 # ------------------------------------------------- fp4 storage mode (4-bit)

@@ -33,3 +33,19 @@ def test_a_deviation_beyond_rounding_is_reported():
     bad[1234] += 0.05 * rms
     m = metrics(bad, y)
     assert m["maxabs_beyond_rounding"] > 0.04
+
+
+def test_literal_clause_has_no_rounding_allowance():
+    """The literal check fails an fp32 result whose only deviation is a bf16
+    rounding the relaxed rule forgives, and passes the exact result."""
+    import pytest
+
+    from parity import assert_parity_literal
+
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal(4096) * 3.0
+    y[7] = 123.4  # one large output: its bf16 rounding error is ~0.2 * RMS
+    assert_parity_literal(y.astype(np.float32), y)
+    yb = synth.round_to_bf16(y.astype(np.float32)).astype(np.float64)
+    with pytest.raises(AssertionError):
+        assert_parity_literal(yb, y)
