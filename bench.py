@@ -227,12 +227,9 @@ def cpu_baseline(cfg, seconds_target: float = 10.0):
     da = rng.uniform(0.01, 0.05, size=(E, H, I // 64)).astype(np.float32)
     x = synth.activations(cfg)
     lg = synth.router_logits(cfg)
-    try:
-        from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     runs, elapsed = 0, 0.0
     while elapsed < seconds_target and runs < 5:
         t0 = time.perf_counter()
@@ -240,6 +237,11 @@ def cpu_baseline(cfg, seconds_target: float = 10.0):
         elapsed += time.perf_counter() - t0
         runs += 1
     per = elapsed / runs
+    # the same forward once more on one thread (BLAS limited to 1)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, lg, cfg.k, gp, ga, dp, da)
+        per1 = time.perf_counter() - t0
     return {
         "value": round(cfg.flops() / per / 1e12, 6),
         "unit": "TFLOP/s",
@@ -247,7 +249,12 @@ def cpu_baseline(cfg, seconds_target: float = 10.0):
         "kind": "oracle",
         "sample": (f"{runs} full {cfg.name} layer forward(s) (T={cfg.T}, E={E}, H={H}, "
                    f"I={I}, top-{cfg.k}) of the NumPy fp64 oracle, random NF4 stacks, "
-                   f"{per:.2f} s each"),
+                   f"{per:.2f} s each; cores = the BLAS threads (NumPy's own loops, "
+                   f"the dequantisation included, run on one)"),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(threads),
+        "one_thread": {"value": round(cfg.flops() / per1 / 1e12, 6), "unit": "TFLOP/s",
+                       "seconds_per_forward": round(per1, 3)},
     }
 
 
@@ -590,6 +597,103 @@ def control_lane(cfg, st, x16, off, sp, stream, iters: int):
     return res, out
 
 
+def measure_prefill(cfg, dev, steps: int, warmup: int, keep: bool = False):
+    """One prefill workload: the whole layer forward timed over `steps`
+    forwards after `warmup` untimed ones (HIP events on the current stream,
+    device syncs around the timed region), then its gate_up and down grouped
+    GEMMs timed alone on the same routing."""
+    import torch
+
+    from grouped_nf4_gemm_quantize_amd import binding, synth
+
+    st = gpu_stacks(cfg, dev)
+    gp, ga = st["gu"]
+    dp, da = st["dn"]
+    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
+    lg = torch.from_numpy(synth.router_logits(cfg)).to(dev)
+    glo = dlo = None
+    lw = synth.lora_weights(cfg)
+    if lw is not None:
+        t = {k_: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k_, v in lw.items()}
+        glo = (t["a_gu"], t["b_gu"], cfg.lora_scale)
+        dlo = (t["a_dn"], t["b_dn"], cfg.lora_scale)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
+                                                     cfg.lora_r),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
+                            y=y, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` forwards, bracketed by device syncs
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    tflops = cfg.flops() / (ms * 1e-3) / 1e12
+    log(f"[bench] {cfg.name} layer forward {ms * 1e3:.1f} us  {tflops:.1f} TFLOP/s")
+
+    # the two grouped GEMMs alone, on this forward's routing
+    ptr = binding.forward_routing(ws, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    base = ws.data_ptr()
+    P = cfg.P
+    sp = ws[ptr["sorted_pair"] - base: ptr["sorted_pair"] - base + 4 * P].view(torch.int32)
+    off = ws[ptr["offsets"] - base: ptr["offsets"] - base + 4 * (cfg.E + 1)].view(torch.int32)
+    x16 = x.to(torch.float16)
+    h = torch.empty((P, cfg.I), dtype=torch.float16, device=dev)
+    o = torch.empty((P, cfg.H), dtype=torch.float16, device=dev)
+
+    def gate_up():
+        binding.grouped_gemm(x16, gp, ga, off, P, gather=sp, gather_div=cfg.k, lora=glo,
+                             swiglu=True, out=h)
+
+    def down():
+        binding.grouped_gemm(h, dp, da, off, P, lora=dlo, scatter=sp, out=o)
+
+    for _ in range(2):
+        gate_up()
+        down()
+    gu_ms = time_events(gate_up, max(steps, 10), stream)
+    dn_ms = time_events(down, max(steps, 10), stream)
+    gu_flops = 4.0 * P * cfg.H * cfg.I
+    dn_flops = 2.0 * P * cfg.H * cfg.I
+    if glo is not None:
+        gu_flops += 2.0 * P * cfg.lora_r * (cfg.H + 2 * cfg.I)
+        dn_flops += 2.0 * P * cfg.lora_r * (cfg.I + cfg.H)
+    gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    dn_tf = dn_flops / (dn_ms * 1e-3) / 1e12
+    log(f"[bench] {cfg.name} gate_up GEMM {gu_ms * 1e3:.1f} us {gu_tf:.1f} TFLOP/s; "
+        f"down GEMM {dn_ms * 1e3:.1f} us {dn_tf:.1f} TFLOP/s")
+    out = {
+        "workload": (f"{cfg.name} layer prefill: E={cfg.E} H={cfg.H} I={cfg.I} top-{cfg.k} "
+                     f"T={cfg.T}" + (f" LoRA r={cfg.lora_r}" if cfg.lora_r else "")
+                     + (" (Zipf routing)" if cfg.logits == "zipf" else "")),
+        "us_per_forward": round(ms * 1e3, 3),
+        "tflops": round(tflops, 3),
+        "frac_peak": round(tflops / PEAK_F16_TFLOPS, 4),
+        "flops_per_forward": cfg.flops(),
+        "gate_up_us": round(gu_ms * 1e3, 3), "gate_up_tflops": round(gu_tf, 3),
+        "gate_up_frac_peak": round(gu_tf / PEAK_F16_TFLOPS, 4),
+        "down_us": round(dn_ms * 1e3, 3), "down_tflops": round(dn_tf, 3),
+        "gate_up_flops": gu_flops,
+    }
+    del o, y, ws, gp, ga, dp, da
+    if keep:
+        out["_keep"] = (st, x16, off, sp, h)
+    else:
+        del st, x16, off, sp, h
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -599,6 +703,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="olmoe",
                     choices=["olmoe", "qwen3_zipf", "qlora"])
+    ap.add_argument("--prefill-workloads", default="qwen3_zipf,qlora",
+                    help="comma-separated further prefill workloads timed the same way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-control", action="store_true",
@@ -632,74 +738,15 @@ def main() -> int:
         copy_calibration(dev)
     cfg = synth.config(args.workload)
     log(f"[bench] workload {cfg}")
-    st = gpu_stacks(cfg, dev)
-    gp, ga = st["gu"]
-    dp, da = st["dn"]
-    x = torch.from_numpy(synth.activations(cfg)).to(dev).to(torch.bfloat16)
-    lg = torch.from_numpy(synth.router_logits(cfg)).to(dev)
-    glo = dlo = None
-    lw = synth.lora_weights(cfg)
-    if lw is not None:
-        t = {k_: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k_, v in lw.items()}
-        glo = (t["a_gu"], t["b_gu"], cfg.lora_scale)
-        dlo = (t["a_dn"], t["b_dn"], cfg.lora_scale)
-    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
-                                                     cfg.lora_r),
-                     dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
-                            y=y, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region: exactly `steps` forwards, bracketed by device syncs
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    pf = measure_prefill(cfg, dev, args.steps, args.warmup, keep=True)
+    ms, tflops = pf["us_per_forward"] / 1e3, pf["tflops"]
+    gu_ms, dn_ms = pf["gate_up_us"] / 1e3, pf["down_us"] / 1e3
+    gu_tf, dn_tf = pf["gate_up_tflops"], pf["down_tflops"]
+    gu_flops = pf["gate_up_flops"]
     flops = cfg.flops()
-    tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] layer forward {ms * 1e3:.1f} us  {tflops:.1f} TFLOP/s")
-
-    # dominant kernel alone: the gate_up grouped GEMM on this forward's routing
-    ptr = binding.forward_routing(ws, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
-    base = ws.data_ptr()
-    P = cfg.P
-    sp = ws[ptr["sorted_pair"] - base: ptr["sorted_pair"] - base + 4 * P].view(torch.int32)
-    off = ws[ptr["offsets"] - base: ptr["offsets"] - base + 4 * (cfg.E + 1)].view(torch.int32)
-    x16 = x.to(torch.float16)
-    h = torch.empty((P, cfg.I), dtype=torch.float16, device=dev)
-    o = torch.empty((P, cfg.H), dtype=torch.float16, device=dev)
-
-    def gate_up():
-        binding.grouped_gemm(x16, gp, ga, off, P, gather=sp, gather_div=cfg.k, lora=glo,
-                             swiglu=True, out=h)
-
-    def down():
-        binding.grouped_gemm(h, dp, da, off, P, lora=dlo, scatter=sp, out=o)
-
-    for _ in range(2):
-        gate_up()
-        down()
-    gu_ms = time_events(gate_up, max(args.steps, 10), stream)
-    dn_ms = time_events(down, max(args.steps, 10), stream)
-    gu_flops = 4.0 * P * cfg.H * cfg.I
-    dn_flops = 2.0 * P * cfg.H * cfg.I
-    if glo is not None:
-        gu_flops += 2.0 * P * cfg.lora_r * (cfg.H + 2 * cfg.I)
-        dn_flops += 2.0 * P * cfg.lora_r * (cfg.I + cfg.H)
-    gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
-    dn_tf = dn_flops / (dn_ms * 1e-3) / 1e12
-    log(f"[bench] gate_up GEMM {gu_ms * 1e3:.1f} us {gu_tf:.1f} TFLOP/s; "
-        f"down GEMM {dn_ms * 1e3:.1f} us {dn_tf:.1f} TFLOP/s")
+    st, x16, off, sp, h = pf.pop("_keep")
+    stream = torch.cuda.current_stream(dev)
+    glo = None if not cfg.lora_r else True
     traffic = traffic_from_profiles(GEMM_SRC)
     control = None
     if glo is None and not args.no_control:
@@ -718,7 +765,7 @@ def main() -> int:
             control["h_rel_fro_vs_fused"] = float(((got - ref).norm() / ref.norm()).item())
         del cout
         log(f"[bench] dequantise-then-GEMM control {control}")
-    del h, o, x16
+    del h, x16
 
     result = {
         "metric": METRIC,
@@ -758,8 +805,17 @@ def main() -> int:
     }
     if control is not None:
         result["control_dequant_then_gemm"] = control
-    del gp, ga, dp, da, st, y, ws
+    del st, off, sp
     torch.cuda.empty_cache()
+    others = [n_ for n_ in args.prefill_workloads.split(",") if n_ and n_ != cfg.name]
+    if others:
+        result["prefill_workloads"] = {}
+        for n_ in others:
+            r_ = measure_prefill(synth.config(n_), dev, args.steps, args.warmup)
+            r_.pop("gate_up_flops")
+            result["prefill_workloads"][n_] = r_
+            log(f"[bench] prefill {n_} {r_}")
+            torch.cuda.empty_cache()
     if not args.no_decode:
         result["decode"] = bench_decode(dev, args.steps)
         log(f"[bench] decode {result['decode']}")
