@@ -17,6 +17,7 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnf4moe.so")
 
 F32, BF16, F16 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 32 << 20  # NF4MOE_NOALLOC_SCRATCH_BYTES
 EPI_NONE, EPI_SWIGLU, EPI_SWIGLU_BWD = 0, 1, 2
 
 STATUS = {
@@ -71,6 +72,10 @@ _SIGNATURES = {
                                     _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                     ctypes.POINTER(LoraStruct), ctypes.POINTER(LoraStruct),
                                     _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
+    "moe_expert_forward_noalloc": (_c_int, [_c_vp, _c_int, _c_vp, _c_i64, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                            ctypes.POINTER(LoraStruct),
+                                            ctypes.POINTER(LoraStruct), _c_vp, _c_int, _c_vp]),
     "moe_expert_forward_routing": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int,
                                             ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp),
                                             ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp)]),
@@ -317,6 +322,29 @@ def moe_forward(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
         _check(lib.moe_expert_forward(*args))
     else:
         _check(lib.moe_expert_forward_nbit(_qt(quant_type), *args))
+    return y
+
+
+def moe_forward_noalloc(x, logits, k: int, gu_packed, gu_absmax, dn_packed, dn_absmax,
+                        gu_lora=None, dn_lora=None, renormalize: bool = True, y=None,
+                        y_dtype=None):
+    """The layer forward on the library's fixed per-device scratch memory
+    (see moe_expert_forward_noalloc): no workspace argument, nothing
+    allocated by the library.  Returns ``y``."""
+    torch = _torch()
+    T, H = x.shape
+    E = logits.shape[1]
+    I = dn_packed.shape[2] * 2
+    if y is None:
+        y = torch.empty((T, H), dtype=y_dtype or torch.bfloat16, device=x.device)
+    ls_gu = make_lora(*gu_lora) if gu_lora is not None else None
+    ls_dn = make_lora(*dn_lora) if dn_lora is not None else None
+    _check(load().moe_expert_forward_noalloc(
+        _ptr(x), _dtype_code(x.dtype), _ptr(logits), T, H, I, E, k, int(bool(renormalize)),
+        _ptr(gu_packed), _ptr(gu_absmax), _ptr(dn_packed), _ptr(dn_absmax),
+        ctypes.byref(ls_gu) if ls_gu is not None else None,
+        ctypes.byref(ls_dn) if ls_dn is not None else None,
+        _ptr(y), _dtype_code(y.dtype), _stream(x.device)))
     return y
 
 

@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libnf4moe.so")
 ARCH = "gfx950"
 
 SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "gemm16.hip", "dgrad.hip", "lora.hip", "gemv.hip",
-           "abi.cpp"]
+           "noalloc.hip", "abi.cpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

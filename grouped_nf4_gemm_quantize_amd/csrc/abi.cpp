@@ -41,6 +41,20 @@ int ok() {
   return NF4MOE_OK;
 }
 
+}  // namespace
+
+int nf4moe::report_error(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+namespace {
+
 int hip_fail(hipError_t err, const char* what) {
   return fail(NF4MOE_EHIP, "%s: %s", what, hipGetErrorString(err));
 }

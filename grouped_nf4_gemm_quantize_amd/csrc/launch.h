@@ -7,6 +7,10 @@
 
 namespace nf4moe {
 
+// Records `fmt` as this thread's last-error message (nf4moe_last_error) and
+// returns `status`.
+int report_error(int status, const char* fmt, ...);
+
 // fp32 thresholds of the quantiser: t[j] is the largest fp32 value that is
 // <= the exact midpoint of levels j and j+1, so  xn > t[j]  <=>  xn lies
 // strictly above that midpoint (a tie goes to the lower level).

@@ -411,6 +411,28 @@ int moe_expert_forward_mxfp4(const void* x, int x_dtype, const float* router_log
                              const uint8_t* dn_scales, void* y, int y_dtype,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- allocation-free layer forward ----------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The same
+ * computation, kernels and arguments as moe_expert_forward, without the
+ * workspace: the library keeps NF4MOE_NOALLOC_SCRATCH_BYTES (32 MiB) of device
+ * memory per device in its code object, held until the process ends, and this
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Sizes whose workspace (moe_expert_forward_workspace) exceeds it
+ * are refused with NF4MOE_EWORKSPACE before anything is launched (the
+ * Qwen3-30B-A3B layer fits up to about 670 tokens without adapters, 410 with
+ * rank-8 adapters on both projections); other
+ * argument errors as for moe_expert_forward.  Every call on one device shares
+ * that memory: calls that overlap in time on one device (other streams,
+ * other threads) race and must be serialised by the caller. */
+#define NF4MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_expert_forward_noalloc(const void* x, int x_dtype, const float* router_logits,
+                               int64_t T, int H, int I, int E, int k, int renormalize,
+                               const uint8_t* gu_packed, const float* gu_absmax,
+                               const uint8_t* dn_packed, const float* dn_absmax,
+                               const nf4moe_lora* gu_lora, const nf4moe_lora* dn_lora,
+                               void* y, int y_dtype, void* stream);
+
 /* Device-pointer views into a moe_expert_forward workspace (for inspection of
  * the routing a forward used; valid after the forward completes on its
  * stream, the T == 1 decode path included: it writes ids, weights, the k

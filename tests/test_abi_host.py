@@ -235,6 +235,34 @@ def test_forward_validation(lib):
     assert call(H=2**16, I=2**16) == -7     # one expert's gate_up stack past 4 GiB
 
 
+def test_noalloc_forward_validation(lib):
+    """The allocation-free forward reports argument errors as the forward does
+    and refuses sizes whose workspace exceeds its scratch, before any launch."""
+    f = lib.moe_expert_forward_noalloc
+    T, H, I, E, k = 64, 256, 128, 8, 2
+
+    def call(**kw):
+        a = dict(x=FAKE, xdt=1, lg=FAKE, T=T, H=H, I=I, E=E, k=k, renorm=1, gp=FAKE,
+                 ga=FAKE, dp=FAKE, da=FAKE, gl=None, dl=None, y=FAKE, ydt=1, stream=None)
+        a.update(kw)
+        return f(a["x"], a["xdt"], a["lg"], a["T"], a["H"], a["I"], a["E"], a["k"],
+                 a["renorm"], a["gp"], a["ga"], a["dp"], a["da"], a["gl"], a["dl"],
+                 a["y"], a["ydt"], a["stream"])
+
+    assert call(x=None) == -1
+    assert call(H=200) == -2
+    assert call(k=9) == -4
+    assert call(ydt=5) == -5
+    T_big = 1024
+    need = lib.moe_expert_forward_workspace(T_big, 2048, 768, 128, 8, 0)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert call(T=T_big, H=2048, I=768, E=128, k=8) == -6
+    assert "scratch" in _last(lib)
+    # the limit sits where the workspace size query says it does
+    assert lib.moe_expert_forward_workspace(670, 2048, 768, 128, 8, 0) <= \
+        binding.NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings(lib):
     for s in range(0, -9, -1):
         assert lib.nf4moe_strerror(s).decode() != "unknown status"
