@@ -5,6 +5,8 @@
                     [--no-control] [--no-mxfp4] [--copy-calibration]
     python bench.py --summarize-trace DIR
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR
+    python bench.py --summarize-pmc DIR KERNEL_SUBSTR
+    python bench.py --summarize-decode-fetch FETCH_DIR
 
 A step is one full routed-expert layer forward (route + permute, gate_up with
 SwiGLU, down, combine) over the whole batch, inputs resident in HBM.  The
@@ -694,6 +696,63 @@ def measure_prefill(cfg, dev, steps: int, warmup: int, keep: bool = False):
     return out
 
 
+def summarize_pmc(directory: str, kernel_substr: str) -> int:
+    """Markdown table of a rocprofv3 --pmc run: the mean of every counter per
+    dispatch of the kernels whose name contains `kernel_substr`."""
+    per = {}
+    names = set()
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if kernel_substr not in r["Kernel_Name"]:
+            continue
+        names.add(r["Kernel_Name"])
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Counter_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of a kernel containing {kernel_substr!r} in {directory}")
+    sums, counts = {}, {}
+    for (_, c), v in per.items():
+        sums[c] = sums.get(c, 0.0) + v
+        counts[c] = counts.get(c, 0) + 1
+    print(f"kernel(s): {', '.join(sorted('`' + n + '`' for n in names))}")
+    print()
+    print("| counter | dispatches | mean per dispatch |")
+    print("|---|---:|---:|")
+    for c in sorted(sums):
+        print(f"| {c} | {counts[c]} | {sums[c] / counts[c]:.6g} |")
+    return 0
+
+
+def summarize_decode_fetch(fetch_dir: str) -> int:
+    """HBM bytes read per decode-layer launch (FETCH_SIZE, scaled by what the
+    counter reads for the 512 MiB calibration copy) against its algorithmic
+    packed-weight bytes."""
+    dec, copy = [], []
+    for r in _csv_rows(fetch_dir, "counter_collection.csv"):
+        if r["Counter_Name"] != "FETCH_SIZE":
+            continue
+        if "decode_layer_kernel" in r["Kernel_Name"]:
+            dec.append(float(r["Counter_Value"]))
+        elif "copyBuffer" in r["Kernel_Name"]:
+            copy.append(float(r["Counter_Value"]))
+    if not dec or not copy:
+        raise SystemExit(f"decode or copy dispatches missing in {fetch_dir}")
+    copy.sort()
+    scale = COPY_BYTES / 1024.0 / copy[-1]
+    mean = sum(dec) / len(dec)
+    algo = 21233664
+    fetch_b = mean * scale * 1024.0
+    print("| quantity | value |")
+    print("|---|---:|")
+    print(f"| decode layer launches | {len(dec)} |")
+    print(f"| FETCH_SIZE per launch, KiB (raw) | {mean:.0f} |")
+    print(f"| 512 MiB copy, KiB (raw) | {copy[-1]:.0f} |")
+    print(f"| scale = 524288 KiB / copy reading | {scale:.4f} |")
+    print(f"| HBM bytes fetched per launch (scaled) | {fetch_b:.0f} |")
+    print(f"| algorithmic packed bytes per layer | {algo} |")
+    print(f"| fetched / algorithmic | {fetch_b / algo:.3f} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -718,7 +777,13 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("DIR", "KERNEL_SUBSTR"))
+    ap.add_argument("--summarize-decode-fetch", metavar="FETCH_DIR")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc)
+    if args.summarize_decode_fetch:
+        return summarize_decode_fetch(args.summarize_decode_fetch)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_counters:
