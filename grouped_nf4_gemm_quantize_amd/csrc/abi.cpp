@@ -306,9 +306,11 @@ static int quantize_impl(int qt, const void* w, int w_dtype, int64_t E, int64_t 
   const int64_t n = E * N * K;
   if (n / E / N != K || n > ((int64_t)1 << 50))
     return fail(NF4MOE_EOVERFLOW, "E*N*K is too large");
-  if (!aligned(w, w_dtype == NF4MOE_F32 ? 16 : 8) || !aligned(packed, 2) ||
-      !aligned(absmax, 4))
-    return fail(NF4MOE_EINVAL, "misaligned buffer (w needs 16 bytes for F32, 8 for BF16)");
+  if (!aligned(w, w_dtype == NF4MOE_F32 ? 16 : 8) || !aligned(packed, is_8bit(qt) ? 4 : 2) ||
+      !aligned(absmax, 4) || !aligned(nonfinite_flag, 4))
+    return fail(NF4MOE_EINVAL,
+                "misaligned buffer (w needs 16 bytes for F32, 8 for BF16; packed 4 bytes for "
+                "the 8-bit modes, 2 otherwise; absmax and nonfinite_flag 4)");
   if (is_16bit(qt) && (!aligned(w, 16) || !aligned(packed, 16)))
     return fail(NF4MOE_EINVAL, "passthrough storage needs w and packed 16-byte aligned");
   int cus = 0;

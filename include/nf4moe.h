@@ -110,9 +110,11 @@ int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K);
  *   blocksize      must be 64 (else EBLOCK)
  *   K              must be a positive multiple of 64 (else ESHAPE)
  *   packed, absmax outputs as described in the conventions above
- *   nonfinite_flag nullable device int32; set to 1 (never cleared) if any
- *                  input element is NaN or +-Inf.  Codes of such blocks are
- *                  unspecified.
+ *   nonfinite_flag nullable device int32, 4-byte aligned; set to 1 (never
+ *                  cleared) if any input element is NaN or +-Inf.  Codes of
+ *                  such blocks are unspecified.
+ * Alignment (else EINVAL): w 16 bytes (F32) or 8 (BF16), packed 2 bytes (4
+ * for the 8-bit modes of nbit_quantize_experts), absmax 4.
  */
 int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
                          int64_t K, int blocksize, uint8_t* packed,

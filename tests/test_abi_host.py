@@ -128,6 +128,11 @@ def test_quantize_validation(lib):
     assert q(FAKE, 0, 0, 1, 64, 64, FAKE, FAKE, None, None) == -1
     assert q(FAKE + 4, 0, 1, 1, 64, 64, FAKE, FAKE, None, None) == -1  # misaligned
     assert "misaligned" in _last(lib)
+    # the 8-bit modes store whole words of codes; the flag is an int32
+    qn = lib.nbit_quantize_experts
+    assert qn(3, FAKE, 0, 1, 1, 64, 64, FAKE + 2, FAKE, None, None) == -1  # int8, packed % 4
+    assert qn(4, FAKE, 0, 1, 1, 64, 64, FAKE + 2, FAKE, None, None) == -1  # fp8, packed % 4
+    assert q(FAKE, 0, 1, 1, 64, 64, FAKE, FAKE, FAKE + 2, None) == -1  # nonfinite_flag % 4
 
 
 def test_route_validation(lib):
