@@ -60,6 +60,7 @@ _SIGNATURES = {
     "nf4moe_packed_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64]),
     "nf4_quantize_experts": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int,
                                       _c_vp, _c_vp, _c_vp, _c_vp]),
+    "nf4moe_f16_range_check": (_c_int, [_c_vp, _c_int, _c_i64, _c_vp, _c_vp]),
     "moe_route_permute_workspace": (_c_size, [_c_i64, _c_int, _c_int]),
     "moe_route_permute": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp,
                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -220,6 +221,16 @@ def quantize(w, nonfinite_flag=None, quant_type: str = "nf4"):
     else:
         _check(load().nbit_quantize_experts(_qt(quant_type), *args))
     return packed, absmax
+
+
+def f16_range_check(t, flags):
+    """OR into ``flags`` (one int32 on the GPU) what an fp16 conversion of the
+    bf16 / fp32 tensor ``t`` would lose (see nf4moe_f16_range_check)."""
+    if not t.is_contiguous():
+        raise ValueError("t must be contiguous")
+    _check(load().nf4moe_f16_range_check(_ptr(t), _dtype_code(t.dtype), t.numel(), _ptr(flags),
+                                         _stream(t.device)))
+    return flags
 
 
 def route_permute(logits, k: int, renormalize: bool = True):

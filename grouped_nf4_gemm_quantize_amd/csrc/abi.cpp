@@ -344,6 +344,22 @@ int nbit_quantize_experts(int quant_type, const void* w, int w_dtype, int64_t E,
                        nonfinite_flag, stream);
 }
 
+int nf4moe_f16_range_check(const void* t, int dtype, int64_t n, int32_t* flags, void* stream) {
+  if (t == nullptr || flags == nullptr) return fail(NF4MOE_EINVAL, "t and flags must be non-null");
+  if (n < 1) return fail(NF4MOE_EINVAL, "n=%lld must be positive", (long long)n);
+  if (dtype != NF4MOE_BF16 && dtype != NF4MOE_F32)
+    return fail(NF4MOE_EDTYPE, "dtype=%d: the range check takes BF16 or F32 values", dtype);
+  if (!aligned(t, dtype == NF4MOE_F32 ? 16 : 8) || !aligned(flags, 4))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (t needs 16 bytes for F32, 8 for BF16; "
+                               "flags 4)");
+  int cus = 0;
+  int st = cu_count(&cus);
+  if (st != NF4MOE_OK) return st;
+  hipError_t err = launch_f16_range(t, dtype == NF4MOE_BF16, n, flags, cus, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "range check launch");
+  return ok();
+}
+
 size_t moe_route_permute_workspace(int64_t T, int E, int k) {
   (void)k;
   if (T < 1 || E < 1 || E > NF4MOE_MAX_EXPERTS) return 0;

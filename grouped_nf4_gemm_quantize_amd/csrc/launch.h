@@ -27,6 +27,11 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t nelem,
                            const QuantThresholds& thr, int num_cus,
                            hipStream_t stream);
 
+// Scan of n bf16 or fp32 values for what an fp16 conversion loses (flag bits
+// as documented at nf4moe_f16_range_check).
+hipError_t launch_f16_range(const void* t, bool bf16, int64_t n, int32_t* flags, int num_cus,
+                            hipStream_t stream);
+
 struct RouteArgs {
   const float* logits;
   int64_t T;

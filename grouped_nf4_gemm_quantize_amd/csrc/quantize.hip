@@ -53,7 +53,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 #pragma unroll
   for (int j = 0; j < 15; ++j) t[j] = thr.t[j];
 
+  // the fp16 multiplier the grouped GEMMs make of a block's absmax: absmax,
+  // absmax / 127 (int8) or absmax / 448 (fp8)
+  constexpr float kScaleDiv = kQ == 2 ? 127.0f : kQ == 3 ? 448.0f : 1.0f;
   bool bad = false;
+  bool out_of_range = false;
   for (int64_t b0 = wave_global * 4; b0 < nblocks; b0 += nwaves * 4) {
     const int64_t blk = b0 + blk_in_wave;
     const bool live = blk < nblocks;
@@ -82,6 +86,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     // max over the 16 lanes of the block (one DPP row: lanes differ only in
     // bits 0..3); max is exact, so the order of the butterfly is immaterial
     a = row16_max(a);
+    {
+      // outside fp16's normal range the multiplier overflows (|s| >= 65520
+      // rounds to inf) or keeps fewer than 11 significant bits (s < 2^-14)
+      const float sc = a / kScaleDiv;
+      // (a non-finite block is reported by the first bit alone)
+      out_of_range |= live && a != 0.f && __builtin_isfinite(a) &&
+                      !(sc >= 0x1p-14f && sc < 65520.0f);
+    }
 
     uint32_t codes[4];
 #pragma unroll
@@ -118,7 +130,70 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       if (sub == 0) absmax[blk] = a;
     }
   }
-  if (bad && nonfinite_flag != nullptr) atomicOr(nonfinite_flag, 1);
+  if (nonfinite_flag != nullptr && (bad || out_of_range))
+    atomicOr(nonfinite_flag, (bad ? 1 : 0) | (out_of_range ? 2 : 0));
+}
+
+// Flags of the fp16 conversion of n values (bf16 or fp32), OR-ed into *flags:
+// 1 = a value fp16 cannot hold (|v| >= 65520 rounds to inf; NaN and inf
+// included), 2 = a nonzero value fp16 flushes to zero (|v| <= 2^-25 rounds
+// to 0), 4 = a nonzero value below fp16's normal range (|v| < 2^-14: fewer than
+// 11 significant bits).  One atomic per wave that saw anything.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void f16_range_kernel(const void* __restrict__ t, int64_t n,
+                                                        int32_t* __restrict__ flags) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  uint32_t f = 0;
+  for (int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i0 < n; i0 += stride) {
+    float v[4];
+    if (i0 + 4 <= n) {
+      if constexpr (kBF16) {
+        const u32x2 r = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(t) + i0);
+        v[0] = bf16_bits_to_f32(r.x & 0xffffu);
+        v[1] = bf16_bits_to_f32(r.x >> 16);
+        v[2] = bf16_bits_to_f32(r.y & 0xffffu);
+        v[3] = bf16_bits_to_f32(r.y >> 16);
+      } else {
+        const f32x4 r = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(t) + i0);
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = 0.f;
+        if (i0 + j < n)
+          v[j] = kBF16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(t)[i0 + j])
+                       : reinterpret_cast<const float*>(t)[i0 + j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = fabsf(v[j]);
+      f |= !(a < 65520.0f) ? 1u : 0u;  // NaN compares false
+      f |= (a != 0.f && a <= 0x1p-25f) ? 2u : 0u;
+      f |= (a != 0.f && a < 0x1p-14f) ? 4u : 0u;
+    }
+  }
+  // one OR per wave (the lanes' bits combined through ballots)
+  uint32_t w = 0;
+#pragma unroll
+  for (int b = 0; b < 3; ++b) w |= __ballot((f >> b) & 1u) != 0ull ? (1u << b) : 0u;
+  if ((threadIdx.x & 63) == 0 && w != 0u) atomicOr(flags, (int)w);
+}
+
+hipError_t launch_f16_range(const void* t, bool bf16, int64_t n, int32_t* flags, int num_cus,
+                            hipStream_t stream) {
+  int64_t grid = (n + 1023) / 1024;
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (bf16)
+    hipLaunchKernelGGL(f16_range_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, t, n,
+                       flags);
+  else
+    hipLaunchKernelGGL(f16_range_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, t, n,
+                       flags);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t nelem,

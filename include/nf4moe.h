@@ -39,7 +39,10 @@
  *    are decoded to fp16 MFMA operands (level and absmax rounded to fp16,
  *    product rounded to fp16); activations enter the MFMA as fp16.  Values
  *    must therefore lie in fp16 range (|v| < 65504); values below 2^-14 lose
- *    precision gradually (fp16 subnormals).
+ *    precision gradually (fp16 subnormals).  Both are observable without a
+ *    host sync: the quantiser flags a stack whose absmax leaves the range
+ *    (nonfinite_flag bit 2), nf4moe_f16_range_check flags activations or
+ *    gradients, and values past 65504 inside the layer become +-inf in y.
  */
 #ifndef NF4MOE_H
 #define NF4MOE_H
@@ -110,15 +113,37 @@ int64_t nf4moe_packed_bytes(int64_t E, int64_t N, int64_t K);
  *   blocksize      must be 64 (else EBLOCK)
  *   K              must be a positive multiple of 64 (else ESHAPE)
  *   packed, absmax outputs as described in the conventions above
- *   nonfinite_flag nullable device int32, 4-byte aligned; set to 1 (never
- *                  cleared) if any input element is NaN or +-Inf.  Codes of
- *                  such blocks are unspecified.
+ *   nonfinite_flag nullable device int32, 4-byte aligned; bits OR-ed in,
+ *                  never cleared: 1 if any input element is NaN or +-Inf
+ *                  (codes of such blocks are unspecified); 2 if a block's
+ *                  absmax, as the fp16 multiplier the grouped GEMMs make of
+ *                  it (absmax; absmax/127 for int8, absmax/448 for fp8), is
+ *                  outside fp16's normal range [2^-14, 65504] (all-zero
+ *                  and non-finite blocks excepted): such a block's weights lose precision in
+ *                  the GEMMs (below) or become infinite (above).
  * Alignment (else EINVAL): w 16 bytes (F32) or 8 (BF16), packed 2 bytes (4
  * for the 8-bit modes of nbit_quantize_experts), absmax 4.
  */
 int nf4_quantize_experts(const void* w, int w_dtype, int64_t E, int64_t N,
                          int64_t K, int blocksize, uint8_t* packed,
                          float* absmax, int32_t* nonfinite_flag, void* stream);
+
+/* ---- fp16 range check ----------------------------------------------------
+ * The grouped GEMMs multiply in fp16 (activations converted from bf16, see the
+ * conventions above); this reports on the device, without a host sync, what
+ * that conversion would lose for n values t (BF16 or F32; x before a forward,
+ * dL/dy before a backward).  Bits OR-ed into *flags (never cleared):
+ *   1  a value fp16 cannot hold: |v| >= 65520 rounds to +-inf (NaN and inf
+ *      included) -- the layer's output then carries non-finite values;
+ *   2  a nonzero value fp16 flushes to zero (|v| <= 2^-25);
+ *   4  a nonzero value below fp16's normal range (|v| < 2^-14): fewer than 11
+ *      significant bits (an absolute error below 2^-25; N(0,1) activations
+ *      have a few such values per hundred thousand, harmless in a dot
+ *      product).
+ * Alignment: t 16 bytes (F32) or 8 (BF16), flags 4 (else EINVAL); other
+ * dtypes -> EDTYPE.  The absmax of a stack is checked by the quantiser
+ * (nonfinite_flag bit 2). */
+int nf4moe_f16_range_check(const void* t, int dtype, int64_t n, int32_t* flags, void* stream);
 
 /* ---- router top-k and pair permutation -----------------------------------
  * For T tokens with fp32 router logits [T, E] (E <= NF4MOE_MAX_EXPERTS):

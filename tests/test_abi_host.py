@@ -332,3 +332,13 @@ def test_mxfp4_entry_points_check_shapes_on_the_host(lib):
                                   None, None, FAKE, 2, None) == -1
     assert lib.moe_expert_forward_mxfp4(FAKE, 1, FAKE, 4, 192, 128, 4, 2, 1, FAKE, FAKE,
                                         FAKE, FAKE, FAKE, 1, FAKE, 1 << 30, None) == -2
+
+
+def test_f16_range_check_validation(lib):
+    f = lib.nf4moe_f16_range_check
+    assert f(None, 1, 8, FAKE, None) == -1
+    assert f(FAKE, 1, 8, None, None) == -1
+    assert f(FAKE, 1, 0, FAKE, None) == -1
+    assert f(FAKE, 2, 8, FAKE, None) == -5  # F16 values need no check
+    assert f(FAKE + 4, 0, 8, FAKE, None) == -1  # F32 needs 16 bytes
+    assert f(FAKE, 1, 8, FAKE + 2, None) == -1
