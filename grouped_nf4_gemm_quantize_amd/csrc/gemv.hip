@@ -46,10 +46,6 @@
 
 namespace nf4moe {
 
-__constant__ float c_levels_gemv[16] = NF4MOE_LEVELS_INIT;
-__constant__ float c_levels_gemv_fp4[16] = NF4MOE_FP4_LEVELS_INIT;
-__constant__ float c_levels_gemv_mx[16] = NF4MOE_E2M1_VALUES_INIT;
-
 namespace {
 constexpr int kCopies = 32;
 constexpr int kThreads = 512;          // 8 waves per workgroup
@@ -202,10 +198,51 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
   uint64_t* hx = g.barrier + kDecodeFlagOffset;
   const uint64_t gen = load_agent(gen_p);
 
+  // the decode table, built while the logits are in flight: the 16 levels
+  // rounded to fp16 (immediates, no load), then entry b (two levels) is
+  // written by two threads, 16 of its kCopies interleaved copies each
+  static_assert(kThreads == 2 * 256 && kCopies == 32, "table fill layout");
+  if (tid == 0) {
+    s_fail = 0;
+    constexpr float kNf4[16] = NF4MOE_LEVELS_INIT;
+    constexpr float kFp4[16] = NF4MOE_FP4_LEVELS_INIT;
+    constexpr float kE2m1[16] = NF4MOE_E2M1_VALUES_INIT;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float lv = g.qtype == kQtMXFP4 ? kE2m1[i] : g.qtype == kQtFP4 ? kFp4[i] : kNf4[i];
+      s_stage[i] = __builtin_bit_cast(uint16_t, (_Float16)lv);
+    }
+  }
+  __syncthreads();
+  {
+    const bool low_first = g.qtype == kQtMXFP4;
+    const int b = tid >> 1;
+    const int first = low_first ? (b & 15) : (b >> 4);
+    const int second = low_first ? (b >> 4) : (b & 15);
+    const uint32_t v = (uint32_t)s_stage[first] | ((uint32_t)s_stage[second] << 16);
+    const u32x4 v4 = {v, v, v, v};
+    u32x4* dst = reinterpret_cast<u32x4*>(s_lut + b * kCopies + (tid & 1) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = v4;
+  }
+
   // route in every wave: lane j < k holds slot j
   int id;
   float w;
   route_select<kRegs>(lgv, g.E, k, g.renormalize, lane, &id, &w);
+
+  // x as fp16 in LDS (its loads went out with the logits'; converted by
+  // every thread, so the wait for them is not inside a branch)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i0 = (p * kThreads + tid) * kXPer;
+    const uint2 hv = make_uint2(pack_half2(to_f16(xr[p].x & 0xffffu, g.x_bf16),
+                                           to_f16(xr[p].x >> 16, g.x_bf16)),
+                                pack_half2(to_f16(xr[p].y & 0xffffu, g.x_bf16),
+                                           to_f16(xr[p].y >> 16, g.x_bf16)));
+    if (i0 < H) *reinterpret_cast<uint2*>(s_x + i0) = hv;
+  }
+  __syncthreads();  // table and x complete
 
   const int chunks = H / 32;
   const int64_t row_bytes = H / 2;
@@ -295,51 +332,14 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
       if (m < kDnFirst || 64 * m < total) load_chunk(m, row);
   };
 
-  // every load of the first round goes out back to back (the address
-  // arithmetic above is done, so no wait for an earlier load intervenes)
+  // the gate/up loads of the first round go out back to back (the address
+  // arithmetic above is done, so no wait for an earlier load intervenes); the
+  // down loads follow once this wave's h is computed, so the gate/up bytes
+  // the exchange waits for are not queued behind them
 #pragma unroll
   for (int t = 0; t < kItems; ++t) load_item(t, item_q(t));
   int n = q0;
-  {
-    const int row = n < H ? n : H - 1;
-#pragma unroll
-    for (int m = 0; m < kDnFirst; ++m) load_chunk(m, row);
-#pragma unroll
-    for (int m = kDnFirst; m < kMaxChunksPerLane; ++m)
-      if (64 * m < total) load_chunk(m, row);
-  }
   if (blockIdx.x == 0 && wave == 0) write_routing(g, lane, id, w);
-
-  // stage x as fp16 and build the table while the weights are in flight
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i0 = (p * kThreads + tid) * kXPer;
-    if (i0 < H) {
-      s_x[i0 + 0] = to_f16(xr[p].x & 0xffffu, g.x_bf16);
-      s_x[i0 + 1] = to_f16(xr[p].x >> 16, g.x_bf16);
-      s_x[i0 + 2] = to_f16(xr[p].y & 0xffffu, g.x_bf16);
-      s_x[i0 + 3] = to_f16(xr[p].y >> 16, g.x_bf16);
-    }
-  }
-  if (tid == 0) {
-    s_fail = 0;
-    // the 16 levels (uniform addresses: scalar loads), rounded to fp16
-    const float* levels = g.qtype == kQtMXFP4 ? c_levels_gemv_mx
-                          : g.qtype == kQtFP4 ? c_levels_gemv_fp4 : c_levels_gemv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s_stage[i] = __builtin_bit_cast(uint16_t, (_Float16)levels[i]);
-  }
-  __syncthreads();
-  {
-    const bool low_first = g.qtype == kQtMXFP4;
-    for (int i = tid; i < 256 * kCopies; i += kThreads) {
-      const int b = i / kCopies;
-      const int first = low_first ? (b & 15) : (b >> 4);
-      const int second = low_first ? (b >> 4) : (b & 15);
-      s_lut[i] = (uint32_t)s_stage[first] | ((uint32_t)s_stage[second] << 16);
-    }
-  }
-  __syncthreads();
 
   // ---- gate/up dots -> h (w_j * silu(gate) * up, rounded once to fp16),
   // published as one 64-bit word: this launch's tag | the fp16 bits
@@ -371,6 +371,14 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
   // the first round's loads went out before the table was built; later
   // rounds (more items than waves * kItems) load and compute in turn
   item_dots(0);
+  {
+    const int row = n < H ? n : H - 1;
+#pragma unroll
+    for (int m = 0; m < kDnFirst; ++m) load_chunk(m, row);
+#pragma unroll
+    for (int m = kDnFirst; m < kMaxChunksPerLane; ++m)
+      if (64 * m < total) load_chunk(m, row);
+  }
   for (int it0 = kItems; it0 < n_items; it0 += kItems) {
 #pragma unroll
     for (int t = 0; t < kItems; ++t) load_item(t, item_q(it0 + t));
