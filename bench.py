@@ -316,6 +316,34 @@ def bench_decode(dev, steps: int, mx: bool = False):
     per_elem_16ths = 9 if not mx else 10
     per_layer_bytes = cfg.k * (2 * cfg.I * cfg.H + cfg.H * cfg.I) * per_elem_16ths // 16
     gbs = DECODE_LAYERS * per_layer_bytes / (graph_ms * 1e-3) / 1e9
+    del g
+    torch.cuda.empty_cache()
+    # context: a plain one-shot read of the same byte count from HBM, 48
+    # distinct buffers read back to back on one stream (torch's sum reduction
+    # as the reader, launched eagerly: its launches queue ahead of the GPU as
+    # the decode layers' do), the ceiling of a single dependent-free pass at
+    # this size
+    stream = None
+    if not mx:
+        bufs = [torch.ones(per_layer_bytes // 4, dtype=torch.float32, device=dev)
+                for _ in range(DECODE_LAYERS)]
+        outs = torch.empty(DECODE_LAYERS, dtype=torch.float32, device=dev)
+        s2 = torch.cuda.Stream(device=dev)
+
+        def read_all():
+            for i, b in enumerate(bufs):
+                torch.sum(b, dim=0, out=outs[i])
+
+        with torch.cuda.stream(s2):
+            for _ in range(3):
+                read_all()
+            read_ms = time_events(read_all, max(steps, 10), s2)
+        torch.cuda.synchronize()
+        stream = {"what": f"one-shot read of {per_layer_bytes} B from HBM (torch sum over "
+                          f"{DECODE_LAYERS} distinct buffers, back to back)",
+                  "us_per_read": round(read_ms * 1e3 / DECODE_LAYERS, 3),
+                  "gbs": round(DECODE_LAYERS * per_layer_bytes / (read_ms * 1e-3) / 1e9, 2)}
+        del bufs, outs
     out = {
         "metric": "packed-weight GB/s (decode M=1)",
         "value": round(gbs, 2),
@@ -328,7 +356,9 @@ def bench_decode(dev, steps: int, mx: bool = False):
         "us_per_layer_eager": round(eager_ms * 1e3 / DECODE_LAYERS, 3),
         "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
     }
-    del layers, g
+    if stream is not None:
+        out["stream_read_ceiling"] = stream
+    del layers
     torch.cuda.empty_cache()
     return out
 
