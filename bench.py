@@ -623,11 +623,28 @@ def control_lane(cfg, st, x16, off, sp, stream, iters: int):
     deq_bytes = sum(t.numel() * t.element_size() for t in (gp, ga, dp, da)) + \
         2 * (out["wgu"].numel() + out["wdn"].numel())
     floor_us = deq_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
+    # one dense fp16 library GEMM with the gate_up projection's flops (the
+    # routed rows times one expert's dequantised weights): what the matrix
+    # cores reach on this machine for a plain GEMM with real operands
+    xa = x16[rows]
+    wd = out["wgu"][0]
+
+    def dense():
+        out["dense"] = torch.matmul(xa, wd)
+
+    dense()
+    dense_ms = time_events(dense, iters, stream)
+    dense_flops = 2.0 * xa.shape[0] * xa.shape[1] * wd.shape[1]
     res = {"dequant_us": round(deq_ms * 1e3, 1), "dequant_hbm_floor_us": round(floor_us, 1),
            "dequant_bytes": deq_bytes, "gemm_swiglu_us": round(gemm_ms * 1e3, 1),
            "total_us": round((deq_ms + gemm_ms) * 1e3, 1),
            "total_at_dequant_floor_us": round(floor_us + gemm_ms * 1e3, 1),
-           "padded_rows_per_expert": mmax}
+           "padded_rows_per_expert": mmax,
+           "dense_fp16_gemm_same_flops": {
+               "shape": f"[{xa.shape[0]}x{xa.shape[1]}] x [{wd.shape[0]}x{wd.shape[1]}]",
+               "us": round(dense_ms * 1e3, 1),
+               "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1)}}
+    del out["dense"], xa
     del out["wgu"], out["wdn"], xp
     return res, out
 

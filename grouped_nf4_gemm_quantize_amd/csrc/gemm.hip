@@ -172,6 +172,13 @@ __device__ __forceinline__ void issue_b(const Src& s, int p, uint32_t bst, int w
     dma16(s.b_rsrc, s.b_off[i], (uint32_t)p * BK, bst + (wave * 4 + i) * 1024);
 }
 
+// Copies 2h and 2h + 1 of issue_b (h = 0, 1).
+__device__ __forceinline__ void issue_b_half(const Src& s, int p, uint32_t bst, int wave, int h) {
+#pragma unroll
+  for (int i = 2 * h; i < 2 * h + 2; ++i)
+    dma16(s.b_rsrc, s.b_off[i], (uint32_t)p * BK, bst + (wave * 4 + i) * 1024);
+}
+
 // The absmax of steps [4 grp, 4 grp + 4) into buffer `buf`.
 __device__ __forceinline__ void issue_abs(const Src& s, int grp, int buf, int wave) {
   dma16(s.s_rsrc, s.s_off, (uint32_t)grp * (kAbsGroup * 4),
@@ -343,13 +350,21 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
   }
 }
 
-// The k-loop of one tile.  After the barrier of step kb (every wave is done
-// reading step kb's activations and, for odd kb, the pair stage of steps
-// kb - 1 and kb) the wave issues batch kb, in this order:
+// The k-loop of one tile.  Batch kb holds the copies that step kb issues,
+// in this order:
 //   activations of step kb + 2 into A stage kb % 2;
 //   odd kb: codes of pair (kb + 3) / 2 into that pair stage;
 //   kb % 4 == 1: absmax group (kb + 3) / 4 -- buffer ((kb + 3) / 4) & 1 last
 //     served steps kb - 5 .. kb - 2, whose reads ended at the barrier of kb - 2.
+// The activations go out right after the barrier of step kb (every wave is
+// done reading step kb's activations).  For 4-bit codes the code and absmax
+// copies of batch kb go out during step kb + 1 instead, two code copies
+// after substep 0 and two (and the absmax) after substep 1, so that the
+// eight waves do not all queue their copies at the barrier while their
+// MFMAs wait behind them; their targets were last read before the barrier
+// of step kb (pair stage) or kb - 2 (absmax), and they still complete in
+// issue order before batch kb + 1.  The 8-bit and MXFP4 paths issue each
+// batch whole after the barrier.
 // Before substep 3 of step kb the activations of step kb + 1 (batch kb - 1,
 // issued first in it) must have landed: at most the copies issued after them
 // in batch kb - 1 may be pending -- 4 when kb - 1 is odd, +1 when it carried
@@ -396,8 +411,20 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
     const char* np = g_ring + (a ^ 1) * ASTAGE;        // step kb + 1's
     const char* nbp = g_ring + OFF_BR +
                       ((kW >= kWI8 ? (kb + 1) : ((kb + 1) >> 1)) & 1) * BPAIR;  // kb + 1's codes
+    // 4-bit codes: the code and absmax copies of batch kb - 1
+    const int pb = kb - 1;
+    const int ppn = (pb + 3) >> 1;
+    const bool defer_b = kW == kW4 && kb >= 1 && (pb & 1) && ppn <= last_pair;
     substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    if (defer_b) issue_b_half(src, ppn, ring + OFF_BR + (ppn & 1) * BPAIR, wave, 0);
     substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    if (defer_b) issue_b_half(src, ppn, ring + OFF_BR + (ppn & 1) * BPAIR, wave, 1);
+    if constexpr (kW == kW4) {
+      if (kb >= 1 && (pb & 3) == 1) {
+        const int grp = (pb + 3) >> 2;
+        if (grp <= (last >> 2)) issue_abs(src, grp, grp & 1, wave);
+      }
+    }
     substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
     if (kb >= last - 2) {
       // the batches of the last steps skip every copy past the end, so the
@@ -429,17 +456,14 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
         const int grp = (kb + 3) >> 2;
         if (grp <= (last >> 2)) issue_abs(src, grp, grp & 1, wave);
       }
-    } else if (kb & 1) {
-      const int pn = (kb + 3) >> 1;
-      if (pn <= last_pair) issue_b(src, pn, ring + OFF_BR + (pn & 1) * BPAIR, wave);
-      if constexpr (kW == kWMx) {
+    } else if constexpr (kW == kWMx) {
+      if (kb & 1) {
+        const int pn = (kb + 3) >> 1;
+        if (pn <= last_pair) issue_b(src, pn, ring + OFF_BR + (pn & 1) * BPAIR, wave);
         if ((kb & 7) == 5) {
           const int grp = (kb + 3) >> 3;
           if (grp <= (last >> 3)) issue_abs(src, grp, grp & 1, wave);
         }
-      } else if ((kb & 3) == 1) {
-        const int grp = (kb + 3) >> 2;
-        if (grp <= (last >> 2)) issue_abs(src, grp, grp & 1, wave);
       }
     }
     substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
