@@ -302,16 +302,18 @@ __device__ __forceinline__ void decode_b8(const StepRegs& r, f16x8 (&bf)[NT]) {
   }
 }
 
-// Substep S of a step: its MFMAs, with A fragments `af` and the raw table
-// words `d` of its weights already in registers (scaled here, one n-tile
-// ahead of use), while the A fragments and table words of the next substep
-// are read -- for S = 3 those of substep 0 of the next step, from the next
-// stage `nst` (valid once the barrier before substep 3 has passed).
+// Substep S of a step: its MFMAs, with A fragments `af` and its weights `bs`
+// (table words already scaled by the block's absmax) in registers, while the
+// A fragments and table words of the next substep are read -- for S = 3
+// those of substep 0 of the next step, from the next stage `nst` (valid once
+// the barrier before substep 3 has passed).  The next substep's weights are
+// scaled at the end, behind the MFMAs.  (8-bit codes are decoded and scaled
+// here, from the step's registers.)
 template <int S, int MTV, int kLora, bool kABf16, int kW>
 __device__ __forceinline__ void substep(const char* st, const char* nst, const char* nbst,
                                         int next_step, const Rd& rd,
                                         const StepRegs& cur, StepRegs& nxt, f16x8 (&af)[MT],
-                                        uint32_t (&d)[NT][4],
+                                        f16x8 (&bs)[NT],
                                         f32x16 (&acc)[MT][NT], f32x4& acc_u) {
   f16x8 af_n[MT];
   uint32_t dn[NT][4];
@@ -333,8 +335,12 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
     acc_u = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_u, 0, 0, 0);
   }
   f16x8 bf[NT];
-  if constexpr (kW >= kWI8) decode_b8<kW, S>(cur, bf);
-  else scale_b(cur, d, bf);
+  if constexpr (kW >= kWI8) {
+    decode_b8<kW, S>(cur, bf);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bf[nt] = bs[nt];
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -342,11 +348,11 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, const c
       acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nt], af[mt], acc[mt][nt], 0, 0, 0);
 #pragma unroll
   for (int mt = 0; mt < MTV; ++mt) af[mt] = af_n[mt];
+  // the next substep's weights scaled now, behind this substep's MFMAs, so
+  // that its first MFMA does not wait on the multiplies
   if constexpr (kW < kWI8) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[nt][j] = dn[nt][j];
+    if constexpr (S < 3) scale_b(cur, dn, bs);
+    else scale_b(nxt, dn, bs);
   }
 }
 
@@ -401,10 +407,14 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
   wait_vm_barrier<NA + kDmaB>();
   StepRegs cur, nxt;
   f16x8 af[MT];
-  uint32_t d[NT][4];
+  f16x8 bs[NT];
   load_step_regs<kW>(g_ring + OFF_BR, 0, rd, cur);
   load_a<MTV, kABf16>(g_ring, rd, 0, af);
-  if constexpr (kW < kWI8) lut_lookups(cur, 0, rd.lane_off, d);
+  if constexpr (kW < kWI8) {
+    uint32_t d[NT][4];
+    lut_lookups(cur, 0, rd.lane_off, d);
+    scale_b(cur, d, bs);
+  }
   for (int kb = 0; kb < nk; ++kb) {
     const int a = kb & 1;
     const char* sp = g_ring + a * ASTAGE;              // step kb's activations
@@ -415,9 +425,9 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
     const int pb = kb - 1;
     const int ppn = (pb + 3) >> 1;
     const bool defer_b = kW == kW4 && kb >= 1 && (pb & 1) && ppn <= last_pair;
-    substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    substep<0, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, bs, acc, acc_u);
     if (defer_b) issue_b_half(src, ppn, ring + OFF_BR + (ppn & 1) * BPAIR, wave, 0);
-    substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    substep<1, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, bs, acc, acc_u);
     if (defer_b) issue_b_half(src, ppn, ring + OFF_BR + (ppn & 1) * BPAIR, wave, 1);
     if constexpr (kW == kW4) {
       if (kb >= 1 && (pb & 3) == 1) {
@@ -425,7 +435,7 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
         if (grp <= (last >> 2)) issue_abs(src, grp, grp & 1, wave);
       }
     }
-    substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    substep<2, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, bs, acc, acc_u);
     if (kb >= last - 2) {
       // the batches of the last steps skip every copy past the end, so the
       // counts below no longer describe them: drain
@@ -466,7 +476,7 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
         }
       }
     }
-    substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, d, acc, acc_u);
+    substep<3, MTV, kLora, kABf16, kW>(sp, np, nbp, kb + 1, rd, cur, nxt, af, bs, acc, acc_u);
     cur = nxt;
   }
 }
