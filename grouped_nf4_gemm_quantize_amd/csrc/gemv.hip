@@ -72,6 +72,34 @@ __device__ __forceinline__ float dot_chunk(const uint32_t* lut, uint32_t lane_of
   return p;
 }
 
+// The table words of one chunk (32 codes -> 16 half2, unscaled), decoded
+// ahead of its activations; chunk_dot then matches dot_chunk exactly.
+__device__ __forceinline__ void decode_chunk(const uint32_t* lut, uint32_t lane_off, u32x4 q,
+                                             uint32_t (&d)[16]) {
+  const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t dw[4];
+    decode8<kCopies>(lut, lane_off, qq[w], dw);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) d[4 * w + t] = dw[t];
+  }
+}
+
+__device__ __forceinline__ float chunk_dot(const uint32_t (&d)[16], const _Float16* act) {
+  const u32x4* a4 = reinterpret_cast<const u32x4*>(act);
+  float p = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const u32x4 av = a4[w];
+    const uint32_t aa[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      p = __builtin_amdgcn_fdot2(u32_as_half2(d[4 * w + t]), u32_as_half2(aa[t]), p, false);
+  }
+  return p;
+}
+
 __device__ __forceinline__ float silu_g(float z) {
   return z / (1.0f + expf(-z));
 }
@@ -387,6 +415,16 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
 
   // ---- grid-wide exchange of h: every workgroup reads all k*I words until
   // each carries this launch's tag (a bounded wait), keeping the fp16 value
+  // the first row's first kDnFirst chunks are decoded (table words, not yet
+  // scaled) while the first polls are in flight: after the exchange only
+  // their dot products with h remain
+  uint32_t dd[kDnFirst][16];
+  bool decoded = false;
+  auto predecode = [&]() {
+#pragma unroll
+    for (int m = 0; m < kDnFirst; ++m) decode_chunk(s_lut, lane_off, qd[m], dd[m]);
+    decoded = true;
+  };
   bool ok = true;
   for (int i0 = tid; i0 < items; i0 += kThreads * kHPer) {
     uint64_t v[kHPer];
@@ -399,6 +437,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
 #pragma unroll
       for (int t = 0; t < kHPer; ++t)
         if (pending & (1u << t)) v[t] = load_agent(hx + i0 + t * kThreads);
+      if (!decoded) predecode();
 #pragma unroll
       for (int t = 0; t < kHPer; ++t) {
         if ((pending & (1u << t)) && (v[t] & ~0xffffull) == tag) {
@@ -409,6 +448,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
     }
     ok = ok && pending == 0;
   }
+  if (!decoded) predecode();  // a workgroup with no word to poll
   if (!ok) s_fail = 1;
   __syncthreads();
   const bool failed = s_fail != 0;
@@ -418,13 +458,14 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(GemvArgs g) {
   if (tid == 0 && (blockIdx.x == 0 || failed)) store_agent(gen_p, gen + 1);
 
   // ---- down rows
-  for (; n < H; n += nw) {
+  for (bool first = true; n < H; n += nw, first = false) {
     float acc = 0.f;
 #pragma unroll
     for (int m = 0; m < kMaxChunksPerLane; ++m) {
       if (m < kDnFirst || 64 * m < total) {  // compile-time or wave-uniform
-        const float p =
-            dot_chunk(s_lut, lane_off, qd[m], s_h + h_off[m]) * scale_value(sd[m], mx);
+        const float dot = m < kDnFirst && first ? chunk_dot(dd[m], s_h + h_off[m])
+                                                : dot_chunk(s_lut, lane_off, qd[m], s_h + h_off[m]);
+        const float p = dot * scale_value(sd[m], mx);
         acc += dvalid[m] ? p : 0.f;
       }
     }
