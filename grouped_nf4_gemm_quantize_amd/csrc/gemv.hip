@@ -5,33 +5,37 @@
 // "Inference": the single-token decode fast path uses a fused 4-bit GEMV).  HBM
 // bandwidth on the NF4 codes + absmax is the roofline, and with only ~21 MB
 // per layer the time is set by the chain of dependent memory round trips:
-// the router logits, then the weights.  So one kernel does the whole layer
-// and issues every weight load -- gate/up rows and down rows alike -- as soon
-// as the routing is known:
+// the router logits, then the weights.  So one kernel does the whole layer,
+// and each of its waves:
 //
-//   1. every wave routes the token itself (a top-k over the E logits costs a
-//      few hundred cycles, cheaper than any exchange);
-//   2. it issues the loads of its (slot j, column i) gate/up items -- the gate
-//      row i and the up row I+i of expert ids[j] -- and of its down output
-//      row n, whose K is the concatenation of the k experts' I inputs (so the
-//      combine over the slots is part of the dot product);
-//   3. while they are in flight it stages x as fp16 and builds the decode
-//      table, then computes h[j, i] = w_j * silu(gate) * up (fp32) and
-//      publishes it;
-//   4. a grid-wide exchange of h: each workgroup writes its h values, then its
-//      flag; every workgroup waits for all flags (a bounded wait), then reads
-//      the whole h (fp16 in LDS) and finishes its down rows, whose weights
-//      arrived meanwhile.
+//   1. loads the logits, x and the exchange's generation word, and (with its
+//      workgroup) builds the decode table while they are in flight;
+//   2. routes the token itself (a top-k over the E logits costs a few
+//      hundred cycles, cheaper than any exchange);
+//   3. issues the loads of its (slot j, column i) gate/up items -- the gate
+//      row i and the up row I+i of expert ids[j] -- stages x as fp16 and
+//      computes h[j, i] = w_j * silu(gate) * up (fp32, rounded once to fp16),
+//      which it publishes;
+//   4. issues the loads of its down output row n, whose K is the
+//      concatenation of the k experts' I inputs (so the combine over the
+//      slots is part of the dot product) -- after its h, so the gate/up bytes
+//      the exchange waits for are not queued behind them;
+//   5. takes part in a grid-wide exchange of h: every workgroup reads all
+//      k*I values (a bounded wait), decoding its first down chunks while the
+//      first reads are in flight, and finishes its down rows.
 //
-// The exchange needs every workgroup resident at once: the grid is at most one
-// workgroup per compute unit, and each workgroup fits on one.  Its state is
-// a generation word and one flag per workgroup in the caller's workspace; the
-// flag value of a launch is a hash of (generation + 1, workspace address), so
-// stale or uninitialised workspace bytes never match it (the workspace needs
-// no clearing), and the launch advances the generation once every flag is
-// seen.  A wait that exceeds its bound writes NaN to the workgroup's outputs
-// and advances the generation, so a failure is loud and does not poison the
-// next call.
+// Each h value travels as one 64-bit word: a 48-bit tag | the fp16 bits,
+// stored and loaded whole at agent scope, so a word with this launch's tag
+// holds this launch's value and no fence or flag is needed.  The tag is a
+// hash of (generation + 1, workspace address); the generation word sits in
+// the caller's workspace, every workgroup reads it before it publishes
+// anything, and workgroup 0 advances it once every word was seen, so stale
+// or uninitialised workspace bytes never match (the workspace needs no
+// clearing).  The exchange needs every workgroup resident at once: the grid
+// is at most one workgroup per compute unit, and each workgroup fits on one.
+// A wait that exceeds its bound writes NaN to the workgroup's outputs and
+// advances the generation, so a failure is loud and does not poison the next
+// call.
 //
 // Split-K inside a wave: lane l takes the 32-weight chunks l, l+64, ... of a
 // row (16 packed bytes = one 16-byte load; a chunk is half of one 64-block so
