@@ -228,11 +228,25 @@ __global__ __launch_bounds__(kFuseThreads) void route_scan_scatter_kernel(
   __shared__ int32_t s_tot[kFuseThreads];
   __shared__ int32_t s_pre[kFuseThreads];
   __shared__ int32_t s_base[kFuseThreads];
+  __shared__ uint32_t s_mask[kFuseThreads];  // this chunk's mask per expert
   __shared__ int32_t s_wsum[kFuseThreads / 64];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int64_t chunk = blockIdx.x;
   const int64_t nchunks = (T + kRouteChunk - 1) / kRouteChunk;
+  const int64_t t0 = chunk * kRouteChunk;
+  int64_t t1 = t0 + kRouteChunk;
+  if (t1 > T) t1 = T;
+  // this chunk's pair ids go out first (the scatter needs them after the
+  // scan; at most kRouteChunk * k pairs, two per thread)
+  constexpr int kPairsPerThread = kRouteChunk * kMaxTopK / kFuseThreads;
+  static_assert(kPairsPerThread * kFuseThreads == kRouteChunk * kMaxTopK, "pair prefetch");
+  int32_t ids_pre[kPairsPerThread];
+#pragma unroll
+  for (int u = 0; u < kPairsPerThread; ++u) {
+    const int64_t p = t0 * k + t + (int64_t)u * kFuseThreads;
+    ids_pre[u] = p < t1 * k ? topk_ids[p] : 0;
+  }
   int Ep = 1;
   while (Ep < E) Ep <<= 1;
   const int groups = kFuseThreads / Ep;
@@ -253,6 +267,8 @@ __global__ __launch_bounds__(kFuseThreads) void route_scan_scatter_kernel(
       const int32_t n = __popc(mv[u]);
       tot += n;
       pre += (cb + u < chunk) ? n : 0;
+      // the group holding this chunk: one thread per expert
+      if (cb + u == chunk && cb + u < c1 && e < E) s_mask[e] = mv[u];
     }
   }
   s_tot[t] = tot;
@@ -286,17 +302,18 @@ __global__ __launch_bounds__(kFuseThreads) void route_scan_scatter_kernel(
     }
   }
   __syncthreads();
-  const int64_t t0 = chunk * kRouteChunk;
-  int64_t t1 = t0 + kRouteChunk;
-  if (t1 > T) t1 = T;
-  for (int64_t p = t0 * k + t; p < t1 * k; p += kFuseThreads) {
-    const int64_t tk = p / k;
-    const int ex = topk_ids[p];
-    const uint32_t m = chunk_masks[chunk * E + ex];
-    const uint32_t below = (1u << (uint32_t)(tk - t0)) - 1u;
-    const int32_t rank = s_base[ex] + __popc(m & below);
-    sorted_pair[rank] = (int32_t)p;
-    if (pair_pos != nullptr) pair_pos[p] = rank;
+#pragma unroll
+  for (int u = 0; u < kPairsPerThread; ++u) {
+    const int64_t p = t0 * k + t + (int64_t)u * kFuseThreads;
+    if (p < t1 * k) {
+      const int64_t tk = p / k;
+      const int ex = ids_pre[u];
+      const uint32_t m = s_mask[ex];
+      const uint32_t below = (1u << (uint32_t)(tk - t0)) - 1u;
+      const int32_t rank = s_base[ex] + __popc(m & below);
+      sorted_pair[rank] = (int32_t)p;
+      if (pair_pos != nullptr) pair_pos[p] = rank;
+    }
   }
 }
 
