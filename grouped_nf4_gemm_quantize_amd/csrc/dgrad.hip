@@ -40,7 +40,8 @@
 //   B (codes): 64 stack rows x 256 B (the tile's 512 columns), 16-byte chunk
 //     c of row n at c ^ f(n), f(n) = (n & 7) | 8 * ((n >> 5) & 1): the 64
 //     lanes of one code-word read (16 rows, 4 words) hit 64 different banks;
-//   S (absmax): [wave][64 rows] fp32, one 4-byte copy per wave.
+//   S (absmax): [64 rows][the tile's 8 blocks] fp32, one 4-byte copy per
+//     wave (8 rows x 32 contiguous bytes: 8 row segments per copy).
 // The kernel waits with a counted s_waitcnt on the vector-memory counter
 // (copies complete in issue order) and s_barrier, as the forward kernel.
 //
@@ -73,7 +74,7 @@ constexpr int BN = NWAVES * BNW;   // 512 output columns per tile
 constexpr int kCopies = 32;
 constexpr int OFF_A = 0;                        // 128 rows x 128 B
 constexpr int OFF_B = BM * BK * 2;              // 64 stack rows x 256 B
-constexpr int OFF_S = OFF_B + BK * (BN / 2);    // [8 waves][64 rows] fp32
+constexpr int OFF_S = OFF_B + BK * (BN / 2);    // [64 rows][8 blocks] fp32
 constexpr int STAGE = OFF_S + NWAVES * BK * 4;  // 34816 B
 constexpr int NSTAGE = 3;
 constexpr int RING = NSTAGE * STAGE;            // 104448 B
@@ -186,14 +187,29 @@ __device__ __forceinline__ u32x4 load_sc(int par, const DRd& rd, int s) {
                                           rd.sc + s * 16);
 }
 
+// Decoded table words times the rows' absmax: the weight operands.
+__device__ __forceinline__ void scale_b(const uint32_t (&d)[NT][4], const u32x4 sc,
+                                        f16x8 (&bf)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const u32x4 v = {half2_as_u32(u32_as_half2(d[nt][0]) * u32_as_half2(sc.x)),
+                     half2_as_u32(u32_as_half2(d[nt][1]) * u32_as_half2(sc.y)),
+                     half2_as_u32(u32_as_half2(d[nt][2]) * u32_as_half2(sc.z)),
+                     half2_as_u32(u32_as_half2(d[nt][3]) * u32_as_half2(sc.w))};
+    bf[nt] = as_f16x8(v);
+  }
+}
+
 // One substep: MFMAs of substep S with the operands prepared in registers,
 // while the operands of the next substep are prepared -- for S = 3, substep
 // 0 of the next step, from the next stage (valid once the barrier before
-// substep 3 has passed), after converting that step's absmax.
+// substep 3 has passed), after converting that step's absmax.  The next
+// weights are scaled after this substep's MFMAs are issued, so no MFMA
+// waits on the multiplies.
 template <int S, int MTV, bool kABf16>
 __device__ __forceinline__ void substep(const char* st, const char* nst, int par, int wave,
                                         int lane, const DRd& rd, uint32_t (&cw)[4][NT],
-                                        f16x8 (&af)[MT], uint32_t (&d)[NT][4], u32x4& sc,
+                                        f16x8 (&af)[MT], f16x8 (&bf)[NT],
                                         f32x16 (&acc)[MT][NT]) {
   f16x8 af_n[MT];
   uint32_t dn[NT][4];
@@ -203,21 +219,12 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int par
     lookups(cw[S + 1], rd, dn);
     sc_n = load_sc(par, rd, S + 1);
   } else {
-    const float sv = *reinterpret_cast<const float*>(nst + OFF_S + wave * 256 + lane * 4);
+    const float sv = *reinterpret_cast<const float*>(nst + OFF_S + lane * 32 + wave * 4);
     d_sc[par ^ 1][wave][lane] = (_Float16)sv;
     load_codes(nst, rd, cw);
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
     lookups(cw[0], rd, dn);
     sc_n = load_sc(par ^ 1, rd, 0);
-  }
-  f16x8 bf[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const u32x4 v = {half2_as_u32(u32_as_half2(d[nt][0]) * u32_as_half2(sc.x)),
-                     half2_as_u32(u32_as_half2(d[nt][1]) * u32_as_half2(sc.y)),
-                     half2_as_u32(u32_as_half2(d[nt][2]) * u32_as_half2(sc.z)),
-                     half2_as_u32(u32_as_half2(d[nt][3]) * u32_as_half2(sc.w))};
-    bf[nt] = as_f16x8(v);
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -226,11 +233,7 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int par
       acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nt], af[mt], acc[mt][nt], 0, 0, 0);
 #pragma unroll
   for (int mt = 0; mt < MTV; ++mt) af[mt] = af_n[mt];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) d[nt][j] = dn[nt][j];
-  sc = sc_n;
+  scale_b(dn, sc_n, bf);
 }
 
 // The contraction loop of one tile.  Batch kb (the copies of step kb) goes
@@ -254,28 +257,31 @@ __device__ __forceinline__ void kloop(const DSrc& src, int nk, const DRd& rd, in
 
   uint32_t cw[4][NT];
   f16x8 af[MT];
-  uint32_t d[NT][4];
+  f16x8 bf[NT];
   {
-    const float sv = *reinterpret_cast<const float*>(d_ring + OFF_S + wave * 256 + lane * 4);
+    const float sv = *reinterpret_cast<const float*>(d_ring + OFF_S + lane * 32 + wave * 4);
     d_sc[0][wave][lane] = (_Float16)sv;
   }
   load_codes(d_ring, rd, cw);
   load_a<MTV, kABf16>(d_ring, rd, 0, af);
-  lookups(cw[0], rd, d);
-  u32x4 sc = load_sc(0, rd, 0);
+  {
+    uint32_t d[NT][4];
+    lookups(cw[0], rd, d);
+    scale_b(d, load_sc(0, rd, 0), bf);
+  }
   int sidx = 0;  // kb % 3
   for (int kb = 0; kb < nk; ++kb) {
     const int nidx = sidx == 2 ? 0 : sidx + 1;
     const char* st = d_ring + sidx * STAGE;
     const char* nst = d_ring + nidx * STAGE;
     const int par = kb & 1;
-    substep<0, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
-    substep<1, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
-    substep<2, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
+    substep<0, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
+    substep<1, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
+    substep<2, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
     if (kb >= last - 1) wait_vm_barrier<0>();
     else wait_vm_barrier<kDma>();
     if (kb + 3 <= last) issue_step(src, kb + 3, ring + sidx * STAGE, wave);
-    substep<3, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, d, sc, acc);
+    substep<3, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
     sidx = nidx;
   }
 }
@@ -394,7 +400,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
     }
     const int mtv = (rows_valid + 31) >> 5;
     const int cbase = n_idx * BN;
-    const int kb_w = min(cbase / 64 + wave, KB - 1);  // this wave's absmax block (clamped)
 
     DSrc src;
     src.a_rsrc = a_rsrc;
@@ -423,7 +428,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
       const int c = (lane & 15) ^ f;
       src.b_off[i] = (uint32_t)row * (uint32_t)(K / 2) + (uint32_t)(cbase / 2 + c * 16);
     }
-    src.s_off = ((uint32_t)lane * (uint32_t)KB + (uint32_t)kb_w) * 4u;
+    // absmax: wave w copies stack rows 8w..8w+7 of the step, the tile's 8
+    // blocks of each (32 contiguous bytes per row); blocks past KB (a partial
+    // last tile) read values only waves with no live columns use
+    src.s_off = ((uint32_t)(wave * 8 + (lane >> 3)) * (uint32_t)KB +
+                 (uint32_t)(cbase / 64 + (lane & 7))) * 4u;
 
     const int par = r & 1;
     if (tid < BM) {
