@@ -367,9 +367,10 @@ def bench_decode(dev, steps: int, mx: bool = False):
 
 
 def bench_backward(name: str, dev, steps: int):
-    """The QLoRA training backward of one layer (route, recomputed gate_up,
-    down dgrad with the SwiGLU backward, gate_up dgrad, combine, adapter
-    gradients) and its two dgrad kernels timed alone on the same routing."""
+    """The QLoRA training backward of one layer (route, down dgrad, gate_up
+    recomputed with the SwiGLU backward as its epilogue, gate_up dgrad,
+    combine, adapter gradients) and its three grouped kernels timed alone on
+    the same routing."""
     import torch
 
     from grouped_nf4_gemm_quantize_amd import binding, synth
@@ -401,7 +402,9 @@ def bench_backward(name: str, dev, steps: int):
         step()
     bwd_ms = time_events(step, max(steps, 5), stream)
 
-    # the dgrad kernels alone, on this layer's routing and recomputed G
+    # the backward's three grouped kernels alone (without adapters), on this
+    # layer's routing: the down dgrad (dh), the gate_up GEMM recomputed with
+    # the SwiGLU backward as its epilogue (dG), the gate_up dgrad (dX)
     fws = torch.empty(binding.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, r),
                       dtype=torch.uint8, device=dev)
     binding.moe_forward(x, lg, cfg.k, gp, ga, dp, da, glo, dlo, cfg.renormalize,
@@ -411,26 +414,29 @@ def bench_backward(name: str, dev, steps: int):
     P = cfg.P
     sp = fws[ptr["sorted_pair"] - base: ptr["sorted_pair"] - base + 4 * P].view(torch.int32)
     off = fws[ptr["offsets"] - base: ptr["offsets"] - base + 4 * (cfg.E + 1)].view(torch.int32)
-    wts = fws[ptr["w"] - base: ptr["w"] - base + 4 * P].view(torch.float32)
     x16 = x.to(torch.float16)
-    G = torch.empty((P, 2 * cfg.I), dtype=torch.float16, device=dev)
-    binding.grouped_gemm(x16, gp, ga, off, P, gather=sp, gather_div=cfg.k, out=G)
-    dG = torch.empty_like(G)
+    dH = torch.empty((P, cfg.I), dtype=torch.float16, device=dev)
+    dG = torch.empty((P, 2 * cfg.I), dtype=torch.float16, device=dev)
     dXp = torch.empty((P, cfg.H), dtype=torch.float16, device=dev)
 
     dy16 = dy.to(torch.float16)  # the layer backward converts dy once, as here
 
     def down_dgrad():
-        binding.grouped_dgrad(dy16, dp, da, off, P, gather=sp, gather_div=cfg.k, g_pre=G,
-                              row_scale=wts, out=dG)
+        binding.grouped_dgrad(dy16, dp, da, off, P, gather=sp, gather_div=cfg.k, out=dH)
+
+    def recompute():
+        binding.grouped_gemm_swiglu_bwd(x16, gp, ga, off, P, dH, gather=sp, gather_div=cfg.k,
+                                        out=dG)
 
     def gate_up_dgrad():
         binding.grouped_dgrad(dG, gp, ga, off, P, scatter=sp, out=dXp)
 
     for _ in range(2):
         down_dgrad()
+        recompute()
         gate_up_dgrad()
     dn_ms = time_events(down_dgrad, max(steps, 10), stream)
+    rc_ms = time_events(recompute, max(steps, 10), stream)
     gu_ms = time_events(gate_up_dgrad, max(steps, 10), stream)
     phi = float(P) * cfg.H * cfg.I
     grad_flops = 6.0 * phi           # the two dgrads
@@ -448,13 +454,15 @@ def bench_backward(name: str, dev, steps: int):
         "us_per_backward": round(bwd_ms * 1e3, 2),
         "tflops_gradient": round(grad_flops / (bwd_ms * 1e-3) / 1e12, 2),
         "tflops_executed": round(exec_flops / (bwd_ms * 1e-3) / 1e12, 2),
-        "down_dgrad_swiglu_bwd_us": round(dn_ms * 1e3, 2),
+        "down_dgrad_us": round(dn_ms * 1e3, 2),
         "down_dgrad_tflops": round(2.0 * phi / (dn_ms * 1e-3) / 1e12, 2),
+        "recompute_swiglu_bwd_us": round(rc_ms * 1e3, 2),
+        "recompute_swiglu_bwd_tflops": round(4.0 * phi / (rc_ms * 1e-3) / 1e12, 2),
         "gate_up_dgrad_us": round(gu_ms * 1e3, 2),
         "gate_up_dgrad_tflops": round(4.0 * phi / (gu_ms * 1e-3) / 1e12, 2),
         "gate_up_dgrad_frac_peak": round(4.0 * phi / (gu_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
     }
-    del st, gp, ga, dp, da, G, dG, dXp, ws, fws
+    del st, gp, ga, dp, da, dH, dG, dXp, ws, fws
     torch.cuda.empty_cache()
     return out
 

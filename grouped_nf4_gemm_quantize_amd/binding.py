@@ -91,6 +91,10 @@ _SIGNATURES = {
                                          _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                          ctypes.POINTER(LoraStruct), ctypes.POINTER(LoraStruct),
                                          _c_vp, _c_int, _c_vp, _c_size, _c_vp]),
+    "grouped_nf4_gemm_swiglu_bwd": (_c_int, [_c_vp, _c_i64, _c_vp, _c_int, _c_vp, _c_vp, _c_vp,
+                                             _c_int, _c_i64, _c_i64, _c_i64,
+                                             ctypes.POINTER(LoraStruct), _c_vp, _c_vp, _c_vp,
+                                             _c_vp]),
     "grouped_nf4_gemm_dgrad": (_c_int, _DGRAD_ARGS),
     "grouped_nbit_gemm_dgrad": (_c_int, [_c_int] + _DGRAD_ARGS),
     "moe_expert_backward_workspace": (_c_size, [_c_i64, _c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -293,6 +297,24 @@ def grouped_gemm(a, packed, absmax, offsets, P: int, gather=None, gather_div: in
         _check(lib.grouped_nf4_gemm(*args))
     else:
         _check(lib.grouped_nbit_gemm(_qt(quant_type), *args))
+    return out
+
+
+def grouped_gemm_swiglu_bwd(a, packed, absmax, offsets, P: int, dh, gather=None,
+                            gather_div: int = 1, lora=None, out=None, h_out=None):
+    """The gate_up GEMM recomputed with the SwiGLU backward as its epilogue
+    (see grouped_nf4_gemm_swiglu_bwd in include/nf4moe.h): returns
+    ``out`` = [dh * up * silu'(gate) | dh * silu(gate)], fp16 [P, N]; pass an
+    fp16 ``h_out`` [P, N/2] to get h = silu(gate) * up as well."""
+    torch = _torch()
+    E, N, K2 = packed.shape
+    if out is None:
+        out = torch.empty((P, N), dtype=torch.float16, device=a.device)
+    ls = make_lora(*lora) if lora is not None else None
+    _check(load().grouped_nf4_gemm_swiglu_bwd(
+        _ptr(a), a.shape[0], _ptr(gather), gather_div, _ptr(packed), _ptr(absmax),
+        _ptr(offsets), E, P, N, K2 * 2, ctypes.byref(ls) if ls is not None else None, _ptr(dh),
+        _ptr(out), _ptr(h_out), _stream(a.device)))
     return out
 
 

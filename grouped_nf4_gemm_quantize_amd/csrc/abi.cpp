@@ -408,7 +408,8 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
                        const int32_t* expert_offsets, int E, int64_t P, int64_t N, int64_t K,
                        const nf4moe_lora* lora, int epilogue,
                        const float* row_scale, const int32_t* scatter, void* out,
-                       int out_dtype, int qt, hipStream_t stream) {
+                       int out_dtype, int qt, hipStream_t stream,
+                       const void* swiglu_bwd_dh = nullptr, void* swiglu_bwd_h = nullptr) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
@@ -432,7 +433,9 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
     g.lora_scale = lora->scale;
     g.lora_bf16 = lora->dtype == NF4MOE_BF16;
   }
-  g.swiglu = epilogue == NF4MOE_EPI_SWIGLU;
+  g.swiglu = epilogue == NF4MOE_EPI_SWIGLU || swiglu_bwd_dh != nullptr;
+  g.dh = swiglu_bwd_dh;
+  g.h_out = swiglu_bwd_h;
   g.row_scale = row_scale;
   g.scatter = scatter;
   g.out = out;
@@ -519,6 +522,32 @@ int grouped_nbit_gemm(int quant_type, const void* a, int a_dtype, int64_t a_rows
   return gemm_impl(quant_type, a, a_dtype, a_rows, gather, gather_div, packed, absmax,
                    expert_offsets, E, P, N, K, lora, epilogue, row_scale, scatter, out,
                    out_dtype, stream);
+}
+
+int grouped_nf4_gemm_swiglu_bwd(const void* a, int64_t a_rows, const int32_t* gather,
+                                int gather_div, const uint8_t* packed, const float* absmax,
+                                const int32_t* expert_offsets, int E, int64_t P, int64_t N,
+                                int64_t K, const nf4moe_lora* lora, const void* dh, void* out,
+                                void* h_out, void* stream) {
+  if (dh == nullptr) return fail(NF4MOE_EINVAL, "dh must be non-null");
+  if (!aligned(dh, 16) || !aligned(h_out, 16))
+    return fail(NF4MOE_EINVAL, "misaligned buffer (dh and h_out need 16 bytes)");
+  if (a == nullptr || packed == nullptr || absmax == nullptr || expert_offsets == nullptr ||
+      out == nullptr)
+    return fail(NF4MOE_EINVAL, "a, packed, absmax, expert_offsets and out must be non-null");
+  // the shape, dtype, alignment and size checks of the SwiGLU GEMM
+  int st = gemm_impl(kQtNF4, a, NF4MOE_F16, a_rows, gather, gather_div, packed, absmax,
+                     expert_offsets, E, /*P=*/0, N, K, lora, NF4MOE_EPI_SWIGLU, nullptr,
+                     nullptr, out, NF4MOE_F16, stream);
+  if (st != NF4MOE_OK) return st;
+  if (P < 0) return fail(NF4MOE_EINVAL, "P must be >= 0");
+  if (P >= INT32_MAX) return fail(NF4MOE_EOVERFLOW, "P too large for 32-bit row indexing");
+  if (P == 0) return ok();
+  st = gemm_common(a, NF4MOE_F16, a_rows, gather, gather_div, packed, absmax, expert_offsets,
+                   E, P, N, K, lora, NF4MOE_EPI_SWIGLU, nullptr, nullptr, out, NF4MOE_F16,
+                   kQtNF4, (hipStream_t)stream, dh, h_out);
+  if (st != NF4MOE_OK) return st;
+  return ok();
 }
 
 size_t moe_expert_forward_workspace(int64_t T, int H, int I, int E, int k, int r) {
@@ -1008,10 +1037,10 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     dyh = ws + L.dy16;
   }
 
-  // 2. recompute the gate_up pre-activation G = x W_gu^T (+ LoRA), fp16.
-  //    A_gu goes to fp16 once here (the adapter passes below read it too);
-  //    bf16 adapters get an fp16 B_gu as well, so the recompute's k-loop
-  //    reads fp16 adapter rows (the same rounding the GEMM would apply)
+  // 2. the gate_up adapter of the recompute: A_gu goes to fp16 once here
+  //    (the adapter passes below read it too); bf16 adapters get an fp16
+  //    B_gu as well, so the recompute's k-loop reads fp16 adapter rows (the
+  //    same rounding the GEMM would apply)
   nf4moe_lora gu16{};
   const nf4moe_lora* gu_rc = gu_lora;
   if (gu_lora) {
@@ -1033,45 +1062,49 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
       gu_rc = &gu16;
     }
   }
-  st = gemm_common(xa, NF4MOE_F16, T, sorted, k, gu_packed, gu_absmax, offs, E, P,
-                   2 * (int64_t)I, H, gu_rc, NF4MOE_EPI_NONE, nullptr, nullptr, G,
-                   NF4MOE_F16, qt, s);
-  if (st != NF4MOE_OK) return st;
 
-  // 3. down adapter: h, u = h A_dn^T, then one pass over dy for
-  //    v' = dy B_dn (without the routing weight) and dB_dn = s sum w dy u^T
+  // 3. with a down adapter: A_dn and B_dn to fp16 (B_dn transposed), then
+  //    v' = dy B_dn (without the routing weight), one projection pass
   if (dn_lora) {
     const int bf = dn_lora->dtype == NF4MOE_BF16;
-    err = launch_swiglu_rows(G, P, I, hbuf, cus, s);
-    if (err != hipSuccess) return hip_fail(err, "SwiGLU launch");
     err = launch_lora_to_f16(dn_lora->A, bf, 0, E, I, r, a16_dn, cus, s);
     if (err == hipSuccess) err = launch_lora_to_f16(dn_lora->B, bf, 1, E, H, r, bt_dn, cus, s);
     if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
-    st = lora_pass(hbuf, 0, nullptr, 1, offs, E, P, I, r, a16_dn, u_dn, nullptr, nullptr,
-                   nullptr, nullptr, nullptr, 0.f, 0, cus, s);
+    st = lora_pass(dyh, 0, sorted, k, offs, E, P, H, r, bt_dn, v_dn, nullptr, nullptr, nullptr,
+                   nullptr, nullptr, 0.f, 0, cus, s);
     if (st != NF4MOE_OK) return st;
-    st = lora_pass(dyh, 0, sorted, k, offs, E, P, H, r, bt_dn, v_dn, wts, sorted, u_dn,
+  }
+
+  // 4. dH = dy_t W_dn (+ s v' A_dn) for a unit routing weight, fp16 (in
+  //    G's space: G itself never goes to memory).  Everything downstream is
+  //    linear in w, so w is applied later as a row scale: stored fp16
+  //    gradients then keep their precision however small a pair's weight is.
+  _Float16* dH = G;
+  st = dgrad_common(dyh, NF4MOE_F16, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
+                    NF4MOE_EPI_NONE, nullptr, NF4MOE_F16, nullptr, nullptr, nullptr,
+                    dn_lora ? v_dn : nullptr, dn_lora, dH, NF4MOE_F16, qt, s);
+  if (st != NF4MOE_OK) return st;
+
+  // 5. G = x W_gu^T (+ LoRA) recomputed with the SwiGLU backward in its
+  //    epilogue: dG1 = [dh * up * silu'(gate) | dh * silu(gate)] in fp16,
+  //    and h = silu(gate) * up as well when the down adapter needs it
+  st = gemm_common(xa, NF4MOE_F16, T, sorted, k, gu_packed, gu_absmax, offs, E, P,
+                   2 * (int64_t)I, H, gu_rc, NF4MOE_EPI_SWIGLU, nullptr, nullptr, dG,
+                   NF4MOE_F16, qt, s, dH, dn_lora ? hbuf : nullptr);
+  if (st != NF4MOE_OK) return st;
+
+  // 6. the down adapter's gradients: one pass over h for u = h A_dn^T and
+  //    dA_dn = s sum w v' h^T, one over dy for dB_dn = s sum w dy u^T
+  if (dn_lora) {
+    st = lora_pass(hbuf, 0, nullptr, 1, offs, E, P, I, r, a16_dn, u_dn, wts, sorted, v_dn,
+                   part, d_dn_A, dn_lora->scale, 1, cus, s);
+    if (st != NF4MOE_OK) return st;
+    st = lora_pass(dyh, 0, sorted, k, offs, E, P, H, r, nullptr, nullptr, wts, sorted, u_dn,
                    part, d_dn_B, dn_lora->scale, 0, cus, s);
     if (st != NF4MOE_OK) return st;
   }
 
-  // 4. dG1 = SwiGLU backward of dy_t W_dn (+ LoRA) for a unit routing
-  //    weight, fp16.  Everything downstream is linear in w, so w is applied
-  //    later as a row scale: stored fp16 gradients then keep their precision
-  //    however small a pair's weight is.
-  st = dgrad_common(dyh, NF4MOE_F16, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
-                    NF4MOE_EPI_SWIGLU_BWD, G, NF4MOE_F16, nullptr, nullptr, nullptr,
-                    dn_lora ? v_dn : nullptr, dn_lora, dG, NF4MOE_F16, qt, s);
-  if (st != NF4MOE_OK) return st;
-
-  // 5. dA_dn = s sum w v' h^T
-  if (dn_lora) {
-    st = lora_pass(hbuf, 0, nullptr, 1, offs, E, P, I, r, nullptr, nullptr, wts, sorted, v_dn,
-                   part, d_dn_A, dn_lora->scale, 1, cus, s);
-    if (st != NF4MOE_OK) return st;
-  }
-
-  // 6. gate_up adapter: u = x A_gu^T, then one pass over dG1 for
+  // 7. gate_up adapter: u = x A_gu^T, then one pass over dG1 for
   //    v1 = dG1 B_gu and dB_gu = s sum w dG1 u^T
   if (gu_lora) {
     const int bf = gu_lora->dtype == NF4MOE_BF16;
@@ -1085,7 +1118,7 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     if (st != NF4MOE_OK) return st;
   }
 
-  // 7. per-pair input gradients dG W_gu (+ LoRA) in pair order, then the sum
+  // 8. per-pair input gradients dG W_gu (+ LoRA) in pair order, then the sum
   //    over each token's k pairs
   // (the routing weight w of each pair applied here as the row scale)
   st = dgrad_common(dG, NF4MOE_F16, P, nullptr, 1, gu_packed, gu_absmax, offs, E, P,
@@ -1095,7 +1128,7 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
   err = launch_combine(dXp, nullptr, T, k, H, dx, dx_dtype, cus, s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
 
-  // 8. dA_gu = s sum w v1 x^T
+  // 9. dA_gu = s sum w v1 x^T
   if (gu_lora) {
     st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, nullptr, nullptr, wts, sorted, v_gu,
                    part, d_gu_A, gu_lora->scale, 1, cus, s);

@@ -286,47 +286,6 @@ __device__ __forceinline__ void kloop(const DSrc& src, int nk, const DRd& rd, in
   }
 }
 
-__device__ __forceinline__ float sigmoid_f(float z) {
-  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-}
-
-template <bool kBf16>
-__device__ __forceinline__ void unpack8(const u32x4 w, float (&v)[8]) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (kBf16) {
-      v[2 * i] = bf16_bits_to_f32(ws[i] & 0xffffu);
-      v[2 * i + 1] = bf16_bits_to_f32(ws[i] >> 16);
-    } else {
-      const f16x2 h = u32_as_half2(ws[i]);
-      v[2 * i] = (float)h.x;
-      v[2 * i + 1] = (float)h.y;
-    }
-  }
-}
-
-template <int kOut>
-__device__ __forceinline__ void store8(void* out, int64_t idx, const float (&v)[8]) {
-  if constexpr (kOut == kF32) {
-    float* p = reinterpret_cast<float*>(out) + idx;
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
-  } else {
-    u32x4 w;
-    uint32_t* pw = reinterpret_cast<uint32_t*>(&w);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (kOut == kBF16)
-        pw[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) |
-                ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
-      else
-        pw[i] = pack_half2((_Float16)v[2 * i], (_Float16)v[2 * i + 1]);
-    }
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + idx) = w;
-  }
-}
-
 }  // namespace
 
 template <int kEpi, bool kLora, bool kABf16, int kOut>

@@ -483,8 +483,9 @@ __device__ __forceinline__ void kloop(const Src& src, int nk, const Rd& rd, int 
 
 }  // namespace
 
-template <bool kSwiglu, int kLora, bool kABf16, int kOut, int kW>
+template <bool kSwiglu, int kLora, bool kABf16, int kOut, int kW, bool kBwd = false>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, int n_tiles) {
+  static_assert(!kBwd || kSwiglu, "the SwiGLU backward pairs gate and up rows like SwiGLU");
   constexpr bool kMx = kW == kWMx;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -651,8 +652,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
   // The epilogue stages its output in the A stages only (for 16-bit
   // outputs, and 32-bit SwiGLU ones): the next tile's absmax group 0 and
   // code pair 0 are then copied in under the epilogue.
+  // (The SwiGLU backward stages fp32 gate, then up, of its 32 columns.)
   constexpr int kStageBytes =
-      NWAVES * 32 * ((kSwiglu ? BNW / 2 : BNW) * (kOut == kF32 ? 4 : 2) + 16);
+      kBwd ? NWAVES * 32 * (BNW / 2 * 4 + 16)
+           : NWAVES * 32 * ((kSwiglu ? BNW / 2 : BNW) * (kOut == kF32 ? 4 : 2) + 16);
   constexpr bool kEarly = kStageBytes <= OFF_BR && kLora == kLoraNone;
 
   // (the found flags are made wave-uniform explicitly: the copy sources
@@ -688,6 +691,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       case 2: kloop<2, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
       case 3: kloop<3, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
       default: kloop<4, kLora, kABf16, kW>(src, nk, rd, wave, lane, early, acc, acc_u); break;
+    }
+    // SwiGLU backward: dh of every m-tile of the tile, two items of 8
+    // columns per lane and m-tile (the epilogue's row layout), loaded before
+    // the final wait so their latency is paid once per tile
+    u32x4 dq[kBwd ? MT : 1][2];
+    if constexpr (kBwd) {
+      const _Float16* dh = reinterpret_cast<const _Float16*>(g.dh);
+      const int cbase = n_idx * 256 + wave * (BNW / 2);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int idx = it * 64 + lane;
+          const int row = mt * 32 + (idx >> 2);
+          const int col = cbase + (idx & 3) * 8;
+          dq[mt][it] = u32x4{0u, 0u, 0u, 0u};
+          if (row < rows_valid && col < I)
+            dq[mt][it] = *reinterpret_cast<const u32x4*>(dh + (int64_t)(row0 + row) * I + col);
+        }
     }
     // LoRA B_e: ranks 8 g2 .. 8 g2 + 7 of this lane's weight row in each
     // n-tile (zero past r), loaded before the final wait so their latency
@@ -752,6 +774,70 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       }
     }
 
+    // ---- SwiGLU backward (training): out = [dh*up*silu'(gate) | dh*silu(gate)]
+    // for the gate and up pre-activations of this tile, with dh the
+    // upstream gradient of h (fp16 [P, I], row i = tile row i), so the
+    // pre-activations never leave the chip.  Each wave stages its m-tile's
+    // gate values in fp32 in a private LDS region, reads them back as 8
+    // consecutive columns of one row per item (two items per lane), then
+    // does the same for up; dh was loaded in that row layout before the
+    // tile's final wait.  No row scale applies.  Optionally h = silu(gate)
+    // * up too (fp16 [P, I]), for the down adapter's gradients.
+    if constexpr (kBwd) {
+      constexpr int PITCH = BNW / 2 * 4 + 16;
+      static_assert(NWAVES * 32 * PITCH == kStageBytes, "staging size as assumed");
+      char* ws = g_ring + wave * 32 * PITCH;
+      const int cbase = n_idx * 256 + wave * (BNW / 2);
+      char* prow = ws + n32 * PITCH;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt >= mtv) continue;
+        float gate[2][8], up[2][8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float v[4] = {acc[mt][half][4 * jj], acc[mt][half][4 * jj + 1],
+                                acc[mt][half][4 * jj + 2], acc[mt][half][4 * jj + 3]};
+            stage_out4<kF32>(prow + (8 * jj + 4 * g2) * 4, v);
+          }
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int idx = it * 64 + lane;
+            const char* src = ws + (idx >> 2) * PITCH + (idx & 3) * 32;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+            float* dst = half == 0 ? gate[it] : up[it];
+            dst[0] = lo.x; dst[1] = lo.y; dst[2] = lo.z; dst[3] = lo.w;
+            dst[4] = hi.x; dst[5] = hi.y; dst[6] = hi.z; dst[7] = hi.w;
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int idx = it * 64 + lane;
+          const int row = mt * 32 + (idx >> 2);
+          const int col = cbase + (idx & 3) * 8;
+          if (row < rows_valid && col < I) {
+            float d[8];
+            unpack8<false>(dq[mt][it], d);
+            float dg[8], du[8], hv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const float z = gate[it][t];
+              const float sg = sigmoid_f(z);
+              const float si = z * sg;
+              dg[t] = d[t] * up[it][t] * (sg * (1.0f + z * (1.0f - sg)));
+              du[t] = d[t] * si;
+              hv[t] = si * up[it][t];
+            }
+            const int64_t orow = g_orow[par][row];
+            store8<kOut>(g.out, orow * 2 * I + col, dg);
+            store8<kOut>(g.out, orow * 2 * I + I + col, du);
+            if (g.h_out != nullptr) store8<kF16>(g.h_out, orow * I + col, hv);
+          }
+        }
+      }
+    } else
     // ---- epilogue: SwiGLU, row scale, conversion to the output dtype, then
     // coalesced stores.  Each wave stages its 32-row slices of the tile in a
     // private LDS region (rows of COLS values, padded by 16 bytes) and stores
@@ -834,6 +920,14 @@ static void launch_out(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s)
   }
 }
 
+// The layer backward's recompute with the SwiGLU backward in its epilogue:
+// fp16 activations and fp16 output only.
+template <int kLora>
+static void launch_bwd(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<true, kLora, false, kF16, kW4, true>), grid,
+                     dim3(NTHREADS), 0, s, g, n_tiles);
+}
+
 template <bool kSwiglu, int kLora, int kW = kW4>
 static void launch_a(const GemmArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
   if (g.a_bf16) launch_out<kSwiglu, kLora, true, kW>(g, grid, n_tiles, s);
@@ -866,6 +960,12 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, int num_cus, hipStream_t strea
     return hipGetLastError();
   }
   const int kind = !lora ? kLoraNone : g.lora_bf16 ? kLoraBF16 : kLoraF16;
+  if (g.dh != nullptr) {
+    if (kind == kLoraBF16) launch_bwd<kLoraBF16>(g, dg, n_tiles, stream);
+    else if (kind == kLoraF16) launch_bwd<kLoraF16>(g, dg, n_tiles, stream);
+    else launch_bwd<kLoraNone>(g, dg, n_tiles, stream);
+    return hipGetLastError();
+  }
   if (g.swiglu) {
     if (kind == kLoraBF16) launch_a<true, kLoraBF16>(g, dg, n_tiles, stream);
     else if (kind == kLoraF16) launch_a<true, kLoraF16>(g, dg, n_tiles, stream);

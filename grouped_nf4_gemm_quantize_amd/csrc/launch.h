@@ -77,6 +77,12 @@ struct GemmArgs {
   float lora_scale;
   int lora_bf16;
   int swiglu;
+  // nullable: with swiglu, the SwiGLU backward instead of SwiGLU -- out =
+  // [dh*up*silu'(gate) | dh*silu(gate)] ([P, N] fp16, row i = tile row i)
+  // for dh the gradient of h ([P, N/2] fp16); fp16 a, fp16 out, nf4 / fp4
+  // stacks, no row scale or scatter
+  const void* dh;
+  void* h_out;  // nullable (SwiGLU backward): h = silu(gate) * up, [P, N/2] fp16
   const float* row_scale;  // nullable
   const int32_t* scatter;  // nullable
   void* out;
@@ -189,8 +195,6 @@ struct LoraPassArgs {
   int rank_major;
 };
 
-hipError_t launch_swiglu_rows(const _Float16* g, int64_t P, int I, _Float16* h, int num_cus,
-                              hipStream_t s);
 hipError_t launch_bf16_to_f16(const void* src, int64_t n, _Float16* dst, int num_cus,
                               hipStream_t s);
 // Up to four bf16 arrays (each a multiple of 8 elements, dst 16-byte

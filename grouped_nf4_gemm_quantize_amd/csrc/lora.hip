@@ -23,50 +23,7 @@ namespace {
 
 constexpr int kLoraTile = 64;  // rows per tile (one expert's rows only)
 
-template <bool kBf16>
-__device__ __forceinline__ void ld8(const void* base, int64_t idx, float (&v)[8]) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (kBf16) {
-      v[2 * i] = bf16_bits_to_f32(ws[i] & 0xffffu);
-      v[2 * i + 1] = bf16_bits_to_f32(ws[i] >> 16);
-    } else {
-      const f16x2 h = u32_as_half2(ws[i]);
-      v[2 * i] = (float)h.x;
-      v[2 * i + 1] = (float)h.y;
-    }
-  }
-}
-
 }  // namespace
-
-// h = silu(g[:, :I]) * g[:, I:], fp16 rows of the recomputed pre-activation.
-__global__ __launch_bounds__(256) void swiglu_rows_kernel(const _Float16* __restrict__ g,
-                                                          int64_t P, int I,
-                                                          _Float16* __restrict__ h) {
-  const int i8 = I / 8;
-  const int64_t n = P * i8;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n;
-       q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = q / i8;
-    const int c = (int)(q - row * i8) * 8;
-    float gate[8], up[8];
-    ld8<false>(g, row * 2 * I + c, gate);
-    ld8<false>(g, row * 2 * I + I + c, up);
-    u32x4 o;
-    uint32_t* po = reinterpret_cast<uint32_t*>(&o);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float a = gate[2 * t] * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[2 * t])) * up[2 * t];
-      const float b = gate[2 * t + 1] * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[2 * t + 1])) *
-                      up[2 * t + 1];
-      po[t] = pack_half2((_Float16)a, (_Float16)b);
-    }
-    *reinterpret_cast<u32x4*>(h + row * I + c) = o;
-  }
-}
 
 // bf16 -> fp16 rows (the output gradient, converted once so the dgrad's
 // contraction loop reads fp16 operands); 8 elements per thread and step.
@@ -319,16 +276,6 @@ __global__ __launch_bounds__(256) void lora_wgrad_reduce_kernel(LoraPassArgs a) 
     if (a.rank_major) a.z[q] = s;
     else a.z[((int64_t)e * a.C + c) * a.r + j] = s;
   }
-}
-
-hipError_t launch_swiglu_rows(const _Float16* g, int64_t P, int I, _Float16* h, int num_cus,
-                              hipStream_t s) {
-  const int64_t n = P * (I / 8);
-  int64_t grid = (n + 255) / 256;
-  if (grid > (int64_t)num_cus * 16) grid = (int64_t)num_cus * 16;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(swiglu_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, g, P, I, h);
-  return hipGetLastError();
 }
 
 hipError_t launch_bf16_to_f16(const void* src, int64_t n, _Float16* dst, int num_cus,

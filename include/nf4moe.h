@@ -296,6 +296,32 @@ int grouped_nf4_gemm_dgrad(const void* a, int a_dtype, int64_t a_rows,
                            const int32_t* scatter, void* out, int out_dtype,
                            void* stream);
 
+/* ---- recompute-and-differentiate SwiGLU (training) -----------------------
+ * The gate_up GEMM of grouped_nf4_gemm recomputed inside backward, with the
+ * SwiGLU backward as its epilogue: for rows expert_offsets[e] <= i <
+ * expert_offsets[e+1], the pre-activation G_i = a[src(i)] . dequant(W_e)^T
+ * ([gate | up], N = 2I columns, fp32 in registers) is never written; the
+ * output is
+ *   out row i = [dh_i * up * silu'(gate) | dh_i * silu(gate)]  (2I columns)
+ * for dh the upstream gradient of h = silu(gate) * up, and optionally h
+ * itself.  The frozen projection is decoded again from the packed bytes
+ * inside backward (README "Training + expert offload"; the dgrad=True
+ * training path of the 0.22.0 README "Which training path?").
+ *   a [a_rows, K]   F16 rows; gather / gather_div as for grouped_nf4_gemm;
+ *   packed, absmax  the gate_up stack [E, N, K]; N = 2I with I a multiple of
+ *                   16, K a multiple of 64 (ESHAPE);
+ *   lora            [host] nullable adapter on the gate_up projection;
+ *   dh              F16 [P, I] (row i), 16-byte aligned;
+ *   out             F16 [P, 2I], 16-byte aligned;
+ *   h_out           nullable F16 [P, I], 16-byte aligned.
+ * No row scale or scatter.  One kernel launch, no workspace; other
+ * arguments and errors as for grouped_nf4_gemm. */
+int grouped_nf4_gemm_swiglu_bwd(const void* a, int64_t a_rows, const int32_t* gather,
+                                int gather_div, const uint8_t* packed, const float* absmax,
+                                const int32_t* expert_offsets, int E, int64_t P, int64_t N,
+                                int64_t K, const nf4moe_lora* lora, const void* dh, void* out,
+                                void* h_out, void* stream);
+
 /* ---- routed-expert layer backward (QLoRA) --------------------------------
  * Given dL/dy for y = moe_expert_forward(x, ...), returns dL/dx through the
  * frozen stacks and, per adapter, dL/dA and dL/dB; the stacks get no
@@ -304,9 +330,10 @@ int grouped_nf4_gemm_dgrad(const void* a, int a_dtype, int64_t a_rows,
  * gate_up pre-activation are recomputed from x and the logits, and both
  * projections are decoded again from the packed bytes (README "Training +
  * expert offload").  The router logits are an input, so no gradient flows
- * through the routing.  Steps: route; G = gate_up(x) (+LoRA); for the down
- * adapter h = SwiGLU(G) and its rank-r projections; dG = SwiGLU backward of
- * (w * dy) . W_dn (+ LoRA), one dgrad launch; per-pair dX = dG . W_gu (+
+ * through the routing.  Steps: route; dh = dy . W_dn (+ LoRA), one dgrad
+ * launch; G = gate_up(x) (+LoRA) recomputed with the SwiGLU backward as its
+ * epilogue, dG = [dh * up * silu'(gate) | dh * silu(gate)] (and h for the
+ * down adapter), one grouped GEMM launch; per-pair dX = w * dG . W_gu (+
  * LoRA), one dgrad launch; dx_t = sum of its k pairs; the adapters'
  * gradients as per-128-row partial sums reduced per expert in a fixed order
  * (deterministic).

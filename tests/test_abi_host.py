@@ -297,6 +297,28 @@ def test_dgrad_rejects_bad_arguments_on_the_host(lib):
     assert lib.grouped_nbit_gemm_dgrad(5, *ok_args.values()) == -1
 
 
+def test_swiglu_bwd_gemm_rejects_bad_arguments_on_the_host(lib):
+    ok_args = dict(a=FAKE, a_rows=8, gather=None, gather_div=1, packed=FAKE, absmax=FAKE,
+                   offsets=FAKE, E=1, P=8, N=128, K=64, lora=None, dh=FAKE, out=FAKE,
+                   h=None, stream=None)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.grouped_nf4_gemm_swiglu_bwd(*a.values())
+
+    assert call(dh=None) == -1
+    assert "dh" in _last(lib)
+    assert call(dh=FAKE + 8) == -1     # dh and h_out need 16 bytes
+    assert call(h=FAKE + 2) == -1
+    assert call(a=None) == -1
+    assert call(out=None) == -1
+    assert call(N=120) == -2           # N = 2I with I a multiple of 16
+    assert call(K=96) == -2
+    assert call(E=0) == -1
+    assert call(P=-1) == -1
+    assert call(P=0) == 0              # nothing to do: no launch
+
+
 def test_backward_rejects_bad_arguments_on_the_host(lib):
     lora = binding.LoraStruct(FAKE, FAKE, 8, 2.0, 1)
     base = dict(x=FAKE, x_dtype=1, logits=FAKE, dy=FAKE, dy_dtype=1, T=4, H=64, I=64, E=4,

@@ -165,6 +165,65 @@ def test_dgrad_swiglu_backward_epilogue(gpu_lib):
                   out_dtype="f32")
 
 
+@pytest.mark.parametrize("lora", [False, True])
+def test_swiglu_bwd_gemm_matches_oracle(gpu_lib, lora):
+    """The gate_up GEMM recomputed with the SwiGLU backward as its epilogue:
+    dG = [dh * up * silu'(gate) | dh * silu(gate)] and h = silu(gate) * up,
+    against the oracle's fp64 G from the same bytes (several row tiles, an
+    empty expert, a one-row expert, I = 272 so the last column tile is
+    ragged)."""
+    rng = np.random.default_rng(300 + lora)
+    E, I, K = 5, 272, 320
+    N = 2 * I
+    counts = [130, 1, 0, 77, 260]
+    P = sum(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    packed, absmax = _random_stack(rng, E, N, K)
+    a = rng.standard_normal((300, K)).astype(np.float16)
+    gather = rng.integers(0, 300 * 3, size=P).astype(np.int32)
+    dh = rng.standard_normal((P, I)).astype(np.float16)
+    lo = lo_ref = None
+    if lora:
+        r = 8
+        A = synth.round_to_bf16(rng.standard_normal((E, r, K), dtype=np.float32) * 0.05)
+        B = synth.round_to_bf16(rng.standard_normal((E, N, r), dtype=np.float32) * 0.05)
+        lo = (gpu(A, torch.bfloat16), gpu(B, torch.bfloat16), 2.0)
+        lo_ref = (A, B, 2.0)
+    h = torch.full((P, I), float("nan"), dtype=torch.float16, device=DEV)
+    out = gpu_lib.grouped_gemm_swiglu_bwd(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                                          gpu(dh), gather=gpu(gather), gather_div=3, lora=lo,
+                                          h_out=h)
+    G = oracle.grouped_gemm(a.astype(np.float64), packed, absmax, offsets, gather=gather,
+                            gather_div=3, lora=lo_ref)
+    ref = oracle.swiglu_backward(G, dh.astype(np.float64))
+    assert_parity(host(out), ref, what="SwiGLU-backward GEMM dG", out_dtype="f16")
+    href = oracle.silu(G[:, :I]) * G[:, I:]
+    assert_parity(host(h), href, what="SwiGLU-backward GEMM h", out_dtype="f16")
+    # without h_out the same dG, bit for bit
+    out2 = gpu_lib.grouped_gemm_swiglu_bwd(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P,
+                                           gpu(dh), gather=gpu(gather), gather_div=3, lora=lo)
+    assert torch.equal(out, out2)
+
+
+def test_swiglu_bwd_gemm_leaves_rows_beyond_offsets_untouched(gpu_lib):
+    """Rows at and past offsets[E] of dG and h are not written."""
+    rng = np.random.default_rng(33)
+    E, I, K = 3, 128, 128
+    counts = [40, 0, 90]
+    P = sum(counts) + 30
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    packed, absmax = _random_stack(rng, E, 2 * I, K)
+    a = rng.standard_normal((P, K)).astype(np.float16)
+    dh = rng.standard_normal((P, I)).astype(np.float16)
+    out = torch.full((P, 2 * I), float("nan"), dtype=torch.float16, device=DEV)
+    h = torch.full((P, I), float("nan"), dtype=torch.float16, device=DEV)
+    gpu_lib.grouped_gemm_swiglu_bwd(gpu(a), gpu(packed), gpu(absmax), gpu(offsets), P, gpu(dh),
+                                    out=out, h_out=h)
+    n = int(offsets[-1])
+    assert torch.isnan(out[n:]).all() and torch.isnan(h[n:]).all()
+    assert not torch.isnan(out[:n]).any() and not torch.isnan(h[:n]).any()
+
+
 def test_dgrad_leaves_rows_beyond_offsets_untouched(gpu_lib):
     rng = np.random.default_rng(28)
     packed, absmax = _random_stack(rng, 2, 64, 64)
@@ -299,7 +358,9 @@ def test_backward_bf16_adapters_match_their_f16_copies_bitwise(gpu_lib):
 
 
 def test_backward_with_zero_b_has_zero_a_gradient(gpu_lib):
-    """B = 0 adapters: dA is exactly zero and dx equals the adapter-free dx."""
+    """B = 0 adapters: dA is exactly zero and dx equals the adapter-free dx
+    bit for bit (every adapter term adds exact zeros), with the gate_up
+    adapter alone and with both."""
     cfg = synth.config("tiny", lora_r=8, lora_alpha=16.0)
     gp, ga, dp, da = _stacks(cfg)
     x = gpu(synth.activations(cfg), torch.bfloat16)
@@ -309,8 +370,11 @@ def test_backward_with_zero_b_has_zero_a_gradient(gpu_lib):
     glo = (glo[0], torch.zeros_like(glo[1]), glo[2])
     dlo = (dlo[0], torch.zeros_like(dlo[1]), dlo[2])
     st = (gpu(gp), gpu(ga), gpu(dp), gpu(da))
-    dx, g = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo, dx_dtype=torch.float32)
     dx0, _ = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, dx_dtype=torch.float32)
+    dxg, gg = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, None, dx_dtype=torch.float32)
+    assert torch.count_nonzero(gg["dA_gu"]) == 0 and torch.count_nonzero(gg["dB_gu"]) > 0
+    assert torch.equal(dxg, dx0)
+    dx, g = gpu_lib.moe_backward(x, lg, dy, cfg.k, *st, glo, dlo, dx_dtype=torch.float32)
     assert torch.count_nonzero(g["dA_gu"]) == 0 and torch.count_nonzero(g["dA_dn"]) == 0
     assert torch.count_nonzero(g["dB_gu"]) > 0 and torch.count_nonzero(g["dB_dn"]) > 0
     assert torch.equal(dx, dx0)
