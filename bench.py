@@ -153,7 +153,7 @@ def _counter_means(directory: str, counter: str):
             continue
         name = r["Kernel_Name"]
         v = float(r["Counter_Value"])
-        if "grouped_gemm_kernel<true, 0, false, 2, 0>" in name:  # the NF4 gate_up
+        if "grouped_gemm_kernel<true, 0, false, 2, 0, false>" in name:  # the NF4 gate_up
             gemm.append(v)
         elif "copyBuffer" in name:
             copy.append(v)
@@ -173,7 +173,7 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> int:
     fetch_b = f_gemm * f_scale * 1024.0
     write_b = w_gemm * w_scale * 1024.0
     rec = {
-        "kernel": "grouped_gemm_kernel<true,0,false,2,0> (gate_up + SwiGLU, olmoe prefill)",
+        "kernel": "grouped_gemm_kernel<true,0,false,2,0,false> (gate_up + SwiGLU, olmoe prefill)",
         "kernel_source_sha256": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest(),
         "fetch_kib_per_launch_raw": round(f_gemm, 1),
         "write_kib_per_launch_raw": round(w_gemm, 1),

@@ -37,7 +37,7 @@ def test_summarize_trace_table(tmp_path):
     d = tmp_path / "trace"
     _write_csv(str(d / "run_kernel_stats.csv"),
                ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
-               [["void nf4moe::grouped_gemm_kernel<true, 0, false, 2, 0>(nf4moe::GemmArgs, int)",
+               [["void nf4moe::grouped_gemm_kernel<true, 0, false, 2, 0, false>(nf4moe::GemmArgs, int)",
                  "19", "6000000", "315790.5", "61.5", "300000", "330000"],
                 ["combine|kernel", "7", "168000", "24000", "1.7", "23000", "25000"]])
     r = _run("--summarize-trace", str(d))
@@ -50,7 +50,7 @@ def test_summarize_trace_table(tmp_path):
 
 def test_summarize_counters_scales_by_the_copy(tmp_path):
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    gemm = "void nf4moe::grouped_gemm_kernel<true, 0, false, 2, 0>(nf4moe::GemmArgs, int)"
+    gemm = "void nf4moe::grouped_gemm_kernel<true, 0, false, 2, 0, false>(nf4moe::GemmArgs, int)"
     copy = "__amd_rocclr_copyBuffer"
     mib512 = 512 * 1024  # KiB
     _write_csv(str(tmp_path / "f" / "run_counter_collection.csv"), hdr,
