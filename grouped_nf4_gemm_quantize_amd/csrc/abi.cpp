@@ -409,7 +409,8 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
                        const nf4moe_lora* lora, int epilogue,
                        const float* row_scale, const int32_t* scatter, void* out,
                        int out_dtype, int qt, hipStream_t stream,
-                       const void* swiglu_bwd_dh = nullptr, void* swiglu_bwd_h = nullptr) {
+                       const void* swiglu_bwd_dh = nullptr, void* swiglu_bwd_h = nullptr,
+                       float* swiglu_bwd_u = nullptr) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
@@ -436,6 +437,7 @@ static int gemm_common(const void* a, int a_dtype, int64_t a_rows, const int32_t
   g.swiglu = epilogue == NF4MOE_EPI_SWIGLU || swiglu_bwd_dh != nullptr;
   g.dh = swiglu_bwd_dh;
   g.h_out = swiglu_bwd_h;
+  g.u_out = swiglu_bwd_u;
   g.row_scale = row_scale;
   g.scatter = scatter;
   g.out = out;
@@ -1037,17 +1039,16 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     dyh = ws + L.dy16;
   }
 
-  // 2. the gate_up adapter of the recompute: A_gu goes to fp16 once here
-  //    (the adapter passes below read it too); bf16 adapters get an fp16
-  //    B_gu as well, so the recompute's k-loop reads fp16 adapter rows (the
-  //    same rounding the GEMM would apply)
+  // 2. the gate_up adapter of the recompute: bf16 adapters go to fp16 once
+  //    here (A_gu and B_gu), so the recompute's k-loop reads fp16 adapter
+  //    rows (the same rounding the GEMM would apply)
   nf4moe_lora gu16{};
   const nf4moe_lora* gu_rc = gu_lora;
   if (gu_lora) {
     const int bf = gu_lora->dtype == NF4MOE_BF16;
-    err = launch_lora_to_f16(gu_lora->A, bf, 0, E, H, r, a16_gu, cus, s);
-    if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
     if (bf) {
+      err = launch_lora_to_f16(gu_lora->A, bf, 0, E, H, r, a16_gu, cus, s);
+      if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
       HalfCopies hc{};
       hc.src[0] = (const uint16_t*)gu_lora->B;
       hc.dst[0] = (_Float16*)(ws + L.b16_gu);
@@ -1087,10 +1088,11 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
 
   // 5. G = x W_gu^T (+ LoRA) recomputed with the SwiGLU backward in its
   //    epilogue: dG1 = [dh * up * silu'(gate) | dh * silu(gate)] in fp16,
-  //    and h = silu(gate) * up as well when the down adapter needs it
+  //    h = silu(gate) * up as well when the down adapter needs it, and the
+  //    gate_up adapter's u = x A_gu^T (fp32), which its k-loop computes anyway
   st = gemm_common(xa, NF4MOE_F16, T, sorted, k, gu_packed, gu_absmax, offs, E, P,
                    2 * (int64_t)I, H, gu_rc, NF4MOE_EPI_SWIGLU, nullptr, nullptr, dG,
-                   NF4MOE_F16, qt, s, dH, dn_lora ? hbuf : nullptr);
+                   NF4MOE_F16, qt, s, dH, dn_lora ? hbuf : nullptr, gu_lora ? u_gu : nullptr);
   if (st != NF4MOE_OK) return st;
 
   // 6. the down adapter's gradients: one pass over h for u = h A_dn^T and
@@ -1104,15 +1106,12 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     if (st != NF4MOE_OK) return st;
   }
 
-  // 7. gate_up adapter: u = x A_gu^T, then one pass over dG1 for
-  //    v1 = dG1 B_gu and dB_gu = s sum w dG1 u^T
+  // 7. gate_up adapter (u = x A_gu^T came from the recompute): one pass
+  //    over dG1 for v1 = dG1 B_gu and dB_gu = s sum w dG1 u^T
   if (gu_lora) {
     const int bf = gu_lora->dtype == NF4MOE_BF16;
     err = launch_lora_to_f16(gu_lora->B, bf, 1, E, 2 * I, r, bt_gu, cus, s);
     if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
-    st = lora_pass(xa, 0, sorted, k, offs, E, P, H, r, a16_gu, u_gu, nullptr, nullptr, nullptr,
-                   nullptr, nullptr, 0.f, 0, cus, s);
-    if (st != NF4MOE_OK) return st;
     st = lora_pass(dG, 0, nullptr, 1, offs, E, P, 2 * I, r, bt_gu, v_gu, wts, sorted, u_gu,
                    part, d_gu_B, gu_lora->scale, 0, cus, s);
     if (st != NF4MOE_OK) return st;

@@ -764,6 +764,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_kernel(GemmArgs g, i
       for (int i = 0; i < 4; ++i)
         u_buf()[(wave * 16 + g4 * 4 + i) * kMaxLoraR + c16] =
             c16 < g.lora_r ? (_Float16)(acc_u[i] * g.lora_scale) : (_Float16)0.f;
+      // training recompute: the projection u = X A_e^T itself (fp32, without
+      // the scale) for the adapter's weight gradients, written once per
+      // M-tile, by its first N-tile
+      if constexpr (kBwd) {
+        if (g.u_out != nullptr && n_idx == 0 && c16 < g.lora_r) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = wave * 16 + g4 * 4 + i;
+            if (row < rows_valid) g.u_out[(int64_t)(row0 + row) * g.lora_r + c16] = acc_u[i];
+          }
+        }
+      }
       lds_barrier();
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {

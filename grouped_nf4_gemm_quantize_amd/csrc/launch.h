@@ -83,6 +83,7 @@ struct GemmArgs {
   // stacks, no row scale or scatter
   const void* dh;
   void* h_out;  // nullable (SwiGLU backward): h = silu(gate) * up, [P, N/2] fp16
+  float* u_out;  // nullable (SwiGLU backward with an adapter): u = X A_e^T, [P, r] fp32
   const float* row_scale;  // nullable
   const int32_t* scatter;  // nullable
   void* out;
