@@ -333,10 +333,10 @@ int grouped_nf4_gemm_swiglu_bwd(const void* a, int64_t a_rows, const int32_t* ga
  * through the routing.  Steps: route; dh = dy . W_dn (+ LoRA), one dgrad
  * launch; G = gate_up(x) (+LoRA) recomputed with the SwiGLU backward as its
  * epilogue, dG = [dh * up * silu'(gate) | dh * silu(gate)] (and h for the
- * down adapter), one grouped GEMM launch; per-pair dX = w * dG . W_gu (+
- * LoRA), one dgrad launch; dx_t = sum of its k pairs; the adapters'
- * gradients as per-128-row partial sums reduced per expert in a fixed order
- * (deterministic).
+ * down adapter, u = x A_gu^T for the gate_up one), one grouped GEMM launch;
+ * per-pair dX = w * dG . W_gu (+ LoRA), one dgrad launch; dx_t = sum of its
+ * k pairs; the adapters' gradients as per-64-row partial sums reduced per
+ * expert in a fixed order (deterministic).
  *   x [T, H]        BF16 or F16; dy [T, H] BF16 or F16 (dy_dtype);
  *   dx [T, H]       BF16, F16 or F32 (dx_dtype);
  *   d_gu_A [E, r, H], d_gu_B [E, 2I, r], d_dn_A [E, r, I], d_dn_B [E, H, r]
