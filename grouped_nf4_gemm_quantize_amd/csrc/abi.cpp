@@ -755,7 +755,8 @@ static int dgrad_common(const void* a, int a_dtype, int64_t a_rows, const int32_
                         int epilogue, const void* g_pre, int g_dtype, const float* row_scale,
                         const int32_t* rs_idx, const int32_t* scatter, const float* lora_v,
                         const nf4moe_lora* lora, void* out, int out_dtype, int qt,
-                        hipStream_t stream) {
+                        hipStream_t stream, const _Float16* lora_bt = nullptr,
+                        float* lora_v_out = nullptr) {
   int cus = 0;
   int st = cu_count(&cus);
   if (st != NF4MOE_OK) return st;
@@ -778,8 +779,10 @@ static int dgrad_common(const void* a, int a_dtype, int64_t a_rows, const int32_
   d.epilogue = epilogue == NF4MOE_EPI_SWIGLU_BWD ? kDgradEpiSwigluBwd : kDgradEpiNone;
   d.g = g_pre;
   d.g_bf16 = g_dtype == NF4MOE_BF16;
-  if (lora_v != nullptr && lora != nullptr) {
+  if ((lora_v != nullptr || lora_bt != nullptr) && lora != nullptr) {
     d.lora_v = lora_v;
+    d.lora_bt = lora_bt;
+    d.lora_v_out = lora_v_out;
     d.lora_a = lora->A;
     d.lora_r = lora->r;
     d.lora_scale = lora->scale;
@@ -1064,26 +1067,26 @@ static int backward_impl(int qt, const void* x, int x_dtype, const float* router
     }
   }
 
-  // 3. with a down adapter: A_dn and B_dn to fp16 (B_dn transposed), then
-  //    v' = dy B_dn (without the routing weight), one projection pass
+  // 3. with a down adapter: A_dn and B_dn to fp16 (B_dn transposed)
   if (dn_lora) {
     const int bf = dn_lora->dtype == NF4MOE_BF16;
     err = launch_lora_to_f16(dn_lora->A, bf, 0, E, I, r, a16_dn, cus, s);
     if (err == hipSuccess) err = launch_lora_to_f16(dn_lora->B, bf, 1, E, H, r, bt_dn, cus, s);
     if (err != hipSuccess) return hip_fail(err, "LoRA conversion launch");
-    st = lora_pass(dyh, 0, sorted, k, offs, E, P, H, r, bt_dn, v_dn, nullptr, nullptr, nullptr,
-                   nullptr, nullptr, 0.f, 0, cus, s);
-    if (st != NF4MOE_OK) return st;
   }
 
   // 4. dH = dy_t W_dn (+ s v' A_dn) for a unit routing weight, fp16 (in
   //    G's space: G itself never goes to memory).  Everything downstream is
   //    linear in w, so w is applied later as a row scale: stored fp16
   //    gradients then keep their precision however small a pair's weight is.
+  //    With a down adapter the dgrad's k-loop, which reads the dy rows
+  //    anyway, also computes v' = dy B_dn (without the routing weight) and
+  //    writes it out for dA_dn
   _Float16* dH = G;
   st = dgrad_common(dyh, NF4MOE_F16, T, sorted, k, dn_packed, dn_absmax, offs, E, P, H, I,
-                    NF4MOE_EPI_NONE, nullptr, NF4MOE_F16, nullptr, nullptr, nullptr,
-                    dn_lora ? v_dn : nullptr, dn_lora, dH, NF4MOE_F16, qt, s);
+                    NF4MOE_EPI_NONE, nullptr, NF4MOE_F16, nullptr, nullptr, nullptr, nullptr,
+                    dn_lora, dH, NF4MOE_F16, qt, s, dn_lora ? bt_dn : nullptr,
+                    dn_lora ? v_dn : nullptr);
   if (st != NF4MOE_OK) return st;
 
   // 5. G = x W_gu^T (+ LoRA) recomputed with the SwiGLU backward in its

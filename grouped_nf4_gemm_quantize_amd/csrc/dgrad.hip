@@ -46,11 +46,16 @@
 // (copies complete in issue order) and s_barrier, as the forward kernel.
 //
 // Epilogues: optional per-expert LoRA rank-r term out += scale * v_i . A_e
-// (v = the rows' projections onto the adapter's B, precomputed, one more
-// MFMA per accumulator tile), row scale, and either a plain store (with an
-// optional scatter of the rows) or the SwiGLU backward: with the forward's
+// (v = the rows' projections onto the adapter's B, one more MFMA per
+// accumulator tile), row scale, and either a plain store (with an optional
+// scatter of the rows) or the SwiGLU backward: with the forward's
 // pre-activation g = [gate | up] of the same row, the output row is
-// [dh * up * silu'(gate) | dh * silu(gate)] (2K columns).
+// [dh * up * silu'(gate) | dh * silu(gate)] (2K columns).  v is either
+// precomputed or, with the plain epilogue, computed in the k-loop from the
+// rows this kernel reads anyway (a 16x16x32 MFMA per k half of a step on
+// each wave's 16 rows and a sixth copy per wave and step, B^T's 16 ranks x
+// 64 stack rows), exchanged between the waves through LDS and written out
+// for the adapter's weight gradients.
 
 #include "common.h"
 #include "launch.h"
@@ -75,10 +80,16 @@ constexpr int kCopies = 32;
 constexpr int OFF_A = 0;                        // 128 rows x 128 B
 constexpr int OFF_B = BM * BK * 2;              // 64 stack rows x 256 B
 constexpr int OFF_S = OFF_B + BK * (BN / 2);    // [64 rows][8 blocks] fp32
-constexpr int STAGE = OFF_S + NWAVES * BK * 4;  // 34816 B
+constexpr int OFF_L = OFF_S + NWAVES * BK * 4;  // adapter B^T: [16 ranks][64 stack rows] fp16
+constexpr int STAGE = OFF_L + kMaxLoraR * BK * 2;  // 36864 B
 constexpr int NSTAGE = 3;
-constexpr int RING = NSTAGE * STAGE;            // 104448 B
-constexpr int kDma = 5;                         // copies per wave and step
+constexpr int RING = NSTAGE * STAGE;            // 110592 B
+// copies per wave and step (one more with the in-loop adapter projection)
+template <bool kVP>
+constexpr int kDmaOf() { return kVP ? 6 : 5; }
+// the in-loop projection v (fp16, scaled, [BM][16]) at the end of the ring,
+// free once the k-loop has drained; the epilogue staging uses the start
+constexpr int OFF_V = RING - BM * kMaxLoraR * 2;
 
 }  // namespace
 
@@ -100,15 +111,17 @@ __device__ __forceinline__ uint32_t dlut_read(uint32_t addr) {
 }
 
 struct DSrc {
-  i32x4 a_rsrc, b_rsrc, s_rsrc;
+  i32x4 a_rsrc, b_rsrc, s_rsrc, l_rsrc;
   uint32_t a_off[2];  // A: 2 x 16 B per lane
   uint32_t b_off[2];  // codes: 2 x 16 B per lane
   uint32_t s_off;     // absmax: 4 B per lane
+  uint32_t l_off;     // adapter B^T rows: 4 B per lane
   uint32_t b_step;    // bytes of 64 stack rows of codes
   uint32_t s_step;    // bytes of 64 stack rows of absmax
 };
 
 // The copies of step `kb` (clamped by the caller) into the stage at `st`.
+template <bool kVP>
 __device__ __forceinline__ void issue_step(const DSrc& s, int kb, uint32_t st, int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -117,6 +130,7 @@ __device__ __forceinline__ void issue_step(const DSrc& s, int kb, uint32_t st, i
   for (int i = 0; i < 2; ++i)
     dma16(s.b_rsrc, s.b_off[i], (uint32_t)kb * s.b_step, st + OFF_B + (wave * 2 + i) * 1024);
   dma4(s.s_rsrc, s.s_off, (uint32_t)kb * s.s_step, st + OFF_S + wave * 256);
+  if constexpr (kVP) dma4(s.l_rsrc, s.l_off, (uint32_t)kb * (BK * 2), st + OFF_L + wave * 256);
 }
 
 // Per-lane constants: LDS read offsets and the transpose's lane masks.
@@ -206,11 +220,11 @@ __device__ __forceinline__ void scale_b(const uint32_t (&d)[NT][4], const u32x4 
 // substep 3 has passed), after converting that step's absmax.  The next
 // weights are scaled after this substep's MFMAs are issued, so no MFMA
 // waits on the multiplies.
-template <int S, int MTV, bool kABf16>
+template <int S, int MTV, bool kABf16, bool kVP>
 __device__ __forceinline__ void substep(const char* st, const char* nst, int par, int wave,
                                         int lane, const DRd& rd, uint32_t (&cw)[4][NT],
                                         f16x8 (&af)[MT], f16x8 (&bf)[NT],
-                                        f32x16 (&acc)[MT][NT]) {
+                                        f32x16 (&acc)[MT][NT], f32x4& acc_v) {
   f16x8 af_n[MT];
   uint32_t dn[NT][4];
   u32x4 sc_n;
@@ -225,6 +239,21 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int par
     load_a<MTV, kABf16>(nst, rd, 0, af_n);
     lookups(cw[0], rd, dn);
     sc_n = load_sc(par ^ 1, rd, 0);
+  }
+  // in-loop adapter projection: v[this wave's 16 rows][16 ranks] += a B_e,
+  // stack-row half S - 1 of the step
+  // (operand offsets recomputed here rather than held: the kernel is at its
+  // register limit) -- A row c16 of this wave's 16 rows, k chunk 4 s2 + g4,
+  // swizzled like the main fragments; B^T row (rank) c16, same k
+  if constexpr (kVP && (S == 1 || S == 2)) {
+    constexpr int s2 = S - 1;
+    const int c16 = lane & 15, g4 = lane >> 4;
+    const int row = wave * 16 + c16;
+    const uint32_t ua = row * 128 + (((4 * s2 + g4) ^ ((row >> 1) & 7)) << 4);
+    const u32x4 l = *reinterpret_cast<const u32x4*>(st + OFF_L + c16 * 128 + g4 * 16 + s2 * 64);
+    u32x4 v = *reinterpret_cast<const u32x4*>(st + OFF_A + ua);
+    if constexpr (kABf16) v = bf16x8_to_f16x8(v);
+    acc_v = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(v), as_f16x8(l), acc_v, 0, 0, 0);
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -245,14 +274,15 @@ __device__ __forceinline__ void substep(const char* st, const char* nst, int par
 // fetched (only the prologue repeats the last batch, when there are fewer
 // than three steps); in the last two steps batch kb + 2 does not exist, so
 // they drain all copies instead, and the tile ends with none in flight.
-template <int MTV, bool kABf16>
+template <int MTV, bool kABf16, bool kVP>
 __device__ __forceinline__ void kloop(const DSrc& src, int nk, const DRd& rd, int wave,
-                                      int lane, f32x16 (&acc)[MT][NT]) {
+                                      int lane, f32x16 (&acc)[MT][NT], f32x4& acc_v) {
+  constexpr int kDma = kDmaOf<kVP>();
   const uint32_t ring = lds_addr(d_ring);
   const int last = nk - 1;
-  issue_step(src, 0, ring, wave);
-  issue_step(src, min(1, last), ring + STAGE, wave);
-  issue_step(src, min(2, last), ring + 2 * STAGE, wave);
+  issue_step<kVP>(src, 0, ring, wave);
+  issue_step<kVP>(src, min(1, last), ring + STAGE, wave);
+  issue_step<kVP>(src, min(2, last), ring + 2 * STAGE, wave);
   wait_vm_barrier<2 * kDma>();  // batch 0 landed
 
   uint32_t cw[4][NT];
@@ -275,26 +305,28 @@ __device__ __forceinline__ void kloop(const DSrc& src, int nk, const DRd& rd, in
     const char* st = d_ring + sidx * STAGE;
     const char* nst = d_ring + nidx * STAGE;
     const int par = kb & 1;
-    substep<0, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
-    substep<1, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
-    substep<2, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
+    substep<0, MTV, kABf16, kVP>(st, nst, par, wave, lane, rd, cw, af, bf, acc, acc_v);
+    substep<1, MTV, kABf16, kVP>(st, nst, par, wave, lane, rd, cw, af, bf, acc, acc_v);
+    substep<2, MTV, kABf16, kVP>(st, nst, par, wave, lane, rd, cw, af, bf, acc, acc_v);
     if (kb >= last - 1) wait_vm_barrier<0>();
     else wait_vm_barrier<kDma>();
-    if (kb + 3 <= last) issue_step(src, kb + 3, ring + sidx * STAGE, wave);
-    substep<3, MTV, kABf16>(st, nst, par, wave, lane, rd, cw, af, bf, acc);
+    if (kb + 3 <= last) issue_step<kVP>(src, kb + 3, ring + sidx * STAGE, wave);
+    substep<3, MTV, kABf16, kVP>(st, nst, par, wave, lane, rd, cw, af, bf, acc, acc_v);
     sidx = nidx;
   }
 }
 
 }  // namespace
 
-template <int kEpi, bool kLora, bool kABf16, int kOut>
+template <int kEpi, bool kLora, bool kABf16, int kOut, bool kVP>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g, int n_tiles) {
+  static_assert(!kVP || kLora, "the in-loop projection feeds the adapter term");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31;
   const int g2 = lane >> 5;
+  const int c16 = lane & 15, g4 = lane >> 4;  // 16x16x32 operand coordinates
 
   lut_fill<kCopies>(d_lut, d_lstage, g.qtype == kQtFP4 ? c_levels_dgrad_fp4 : c_levels_dgrad,
                     tid, NTHREADS);
@@ -392,6 +424,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
     // last tile) read values only waves with no live columns use
     src.s_off = ((uint32_t)(wave * 8 + (lane >> 3)) * (uint32_t)KB +
                  (uint32_t)(cbase / 64 + (lane & 7))) * 4u;
+    if constexpr (kVP) {
+      // adapter B^T [E, r, N] fp16: 16 ranks x 128 B per step; dword d of the
+      // block is rank d / 32 (ranks past r read rank 0, zeroed afterwards)
+      const uint32_t l_bytes = (uint32_t)g.lora_r * (uint32_t)N * 2u;
+      src.l_rsrc = make_rsrc(reinterpret_cast<const char*>(g.lora_bt) + (int64_t)e * l_bytes,
+                             l_bytes);
+      const int d = wave * 64 + lane;
+      const int rho = d >> 5;
+      const int rc = rho < g.lora_r ? rho : 0;
+      src.l_off = (uint32_t)rc * (uint32_t)N * 2u + (uint32_t)(d & 31) * 4u;
+    } else {
+      src.l_rsrc = i32x4{0, 0, 0, 0};
+      src.l_off = 0;
+    }
 
     const int par = r & 1;
     if (tid < BM) {
@@ -410,15 +456,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
+    f32x4 acc_v = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    lds_barrier();  // every wave is done with the previous tile's stages
+    lds_barrier();  // every wave is done with the previous tile's stages (and v)
     switch (mtv) {
-      case 1: kloop<1, kABf16>(src, nk, rd, wave, lane, acc); break;
-      case 2: kloop<2, kABf16>(src, nk, rd, wave, lane, acc); break;
-      case 3: kloop<3, kABf16>(src, nk, rd, wave, lane, acc); break;
-      default: kloop<4, kABf16>(src, nk, rd, wave, lane, acc); break;
+      case 1: kloop<1, kABf16, kVP>(src, nk, rd, wave, lane, acc, acc_v); break;
+      case 2: kloop<2, kABf16, kVP>(src, nk, rd, wave, lane, acc, acc_v); break;
+      case 3: kloop<3, kABf16, kVP>(src, nk, rd, wave, lane, acc, acc_v); break;
+      default: kloop<4, kABf16, kVP>(src, nk, rd, wave, lane, acc, acc_v); break;
     }
     wait_vm_barrier<0>();  // every copy landed; the ring is free for staging
+
+    // ---- in-loop projection v = a . B_e: 16x16 accumulator layout, lane
+    // holds rank c16 of rows 4 g4 + i of this wave's 16.  Written out once
+    // per M-tile (by its first N-tile) in fp32 for the adapter's weight
+    // gradients, and exchanged between the waves in fp16 with the scale
+    // applied (ranks past r computed on a stand-in row, stored as zero).
+    _Float16* v_buf = reinterpret_cast<_Float16*>(d_ring + OFF_V);
+    if constexpr (kVP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wave * 16 + g4 * 4 + i;
+        v_buf[row * kMaxLoraR + c16] =
+            c16 < g.lora_r ? (_Float16)(acc_v[i] * g.lora_scale) : (_Float16)0.f;
+        if (g.lora_v_out != nullptr && n_idx == 0 && c16 < g.lora_r && row < rows_valid)
+          g.lora_v_out[(int64_t)(row0 + row) * g.lora_r + c16] = acc_v[i];
+      }
+      lds_barrier();
+    }
 
     const int col_w = cbase + wave * BNW;  // first output column of this wave
     const bool wave_live = col_w < K;
@@ -445,13 +510,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt >= mtv) continue;
-        const int row = row0 + min(mt * 32 + n32, rows_valid - 1);
-        const float* vr = g.lora_v + (int64_t)row * g.lora_r;
         f16x8 au;
+        if constexpr (kVP) {
+          au = *reinterpret_cast<const f16x8*>(&v_buf[(mt * 32 + n32) * kMaxLoraR + g2 * 8]);
+        } else {
+          const int row = row0 + min(mt * 32 + n32, rows_valid - 1);
+          const float* vr = g.lora_v + (int64_t)row * g.lora_r;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int rho = g2 * 8 + t;
-          au[t] = (_Float16)(rho < g.lora_r ? vr[rho] * g.lora_scale : 0.f);
+          for (int t = 0; t < 8; ++t) {
+            const int rho = g2 * 8 + t;
+            au[t] = (_Float16)(rho < g.lora_r ? vr[rho] * g.lora_scale : 0.f);
+          }
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -574,28 +643,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int kEpi, bool kLora, bool kABf16>
+template <int kEpi, bool kLora, bool kABf16, bool kVP>
 static void dgrad_out(const DgradArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
   switch (g.out_dtype) {
     case kF32:
-      hipLaunchKernelGGL((grouped_dgrad_kernel<kEpi, kLora, kABf16, kF32>), grid,
+      hipLaunchKernelGGL((grouped_dgrad_kernel<kEpi, kLora, kABf16, kF32, kVP>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     case kBF16:
-      hipLaunchKernelGGL((grouped_dgrad_kernel<kEpi, kLora, kABf16, kBF16>), grid,
+      hipLaunchKernelGGL((grouped_dgrad_kernel<kEpi, kLora, kABf16, kBF16, kVP>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
     default:
-      hipLaunchKernelGGL((grouped_dgrad_kernel<kEpi, kLora, kABf16, kF16>), grid,
+      hipLaunchKernelGGL((grouped_dgrad_kernel<kEpi, kLora, kABf16, kF16, kVP>), grid,
                          dim3(NTHREADS), 0, s, g, n_tiles);
       break;
   }
 }
 
-template <int kEpi, bool kLora>
+template <int kEpi, bool kLora, bool kVP = false>
 static void dgrad_a(const DgradArgs& g, dim3 grid, int n_tiles, hipStream_t s) {
-  if (g.a_bf16) dgrad_out<kEpi, kLora, true>(g, grid, n_tiles, s);
-  else dgrad_out<kEpi, kLora, false>(g, grid, n_tiles, s);
+  if (g.a_bf16) dgrad_out<kEpi, kLora, true, kVP>(g, grid, n_tiles, s);
+  else dgrad_out<kEpi, kLora, false, kVP>(g, grid, n_tiles, s);
 }
 
 hipError_t launch_grouped_dgrad(const DgradArgs& g, int num_cus, hipStream_t stream) {
@@ -606,7 +675,11 @@ hipError_t launch_grouped_dgrad(const DgradArgs& g, int num_cus, hipStream_t str
   if (grid < 8) grid = 8;
   const dim3 dg((unsigned)grid);
   const bool lora = g.lora_v != nullptr;
-  if (g.epilogue == kDgradEpiSwigluBwd) {
+  if (g.lora_bt != nullptr) {
+    // the adapter's projection computed in the k-loop (plain epilogue only)
+    if (g.epilogue != kDgradEpiNone) return hipErrorInvalidValue;
+    dgrad_a<kDgradEpiNone, true, true>(g, dg, n_tiles, stream);
+  } else if (g.epilogue == kDgradEpiSwigluBwd) {
     if (lora) dgrad_a<kDgradEpiSwigluBwd, true>(g, dg, n_tiles, stream);
     else dgrad_a<kDgradEpiSwigluBwd, false>(g, dg, n_tiles, stream);
   } else {

@@ -160,6 +160,11 @@ struct DgradArgs {
   const void* g;           // SwiGLU backward: pre-activation rows [P, 2K] (row i)
   int g_bf16;
   const float* lora_v;     // nullable [P, r] fp32 (row i)
+  // nullable (plain epilogue only): v = a . B_e computed in the k-loop from
+  // the adapter's B transposed, fp16 [E, r, N], instead of lora_v; written to
+  // lora_v_out ([P, r] fp32, row i) when that is non-null
+  const _Float16* lora_bt;
+  float* lora_v_out;
   const void* lora_a;      // [E, r, K]
   int lora_r;
   float lora_scale;
