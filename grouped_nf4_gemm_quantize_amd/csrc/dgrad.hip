@@ -139,7 +139,7 @@ struct DRd {
   uint32_t b[NT];     // code word of n-tile nt, substep 0 (+ 2048 per substep)
   uint32_t sc;        // this lane's 8 scales of substep 0 in d_sc (+ 16 B per substep)
   uint32_t lane_off;  // decode-table word offset
-  uint32_t k1, k2, k3, amt3;
+  uint32_t s1, s2, k3, amt3;
 };
 
 // The 8x8 nibble transpose over the 8 lanes of a group (lanes 8j..8j+7):
@@ -147,17 +147,17 @@ struct DRd {
 // with the codes of column i for rows 0..7, byte m = row 2m << 4 | row 2m+1.
 // Stage 1 exchanges 16-bit halves with the lane 4 away (row_shl:4 into the
 // lower quad, row_shr:4 into the upper one), stage 2 bytes with the lane 2
-// away, stage 3 nibbles with the neighbouring lane; each stage rotates the
-// word so the partner's field lands where it is kept.
+// away -- in both, one byte permute of (partner, own) word keeps the lane's
+// own field and moves the partner's into place -- and stage 3 nibbles with
+// the neighbouring lane, rotating the word so the partner's field lands
+// where it is kept.
 __device__ __forceinline__ uint32_t transpose8(uint32_t x, const DRd& rd) {
-  uint32_t y = __builtin_amdgcn_alignbit(x, x, 16);
-  int p = __builtin_amdgcn_update_dpp(0, (int)y, 0x114 /* row_shr:4 */, 0xf, 0xa, false);
-  p = __builtin_amdgcn_update_dpp(p, (int)y, 0x104 /* row_shl:4 */, 0xf, 0x5, false);
-  x = (x & rd.k1) | ((uint32_t)p & ~rd.k1);
-  y = __builtin_amdgcn_perm(x, x, 0x02030001u);
-  p = __builtin_amdgcn_mov_dpp((int)y, 0x4e /* quad_perm [2,3,0,1] */, 0xf, 0xf, false);
-  x = (x & rd.k2) | ((uint32_t)p & ~rd.k2);
-  y = __builtin_amdgcn_alignbit(x, x, rd.amt3);
+  int p = __builtin_amdgcn_update_dpp(0, (int)x, 0x114 /* row_shr:4 */, 0xf, 0xa, false);
+  p = __builtin_amdgcn_update_dpp(p, (int)x, 0x104 /* row_shl:4 */, 0xf, 0x5, false);
+  x = __builtin_amdgcn_perm((uint32_t)p, x, rd.s1);
+  p = __builtin_amdgcn_mov_dpp((int)x, 0x4e /* quad_perm [2,3,0,1] */, 0xf, 0xf, false);
+  x = __builtin_amdgcn_perm((uint32_t)p, x, rd.s2);
+  uint32_t y = __builtin_amdgcn_alignbit(x, x, rd.amt3);
   p = __builtin_amdgcn_mov_dpp((int)y, 0xb1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false);
   x = (x & rd.k3) | ((uint32_t)p & ~rd.k3);
   return x;
@@ -351,8 +351,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_dgrad_kernel(DgradArgs g,
   }
   rd.sc = (uint32_t)(wave * BK + 32 * g2) * 2u;
   rd.lane_off = (uint32_t)(lane & 31) * 4u;
-  rd.k1 = (lane & 4) ? 0xffff0000u : 0x0000ffffu;
-  rd.k2 = (lane & 2) ? 0xff00ff00u : 0x00ff00ffu;
+  // byte selectors of (partner word : own word), own bytes 0-3, partner's
+  // 4-7: stage 1 keeps the own low half and takes the partner's low half as
+  // its high one (lanes 0-3 of a group) or keeps the own high half and takes
+  // the partner's high half as its low one (lanes 4-7); stage 2 likewise
+  // with bytes 0 and 2 (lanes with bit 1 clear) or 1 and 3
+  rd.s1 = (lane & 4) ? 0x03020706u : 0x05040100u;
+  rd.s2 = (lane & 2) ? 0x03070105u : 0x06020400u;
   rd.k3 = (lane & 1) ? 0x0f0f0f0fu : 0xf0f0f0f0u;
   rd.amt3 = (lane & 1) ? 4u : 28u;
 
