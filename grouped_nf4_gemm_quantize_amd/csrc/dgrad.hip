@@ -152,15 +152,21 @@ struct DRd {
 // the neighbouring lane, rotating the word so the partner's field lands
 // where it is kept.
 __device__ __forceinline__ uint32_t transpose8(uint32_t x, const DRd& rd) {
-  int p = __builtin_amdgcn_update_dpp(0, (int)x, 0x114 /* row_shr:4 */, 0xf, 0xa, false);
+  // the two masked moves of stage 1 together write every lane (banks 1, 3
+  // from 4 lanes down, banks 0, 2 from 4 lanes up), so the first needs no
+  // initialised destination
+  int p = __builtin_amdgcn_mov_dpp((int)x, 0x114 /* row_shr:4 */, 0xf, 0xa, false);
   p = __builtin_amdgcn_update_dpp(p, (int)x, 0x104 /* row_shl:4 */, 0xf, 0x5, false);
   x = __builtin_amdgcn_perm((uint32_t)p, x, rd.s1);
   p = __builtin_amdgcn_mov_dpp((int)x, 0x4e /* quad_perm [2,3,0,1] */, 0xf, 0xf, false);
   x = __builtin_amdgcn_perm((uint32_t)p, x, rd.s2);
-  uint32_t y = __builtin_amdgcn_alignbit(x, x, rd.amt3);
+  const uint32_t y = __builtin_amdgcn_alignbit(x, x, rd.amt3);
   p = __builtin_amdgcn_mov_dpp((int)y, 0xb1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false);
-  x = (x & rd.k3) | ((uint32_t)p & ~rd.k3);
-  return x;
+  // (x & k3) | (p & ~k3) as one bit-field insert (the compiler otherwise
+  // spends an AND and an AND-OR)
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(rd.k3), "v"(x), "v"(p));
+  return r;
 }
 
 // Transpose and table lookups of one substep for both n-tiles.
